@@ -1,0 +1,6 @@
+"""Float64 CPU oracle (test infrastructure only; see ce_oracle's header)."""
+from .ce_oracle import (REDUCTIONS, OracleResult, RowResult, TargetSummary, ce_backward,
+                        ce_forward, reduce_rows, rows_forward, summarize_targets, widen)
+
+__all__ = ["REDUCTIONS", "OracleResult", "RowResult", "TargetSummary", "ce_backward",
+           "ce_forward", "reduce_rows", "rows_forward", "summarize_targets", "widen"]
