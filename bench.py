@@ -1,0 +1,247 @@
+"""Benchmark of the fused softmax cross-entropy forward + gradient on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole hot path over one batch of synthetic logits
+already resident in HBM: ce_forward (loss + gradient written over the
+logits) followed by ce_backward with grad_output = 1 (the training call
+pattern). Every step gets its own pristine copy of the batch (prepared
+before the timed region), so no step reads a gradient left by another.
+
+The default workload is 1023 rows x V = 128256 fp32 logits, reduction
+"sum" (the tt-mlir PR #9324 page's before/after shape). Prints one JSON
+line with rows/s, the roofline of the fused kernel (achieved HBM GB/s from
+algorithmic bytes over its event-timed duration) and the float64 oracle
+timed on the host cores as a CPU baseline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import resource
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+DEFAULT_WORKLOAD = "ce_1023x128256_f32"
+DEFAULT_REDUCTION = {"ce_1023x128256_f32": "sum"}
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def source_hash() -> str:
+    """Hash of the HIP sources: counter-based traffic figures are valid only
+    for the kernels they were taken on."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "softmax_cross_entropy_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(w, reduction: str, n_counted: int) -> int:
+    """Bytes the method itself must move: each counted row read once, every
+    row's gradient written once, targets, class weights and the outputs."""
+    e = w.elem_bytes
+    b = n_counted * w.V * e + w.rows * w.V * e + w.rows * 8
+    if w.weights:
+        b += w.V * 4
+    n_out = 1 + (1 if w.want_z_loss else 0) + (1 if w.want_accuracy else 0)
+    b += (w.rows * 4 if reduction == "none" else 4) * n_out
+    if w.want_argmax:
+        b += w.rows * 8
+    return b
+
+
+def traffic_from_profiles(workload: str, kernel_key: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when it is missing or was taken on different kernel sources."""
+    path = os.path.join(PROFILES, f"{kernel_key}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(x_host, t_host, weight_host, w, reduction, budget_s=12.0):
+    """Time the float64 oracle, as it is, on a bounded sample of the rows."""
+    import numpy as np
+    from oracle import ce_forward as oracle_forward
+
+    rows_per_call = 64
+    done_rows = 0
+    t0 = time.perf_counter()
+    c0 = resource.getrusage(resource.RUSAGE_SELF)
+    calls = 0
+    while True:
+        a = (calls * rows_per_call) % max(1, x_host.shape[0] - rows_per_call)
+        oracle_forward(x_host[a:a + rows_per_call], t_host[a:a + rows_per_call],
+                       weight=weight_host, label_smoothing=w.label_smoothing,
+                       lse_square_scale=w.lse_square_scale, softcap=w.softcap or None,
+                       reduction=reduction)
+        calls += 1
+        done_rows += rows_per_call
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    wall = time.perf_counter() - t0
+    c1 = resource.getrusage(resource.RUSAGE_SELF)
+    cpu = (c1.ru_utime - c0.ru_utime) + (c1.ru_stime - c0.ru_stime)
+    cores = max(1, int(round(cpu / wall)))
+    del np
+    return {"value": done_rows / wall, "unit": "rows/s", "cores": cores, "kind": "oracle",
+            "sample": f"{calls} oracle calls of {rows_per_call} rows of the {w.name} batch "
+                      f"({done_rows} rows, {wall:.1f} s wall, {cpu:.1f} s CPU)"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--reduction", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    a = ap.parse_args(argv)
+
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (the path shards "
+              "by rows with no communication; see the design notes).", file=sys.stderr)
+        return 2
+
+    import torch
+    import synth
+    from softmax_cross_entropy_amd import _lib
+    from softmax_cross_entropy_amd.functional import _workspace
+
+    w = synth.WORKLOADS[a.workload]
+    red = a.reduction or DEFAULT_REDUCTION.get(w.name, w.reductions[0])
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    inp = synth.make_inputs(w, dev)
+    t_host = inp.target.cpu().numpy()
+    n_counted = int(((t_host != -100) & (t_host >= 0) & (t_host < w.V)).sum())
+    nbuf = a.warmup + a.steps
+    bufs = [inp.logits.clone() for _ in range(nbuf)]
+    sample_host = None
+    if not a.no_cpu_baseline:
+        x = inp.logits[:256].detach().cpu()
+        sample_host = (x.view(torch.int16).numpy().view("uint16") if x.dtype == torch.bfloat16
+                       else x.numpy(), t_host[:256])
+    dt = _lib.dtype_code(w.dtype)
+    flags = _lib.CE_F_GRAD
+    rows, V = w.rows, w.V
+    f32 = dict(device=dev, dtype=torch.float32)
+    loss = torch.empty((rows,) if red == "none" else (), **f32)
+    z_loss = torch.empty_like(loss) if w.want_z_loss else None
+    acc = torch.empty_like(loss) if w.want_accuracy else None
+    arg = torch.empty((rows,), device=dev, dtype=torch.int64) if w.want_argmax else None
+    go = torch.ones((), **f32)
+    ws_bytes = _lib.ce_workspace_bytes(rows, V, dt, flags)
+    ws = _workspace(dev, ws_bytes)
+    P = lambda t: 0 if t is None else t.data_ptr()  # noqa: E731
+    tgt, wt = P(inp.target), P(inp.weight)
+    s = stream.cuda_stream
+    path = _lib.PATH_NAMES[_lib.ce_plan_path(P(bufs[0]), dt, rows, V, bufs[0].stride(0), wt,
+                                             w.label_smoothing, flags)]
+    red_code = _lib.REDUCTION_CODES[red]
+
+    def step(buf):
+        st = _lib.ce_forward(P(buf), dt, rows, V, buf.stride(0), tgt, wt, -100,
+                             w.label_smoothing, w.lse_square_scale, w.softcap, red_code, flags,
+                             P(loss), P(z_loss), P(acc), P(arg), 0, P(ws), ws_bytes, s)
+        if st:
+            raise _lib.CEError(st, "ce_forward")
+
+    def bwd(buf):
+        st = _lib.ce_backward(P(buf), dt, rows, V, buf.stride(0), P(go), 0, s)
+        if st:
+            raise _lib.CEError(st, "ce_backward")
+
+    for i in range(a.warmup):
+        step(bufs[i])
+        bwd(bufs[i])
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(a.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(a.steps):
+        b = bufs[a.warmup + i]
+        ev[i][0].record(stream)
+        step(b)
+        ev[i][1].record(stream)
+        bwd(b)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    fwd_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    kernel_ms = sum(fwd_ms) / len(fwd_ms)
+    ms_per_step = total_ms / a.steps
+    del bufs
+
+    # copy ceiling of the same size (read + write), for context
+    src = inp.logits
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(10):
+        dst.copy_(src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * src.numel() * src.element_size() * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del dst
+
+    alg = algorithmic_bytes(w, red, n_counted)
+    achieved = alg / (kernel_ms * 1e-3) / 1e9
+    kernel_key = "ce_fused" if path == "fused" else f"ce_{path}"
+    traffic = traffic_from_profiles(w.name, kernel_key)
+    out = {
+        "metric": "fused CE fwd+grad rows/s and achieved HBM GB/s (% of peak), V=128256",
+        "value": rows * a.steps / (total_ms * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if w.dtype == torch.float32 else "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "rows": rows, "V": V, "reduction": red, "path": path,
+                   "label_smoothing": w.label_smoothing, "softcap": w.softcap,
+                   "lse_square_scale": w.lse_square_scale, "class_weights": w.weights,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "kernel_ms": kernel_ms, "algorithmic_bytes": alg},
+        "copy_ceiling_GBps": copy_gbps,
+    }
+    if sample_host is not None:
+        wh = None if inp.weight is None else inp.weight.cpu().numpy()
+        out["cpu_baseline"] = cpu_baseline(sample_host[0], sample_host[1], wh, w, red,
+                                           a.cpu_budget)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,140 @@
+/* ce.h -- C ABI of the MI355X (gfx950) fused softmax cross-entropy library.
+ *
+ * The operation is the one described on the Liger-Kernel page "Kernel
+ * Profile: CrossEntropy (Tier 3 - Fused/Complex)":
+ *   Forward Pass    -- inputs (logits (rows, V), target (rows,), optional
+ *                      class weights (V,), ignore_index, label_smoothing,
+ *                      reduction, softcap) and outputs (loss, z_loss,
+ *                      token_accuracy, predicted tokens);
+ *   Module Parameters -- lse_square_scale (z-loss), defaults;
+ *   Key Patterns    -- online softmax, gradient-in-forward (the forward
+ *                      overwrites the logits with d loss / d logits),
+ *                      multiple loss components;
+ *   Backward Pass   -- backward only scales the stored gradient by
+ *                      grad_output.
+ * The all-ignored mean (NaN loss, zero gradients) follows the tt-mlir pull
+ * request page "[tt-crank] fuse cross entropy onto the ttml
+ * cross_entropy_fw/bw composites" (#9324), Copilot comments on the mean
+ * reduction.
+ *
+ * Definitions, with z = c tanh(x / c) for softcap c > 0 (else z = x),
+ * lse_i = log sum_k exp(z_ik), eps = label_smoothing, w = class weights
+ * (all ones when NULL), W = sum_k w_k, lam = lse_square_scale:
+ *   l_i    = (1 - eps) w_y (lse_i - z_iy) + (eps / V) sum_k w_k (lse_i - z_ik)
+ *   zeta_i = lam * lse_i^2
+ * A row is counted when target != ignore_index and 0 <= target < V;
+ * n = counted rows, D = sum over counted rows of w[target].
+ *   mean: loss = sum l / D + sum zeta / n,  z_loss = sum zeta / n
+ *   sum:  loss = sum l + sum zeta,          z_loss = sum zeta
+ *   none: loss_i = l_i + zeta_i,            z_loss_i = zeta_i
+ * token_accuracy = n_correct / n (mean, sum) or the per-row 0/1 (none);
+ * argmax is over the raw logits, lowest index on ties, -1 on rows that are
+ * not counted. Ignored rows are never read and get zero loss and a +0.0
+ * gradient. The gradient is that of `loss` with grad_output = 1; for mean,
+ * a zero D (or n) gives zero gradients and a NaN loss.
+ * Rows whose target is outside [0, V) and not ignore_index get a NaN loss,
+ * a zero gradient and argmax -1, are not counted, and set a device error
+ * bit (see CE_F_CHECK_TARGETS).
+ *
+ * Conventions for every call:
+ *  - Pointers marked [device] are HIP device pointers; the library never
+ *    allocates, frees or keeps a pointer after returning.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream);
+ *    the calls return without waiting for the GPU, except with
+ *    CE_F_CHECK_TARGETS.
+ *  - Arguments are validated on the host before anything is enqueued: on
+ *    an error status nothing has been written.
+ *  - Concurrent calls that share a workspace race; give each stream its
+ *    own workspace.
+ */
+#ifndef CE_MI355X_H
+#define CE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CE_OK = 0,
+  CE_E_NULL = -1,         /* a required pointer is NULL                        */
+  CE_E_SHAPE = -2,        /* rows < 0, V < 1, row_stride < V, or too large     */
+  CE_E_DTYPE = -3,        /* unknown dtype                                     */
+  CE_E_PARAM = -4,        /* bad reduction, label_smoothing, softcap, scale    */
+  CE_E_WORKSPACE = -5,    /* workspace NULL, too small or not 256-B aligned    */
+  CE_E_HIP = -6,          /* a HIP runtime call or kernel launch failed        */
+  CE_E_TARGET_RANGE = -7  /* CE_F_CHECK_TARGETS: a target outside [0, V)      */
+} ce_status;
+
+typedef enum { CE_F32 = 0, CE_BF16 = 1 } ce_dtype;
+
+typedef enum { CE_RED_NONE = 0, CE_RED_MEAN = 1, CE_RED_SUM = 2 } ce_reduction;
+
+enum {
+  CE_F_GRAD = 1u << 0,          /* overwrite logits with d loss / d logits     */
+  CE_F_CHECK_TARGETS = 1u << 4, /* wait for the GPU; CE_E_TARGET_RANGE if any  */
+                                /* target is outside [0, V) and not ignored    */
+  CE_F_FORCE_FUSED = 1u << 5,   /* test hooks: pick the kernel path            */
+  CE_F_FORCE_SPLITV = 1u << 6,
+  CE_F_FORCE_SCALAR = 1u << 7
+};
+
+/* Kernel paths (ce_plan_path). */
+enum {
+  CE_PATH_FUSED = 1,   /* one workgroup per row, row kept on chip, 1 HBM read  */
+  CE_PATH_SPLITV = 2,  /* row split over workgroups: partials, then combine    */
+  CE_PATH_SCALAR = 3   /* rows not 16-byte aligned: element loads, two passes  */
+};
+
+/* Bytes of device workspace ce_forward needs for this problem (>= 256).
+ * Returns 0 for invalid sizes or dtype. */
+size_t ce_workspace_bytes(int64_t rows, int64_t V, int dtype, uint32_t flags);
+
+/* The kernel path ce_forward would take (CE_PATH_*), or a negative
+ * ce_status for invalid arguments. Host only; nothing is enqueued. */
+int ce_plan_path(const void* logits, int dtype, int64_t rows, int64_t V, int64_t row_stride,
+                 const float* weight, float label_smoothing, uint32_t flags);
+
+/* Fused forward (+ gradient with CE_F_GRAD).
+ *  logits     [device] (rows, row_stride) row-major, dtype `dtype`; the first V
+ *             elements of each row are the logits. With CE_F_GRAD they are
+ *             overwritten by the gradient in the same dtype (bf16: round to
+ *             nearest even); otherwise they are only read.
+ *  target     [device] int64 (rows).
+ *  weight     [device] fp32 (V) class weights, or NULL.
+ *  softcap    0 = off; else > 0 and finite.
+ *  label_smoothing in [0, 1]; lse_square_scale finite, >= 0.
+ *  loss       [device] fp32: 1 value (mean, sum) or rows values (none).
+ *  z_loss     [device] fp32, same shape as loss, or NULL.
+ *  token_accuracy [device] fp32, same shape as loss, or NULL.
+ *  argmax     [device] int64 (rows), or NULL.
+ *  counts     [device] int64 [n_counted, n_correct], or NULL.
+ *  workspace  [device] >= ce_workspace_bytes(...) bytes, 256-byte aligned,
+ *             zero-filled before its first use (one hipMemset). Every call
+ *             leaves it reusable: later calls on the same stream may pass it
+ *             again without clearing. Two calls in flight at once must not
+ *             share a workspace.
+ */
+ce_status ce_forward(void* logits, int dtype, int64_t rows, int64_t V, int64_t row_stride,
+                     const int64_t* target, const float* weight, int64_t ignore_index,
+                     float label_smoothing, float lse_square_scale, float softcap,
+                     int reduction, uint32_t flags, float* loss, float* z_loss,
+                     float* token_accuracy, int64_t* argmax, int64_t* counts, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* Backward: grad (rows, row_stride) [device] *= grad_output in place.
+ *  grad_output [device] fp32: one value, or rows values when per_row != 0
+ *  (reduction none). Rows whose scale is exactly 1.0 are left untouched. */
+ce_status ce_backward(void* grad, int dtype, int64_t rows, int64_t V, int64_t row_stride,
+                      const float* grad_output, int per_row, void* stream);
+
+/* Static, human-readable text of a ce_status value. */
+const char* ce_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CE_MI355X_H */

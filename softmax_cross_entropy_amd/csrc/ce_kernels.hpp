@@ -1,0 +1,682 @@
+// Kernel templates of the fused softmax cross-entropy forward + gradient.
+//
+// The method (Liger-Kernel page "Kernel Profile: CrossEntropy (Tier 3 -
+// Fused/Complex)", Key Patterns): per row, an online softmax pass gives the
+// max and log-sum-exp, a second pass writes softmax minus the smoothed
+// one-hot over the logits in place (gradient-in-forward), and the backward
+// only rescales that gradient by grad_output.
+//
+// MI355X design (not the page's Triton loop):
+//  * chunk_kernel<FUSED=true>: one workgroup per row. The whole row is read
+//    from HBM once with dwordx4 loads and kept on chip (VGPRs, plus LDS
+//    filled by global_load_lds for the largest rows), so the gradient pass
+//    reads registers instead of re-reading HBM: 1 read + 1 write per logit.
+//  * chunk_kernel<FUSED=false> + splitv_finish_kernel: the row is split into
+//    S chunks held by different workgroups; stage 1 writes per-chunk
+//    partials (max, sum, argmax, target logit), stage 2 combines them in a
+//    fixed order and writes its chunk's gradient. For rows that exceed one
+//    CU's on-chip storage or for batches with too few rows to fill 256 CUs.
+//  * row_scalar_kernel: rows that are not 16-byte aligned (any V, any
+//    stride); element loads, same math.
+//  * prologue_kernel: n, D = sum w[target], W = sum w, the mean scales and
+//    the target range check, needed before any gradient is written.
+//  * backward_kernel: grad *= grad_output (scalar or per row), in place.
+#pragma once
+
+#include "ce_device.hpp"
+
+namespace cedev {
+
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// Softcapped value z = c tanh(x / c) (Liger-Kernel CE profile, Forward Pass:
+// softcap; the tanh form is the reading taken for "softcapping").
+template <int SC>
+__device__ __forceinline__ float zval(const Params& p, float x) {
+  if constexpr (SC) {
+    return p.softcap * tanh_f(x * p.inv_softcap);
+  } else {
+    return x;
+  }
+}
+
+// Weights of the EPV classes of vector jg (weighted smoothing only).
+template <class E>
+__device__ __forceinline__ void load_w(const float* w, int64_t jg, float (&wk)[E::EPV]) {
+  const f4* wv = reinterpret_cast<const f4*>(w + jg * E::EPV);
+#pragma unroll
+  for (int q = 0; q < E::EPV / 4; ++q) {
+    const f4 t = wv[q];
+    wk[4 * q + 0] = t[0];
+    wk[4 * q + 1] = t[1];
+    wk[4 * q + 2] = t[2];
+    wk[4 * q + 3] = t[3];
+  }
+}
+
+// Pass 1 over one vector: raw max and its first slot (argmax), online
+// (max, sum exp) of the softcapped values, and the smoothing sum.
+template <class E, int SC, int SM>
+__device__ __forceinline__ void pass1_vec(const Params& p, Acc& a, const float (&f)[E::EPV],
+                                          int slot, int64_t jg) {
+  constexpr int EPV = E::EPV;
+  float vm = f[0];
+#pragma unroll
+  for (int i = 1; i < EPV; ++i) vm = __builtin_fmaxf(vm, f[i]);
+  const bool take = vm > a.bv;
+  a.bv = take ? vm : a.bv;
+  a.bi = take ? slot : a.bi;
+
+  float z[EPV];
+  if constexpr (SC) {
+    float u[EPV], t[EPV];
+#pragma unroll
+    for (int i = 0; i < EPV; ++i) u[i] = f[i] * p.inv_softcap;
+    tanh_vec<EPV>(u, t);
+#pragma unroll
+    for (int i = 0; i < EPV; ++i) z[i] = p.softcap * t[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < EPV; ++i) z[i] = f[i];
+  }
+  float zm = vm;
+  if constexpr (SC) {
+    zm = z[0];
+#pragma unroll
+    for (int i = 1; i < EPV; ++i) zm = __builtin_fmaxf(zm, z[i]);
+  }
+  const float mn = __builtin_fmaxf(a.m, zm);
+  float e[EPV];
+#pragma unroll
+  for (int i = 0; i < EPV; ++i) e[i] = ex2((z[i] - mn) * kLog2e);
+#pragma unroll
+  for (int h = EPV / 2; h >= 1; h >>= 1) {
+#pragma unroll
+    for (int i = 0; i < h; ++i) e[i] += e[i + h];
+  }
+  a.s = a.s * ex2((a.m - mn) * kLog2e) + e[0];
+  a.m = mn;
+  if constexpr (SM) {
+    if (p.weight) {
+      float wk[EPV];
+      load_w<E>(p.weight, jg, wk);
+#pragma unroll
+      for (int i = 0; i < EPV; ++i) a.sz = __builtin_fmaf(wk[i], z[i], a.sz);
+    } else {
+      float t = 0.0f;
+#pragma unroll
+      for (int i = 0; i < EPV; ++i) t += z[i];
+      a.sz += t;
+    }
+  }
+}
+
+// Pass 1 over one scalar element (row tails and the unaligned path).
+template <int SC, int SM>
+__device__ __forceinline__ void pass1_one(const Params& p, Acc& a, float x, int slot, int64_t k) {
+  const bool take = x > a.bv;
+  a.bv = take ? x : a.bv;
+  a.bi = take ? slot : a.bi;
+  const float z = zval<SC>(p, x);
+  const float mn = __builtin_fmaxf(a.m, z);
+  a.s = a.s * ex2((a.m - mn) * kLog2e) + ex2((z - mn) * kLog2e);
+  a.m = mn;
+  if constexpr (SM) {
+    a.sz = p.weight ? __builtin_fmaf(p.weight[k], z, a.sz) : a.sz + z;
+  }
+}
+
+// Gradient of one element: ((p_k A - B w_k - C [k = y]) * dz/dx), with t the
+// tanh of x / c (softcap only).
+template <int SC, int SM>
+__device__ __forceinline__ float grad_elem(const Params& p, const RowScalars& rs, float x, float t,
+                                           float wk, bool is_y) {
+  float z = x;
+  if constexpr (SC) z = p.softcap * t;
+  const float pk = ex2(__builtin_fmaf(z - rs.m, kLog2e, -rs.l2s));
+  float g;
+  if constexpr (SM) {
+    g = __builtin_fmaf(pk, rs.A, -(rs.B * wk));
+  } else {
+    g = pk * rs.A;
+  }
+  g = is_y ? g - rs.C : g;
+  if constexpr (SC) g = g * __builtin_fmaf(-t, t, 1.0f);
+  return g;
+}
+
+template <int SC, int SM>
+__device__ __forceinline__ float grad_one(const Params& p, const RowScalars& rs, float x, float wk,
+                                          bool is_y) {
+  const float t = SC ? tanh_f(x * p.inv_softcap) : 0.0f;
+  return grad_elem<SC, SM>(p, rs, x, t, wk, is_y);
+}
+
+template <class E, int SC, int SM>
+__device__ __forceinline__ u4 grad_vec(const Params& p, const RowScalars& rs, const u4 v,
+                                       int64_t jg, int64_t y) {
+  constexpr int EPV = E::EPV;
+  float f[EPV], wk[EPV];
+  E::unpack(v, f);
+  if constexpr (SM) {
+    if (p.weight) {
+      load_w<E>(p.weight, jg, wk);
+    } else {
+#pragma unroll
+      for (int i = 0; i < EPV; ++i) wk[i] = 1.0f;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < EPV; ++i) wk[i] = 1.0f;
+  }
+  const int64_t d = y - jg * EPV;  // position of the target inside this vector, if any
+  float t[EPV];
+  if constexpr (SC) {
+    float u[EPV];
+#pragma unroll
+    for (int i = 0; i < EPV; ++i) u[i] = f[i] * p.inv_softcap;
+    tanh_vec<EPV>(u, t);
+  } else {
+#pragma unroll
+    for (int i = 0; i < EPV; ++i) t[i] = 0.0f;
+  }
+  float g[EPV];
+#pragma unroll
+  for (int i = 0; i < EPV; ++i) g[i] = grad_elem<SC, SM>(p, rs, f[i], t[i], wk[i], d == i);
+  return E::pack(g);
+}
+
+// Combine the per-wave Acc records in wave order (fixed, deterministic).
+template <int NW>
+__device__ __forceinline__ Acc block_combine(const Acc (&s)[NW]) {
+  Acc t = s[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) {
+    ms_combine(t.m, t.s, s[w].m, s[w].s);
+    t.sz += s[w].sz;
+    arg_combine(t.bv, t.bi, s[w].bv, s[w].bi);
+  }
+  return t;
+}
+
+// Scales of the row formulas: from the prologue when it ran (mean, weighted
+// smoothing), else the sum/none values alpha = beta = 1 and W = V.
+__device__ __forceinline__ void load_scales(const Params& p, double& W, double& alpha,
+                                            double& beta) {
+  if (p.has_hdr) {
+    W = p.hdr->W;
+    alpha = p.hdr->alpha;
+    beta = p.hdr->beta;
+  } else {
+    W = static_cast<double>(p.V);
+    alpha = 1.0;
+    beta = 1.0;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// chunk_kernel: FUSED = whole row per workgroup, single HBM read;
+//               !FUSED = split-V stage 1 (partials only).
+// Slots: thread tid owns vectors j = k * BLOCK + tid of its chunk for
+// k < NREG (registers) and NREG <= k < NREG + NLDS (LDS); the row tail
+// (V % EPV elements) is held by threads tid < tail.
+// ---------------------------------------------------------------------------
+template <class E, int BLOCK, int NREG, int NLDS, int SC, int SM, bool FUSED>
+__global__ __launch_bounds__(BLOCK) void chunk_kernel(Params p) {
+  constexpr int EPV = E::EPV;
+  constexpr int NS = NREG + NLDS;
+  constexpr int NW = BLOCK / 64;
+  __shared__ u4 lds_rows[NLDS > 0 ? NLDS * BLOCK : 1];
+  __shared__ Acc s_acc[NW];
+  __shared__ RowScalars s_rs;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int64_t row;
+  int c;
+  if constexpr (FUSED) {
+    row = blockIdx.x;
+    c = 0;
+  } else {
+    row = blockIdx.x / p.S;
+    c = blockIdx.x - static_cast<int>(row) * p.S;
+  }
+  const int64_t y = p.target[row];
+  const bool ignored = (y == p.ignore_index);
+  const bool bad = !ignored && (y < 0 || y >= p.V);
+  char* rp = row_ptr(p, row, E::BYTES);
+  const int nvec_row = static_cast<int>(p.V / EPV);
+  const int tail = static_cast<int>(p.V - static_cast<int64_t>(nvec_row) * EPV);
+  int v0, v1;
+  bool has_tail;
+  if constexpr (FUSED) {
+    v0 = 0;
+    v1 = nvec_row;
+    has_tail = tail > 0;
+  } else {
+    v0 = c * p.chunk_vec;
+    v1 = min(v0 + p.chunk_vec, nvec_row);
+    has_tail = (c == p.S - 1) && tail > 0;
+  }
+  const int nv = v1 - v0;
+  u4* vp = reinterpret_cast<u4*>(rp) + v0;
+
+  if (ignored || bad) {
+    if constexpr (FUSED) {
+      // Ignored rows are never read; their gradient is exactly +0.0
+      // (tt-mlir PR #9324 page: ignored rows, also with non-finite logits).
+      if (p.grad) {
+        for (int j = tid; j < nv; j += BLOCK) vp[j] = u4{0u, 0u, 0u, 0u};
+        if (has_tail && tid < tail) E::st(rp, static_cast<int64_t>(nvec_row) * EPV + tid, 0.0f);
+      }
+      if (tid == 0) {
+        const float q = bad ? __builtin_nanf("") : 0.0f;
+        write_row_outputs(p, row, q, q, 0, 0, -1);
+      }
+      if (p.epilogue) epilogue_arrive<BLOCK>(p, gridDim.x);
+    }
+    return;
+  }
+
+  // ---- issue every load of the chunk up front ----
+  u4 r[NREG > 0 ? NREG : 1];
+#pragma unroll
+  for (int k = 0; k < NREG; ++k) {
+    const int j = k * BLOCK + tid;
+    r[k] = (j < nv) ? vp[j] : u4{0u, 0u, 0u, 0u};
+  }
+#pragma unroll
+  for (int k = 0; k < NLDS; ++k) {
+    const int j = (NREG + k) * BLOCK + tid;
+    if (j < nv) {
+      __builtin_amdgcn_global_load_lds(
+          static_cast<const void*>(vp + j),
+          (lds_void_ptr)(lds_rows + k * BLOCK + wave * 64), 16, 0, 0);
+    }
+  }
+  const int64_t tail0 = static_cast<int64_t>(nvec_row) * EPV;
+  float xt = 0.0f;
+  if (has_tail && tid < tail) xt = E::ld(rp, tail0 + tid);
+  const bool y_here = FUSED || (y >= static_cast<int64_t>(v0) * EPV &&
+                                y < static_cast<int64_t>(v1) * EPV) ||
+                      (has_tail && y >= tail0);
+  float xy = 0.0f;
+  if (tid == 0 && y_here) xy = E::ld(rp, y);
+
+  // ---- pass 1: online max / sum, argmax, smoothing sum ----
+  Acc a;
+  acc_init(a);
+#pragma unroll
+  for (int k = 0; k < NS; ++k) {
+    const int j = k * BLOCK + tid;
+    if (j < nv) {
+      const u4 v = (k < NREG) ? r[k < NREG ? k : 0] : lds_rows[(k - NREG) * BLOCK + tid];
+      float f[EPV];
+      E::unpack(v, f);
+      pass1_vec<E, SC, SM>(p, a, f, v0 + j, static_cast<int64_t>(v0) + j);
+    }
+  }
+  if (has_tail && tid < tail) pass1_one<SC, SM>(p, a, xt, nvec_row + tid, tail0 + tid);
+
+  wave_reduce(a);
+  if (lane == 0) s_acc[wave] = a;
+  __syncthreads();
+  const Acc t = block_combine<NW>(s_acc);
+
+  // ---- argmax: the owner of the winning slot finds the first position ----
+  __shared__ int s_arg;
+  if (t.bi >= nvec_row) {
+    if (tid == 0) s_arg = (t.bi == kNoIndex) ? 0 : static_cast<int>(tail0) + (t.bi - nvec_row);
+  } else {
+    const int jl = t.bi - v0;
+    if (jl % BLOCK == tid) {
+      const int kk = jl / BLOCK;
+      int pos = 0;
+#pragma unroll
+      for (int k = 0; k < NS; ++k) {
+        if (k == kk) {
+          const u4 v = (k < NREG) ? r[k < NREG ? k : 0] : lds_rows[(k - NREG) * BLOCK + tid];
+          float f[EPV];
+          E::unpack(v, f);
+#pragma unroll
+          for (int i = EPV - 1; i >= 0; --i) pos = (f[i] == t.bv) ? i : pos;
+        }
+      }
+      s_arg = t.bi * EPV + pos;
+    }
+  }
+  __syncthreads();
+  const int arg = s_arg;
+
+  if constexpr (!FUSED) {
+    if (tid == 0) {
+      Partial q;
+      q.m = t.m;
+      q.s = t.s;
+      q.sz = t.sz;
+      q.bv = t.bv;
+      q.bi = arg;
+      q.xy = xy;
+      q.has_y = y_here ? 1 : 0;
+      q.pad = 0;
+      p.part[row * p.S + c] = q;
+    }
+    return;
+  } else {
+    if (tid == 0) {
+      double W, alpha, beta;
+      load_scales(p, W, alpha, beta);
+      const float wy = p.weight ? p.weight[y] : 1.0f;
+      RowScalars rs;
+      row_scalars(rs, t.m, t.s, t.sz, zval<SC>(p, xy), wy, W, static_cast<double>(p.V),
+                  p.eps, p.lam, alpha, beta);
+      rs.arg = arg;
+      rs.ok = (arg == y);
+      s_rs = rs;
+      write_row_outputs(p, row, rs.ce, rs.zl, rs.ok, 1, arg);
+    }
+    __syncthreads();
+
+    // ---- pass 2: gradient from on-chip data, written over the logits ----
+    if (p.grad) {
+      const RowScalars rs = s_rs;
+#pragma unroll
+      for (int k = 0; k < NS; ++k) {
+        const int j = k * BLOCK + tid;
+        if (j < nv) {
+          const u4 v = (k < NREG) ? r[k < NREG ? k : 0] : lds_rows[(k - NREG) * BLOCK + tid];
+          const u4 g = grad_vec<E, SC, SM>(p, rs, v, j, y);
+          __builtin_nontemporal_store(g, vp + j);
+        }
+      }
+      if (has_tail && tid < tail) {
+        const int64_t k = tail0 + tid;
+        const float wk = (SM && p.weight) ? p.weight[k] : 1.0f;
+        E::st(rp, k, grad_one<SC, SM>(p, rs, xt, wk, k == y));
+      }
+    }
+    if (p.epilogue) epilogue_arrive<BLOCK>(p, gridDim.x);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split-V stage 2: combine the S partials of the row (same order in every
+// chunk's workgroup, so every chunk sees identical row scalars), then
+// re-read this chunk and write its gradient.
+// ---------------------------------------------------------------------------
+template <class E, int BLOCK, int SC, int SM>
+__global__ __launch_bounds__(BLOCK) void splitv_finish_kernel(Params p) {
+  constexpr int EPV = E::EPV;
+  constexpr int U = 4;
+  __shared__ RowScalars s_rs;
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x / p.S;
+  const int c = blockIdx.x - static_cast<int>(row) * p.S;
+  const int64_t y = p.target[row];
+  const bool ignored = (y == p.ignore_index);
+  const bool bad = !ignored && (y < 0 || y >= p.V);
+  char* rp = row_ptr(p, row, E::BYTES);
+  const int nvec_row = static_cast<int>(p.V / EPV);
+  const int tail = static_cast<int>(p.V - static_cast<int64_t>(nvec_row) * EPV);
+  const int v0 = c * p.chunk_vec;
+  const int v1 = min(v0 + p.chunk_vec, nvec_row);
+  const bool has_tail = (c == p.S - 1) && tail > 0;
+  const int nv = v1 - v0;
+  u4* vp = reinterpret_cast<u4*>(rp) + v0;
+  const int64_t tail0 = static_cast<int64_t>(nvec_row) * EPV;
+
+  if (ignored || bad) {
+    if (p.grad) {
+      for (int j = tid; j < nv; j += BLOCK) vp[j] = u4{0u, 0u, 0u, 0u};
+      if (has_tail && tid < tail) E::st(rp, tail0 + tid, 0.0f);
+    }
+    if (c == 0 && tid == 0) {
+      const float q = bad ? __builtin_nanf("") : 0.0f;
+      write_row_outputs(p, row, q, q, 0, 0, -1);
+    }
+    if (p.epilogue) epilogue_arrive<BLOCK>(p, gridDim.x);
+    return;
+  }
+
+  if (tid == 0) {
+    const Partial* q = p.part + row * p.S;
+    float m = q[0].m, s = q[0].s, sz = q[0].sz, bv = q[0].bv, xy = q[0].xy;
+    int bi = q[0].bi;
+    for (int i = 1; i < p.S; ++i) {
+      ms_combine(m, s, q[i].m, q[i].s);
+      sz += q[i].sz;
+      arg_combine(bv, bi, q[i].bv, q[i].bi);
+      if (q[i].has_y) xy = q[i].xy;
+    }
+    double W, alpha, beta;
+    load_scales(p, W, alpha, beta);
+    const float wy = p.weight ? p.weight[y] : 1.0f;
+    RowScalars rs;
+    row_scalars(rs, m, s, sz, zval<SC>(p, xy), wy, W, static_cast<double>(p.V), p.eps, p.lam,
+                alpha, beta);
+    rs.arg = bi;
+    rs.ok = (bi == y);
+    s_rs = rs;
+    if (c == 0) write_row_outputs(p, row, rs.ce, rs.zl, rs.ok, 1, bi);
+  }
+  __syncthreads();
+  if (p.grad) {
+    const RowScalars rs = s_rs;
+    for (int j0 = 0; j0 < nv; j0 += BLOCK * U) {
+      u4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = j0 + u * BLOCK + tid;
+        v[u] = (j < nv) ? vp[j] : u4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = j0 + u * BLOCK + tid;
+        if (j < nv) {
+          const u4 g = grad_vec<E, SC, SM>(p, rs, v[u], static_cast<int64_t>(v0) + j, y);
+          __builtin_nontemporal_store(g, vp + j);
+        }
+      }
+    }
+    if (has_tail && tid < tail) {
+      const int64_t k = tail0 + tid;
+      const float xk = E::ld(rp, k);
+      const float wk = (SM && p.weight) ? p.weight[k] : 1.0f;
+      E::st(rp, k, grad_one<SC, SM>(p, rs, xk, wk, k == y));
+    }
+  }
+  if (p.epilogue) epilogue_arrive<BLOCK>(p, gridDim.x);
+}
+
+// ---------------------------------------------------------------------------
+// Unaligned rows: one workgroup per row, element loads, two passes (the
+// second re-reads the row).
+// ---------------------------------------------------------------------------
+template <class E, int BLOCK, int SC, int SM>
+__global__ __launch_bounds__(BLOCK) void row_scalar_kernel(Params p) {
+  constexpr int NW = BLOCK / 64;
+  __shared__ Acc s_acc[NW];
+  __shared__ RowScalars s_rs;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t row = blockIdx.x;
+  const int64_t y = p.target[row];
+  const bool ignored = (y == p.ignore_index);
+  const bool bad = !ignored && (y < 0 || y >= p.V);
+  char* rp = row_ptr(p, row, E::BYTES);
+  if (ignored || bad) {
+    if (p.grad)
+      for (int64_t k = tid; k < p.V; k += BLOCK) E::st(rp, k, 0.0f);
+    if (tid == 0) {
+      const float q = bad ? __builtin_nanf("") : 0.0f;
+      write_row_outputs(p, row, q, q, 0, 0, -1);
+    }
+    if (p.epilogue) epilogue_arrive<BLOCK>(p, gridDim.x);
+    return;
+  }
+  Acc a;
+  acc_init(a);
+  for (int64_t k = tid; k < p.V; k += BLOCK) pass1_one<SC, SM>(p, a, E::ld(rp, k), static_cast<int>(k), k);
+  wave_reduce(a);
+  if (lane == 0) s_acc[wave] = a;
+  __syncthreads();
+  if (tid == 0) {
+    const Acc t = block_combine<NW>(s_acc);
+    double W, alpha, beta;
+    load_scales(p, W, alpha, beta);
+    const float wy = p.weight ? p.weight[y] : 1.0f;
+    RowScalars rs;
+    row_scalars(rs, t.m, t.s, t.sz, zval<SC>(p, E::ld(rp, y)), wy, W, static_cast<double>(p.V),
+                p.eps, p.lam, alpha, beta);
+    rs.arg = t.bi;
+    rs.ok = (t.bi == y);
+    s_rs = rs;
+    write_row_outputs(p, row, rs.ce, rs.zl, rs.ok, 1, t.bi);
+  }
+  __syncthreads();
+  if (p.grad) {
+    const RowScalars rs = s_rs;
+    for (int64_t k = tid; k < p.V; k += BLOCK) {
+      const float wk = (SM && p.weight) ? p.weight[k] : 1.0f;
+      E::st(rp, k, grad_one<SC, SM>(p, rs, E::ld(rp, k), wk, k == y));
+    }
+  }
+  if (p.epilogue) epilogue_arrive<BLOCK>(p, gridDim.x);
+}
+
+// ---------------------------------------------------------------------------
+// Prologue (one workgroup): counted rows n, D = sum of w[target] over them,
+// W = sum of w, the target-range error bit, the mean scales
+// alpha = 1/D, beta = 1/n (0 when the denominator is 0: zero gradients for
+// an all-ignored mean, tt-mlir PR #9324 page, Copilot comments on the mean
+// reduction), and a reset arrival counter. Fixed-order sums: deterministic.
+// ---------------------------------------------------------------------------
+template <int kPrologueBlock>
+__global__ __launch_bounds__(kPrologueBlock) void prologue_kernel(Params p) {
+  constexpr int NW = kPrologueBlock / 64;
+  __shared__ double s_D[NW], s_W[NW];
+  __shared__ int64_t s_n[NW];
+  __shared__ uint32_t s_e[NW];
+  const int tid = threadIdx.x;
+  double D = 0.0, W = 0.0;
+  int64_t n = 0;
+  uint32_t err = 0;
+  for (int64_t r = tid; r < p.rows; r += kPrologueBlock) {
+    const int64_t y = p.target[r];
+    if (y != p.ignore_index) {
+      if (y >= 0 && y < p.V) {
+        n += 1;
+        D += p.weight ? static_cast<double>(p.weight[y]) : 1.0;
+      } else {
+        err = 1u;
+      }
+    }
+  }
+  if (p.weight)
+    for (int64_t k = tid; k < p.V; k += kPrologueBlock) W += static_cast<double>(p.weight[k]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    D += __shfl_xor(D, off, 64);
+    W += __shfl_xor(W, off, 64);
+    n += __shfl_xor(n, off, 64);
+    err |= __shfl_xor(err, off, 64);
+  }
+  if ((tid & 63) == 0) {
+    s_D[tid >> 6] = D;
+    s_W[tid >> 6] = W;
+    s_n[tid >> 6] = n;
+    s_e[tid >> 6] = err;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double tD = 0.0, tW = 0.0;
+    int64_t tn = 0;
+    uint32_t te = 0;
+    for (int w = 0; w < NW; ++w) {
+      tD += s_D[w];
+      tW += s_W[w];
+      tn += s_n[w];
+      te |= s_e[w];
+    }
+    Header* h = p.hdr;
+    h->D = tD;
+    h->W = p.weight ? tW : static_cast<double>(p.V);
+    h->n = tn;
+    if (p.reduction == 1) {
+      h->alpha = (tD != 0.0) ? static_cast<float>(1.0 / tD) : 0.0f;
+      h->beta = (tn != 0) ? static_cast<float>(1.0 / static_cast<double>(tn)) : 0.0f;
+    } else {
+      h->alpha = 1.0f;
+      h->beta = 1.0f;
+    }
+    h->err = te;
+    h->done = 0u;
+    if (p.rows == 0 && p.epilogue) {
+      // No row blocks will run: the reductions of an empty batch.
+      const double nan = __builtin_nan("");
+      if (p.reduction == 1) {
+        if (p.loss) p.loss[0] = static_cast<float>(nan);
+        if (p.z_loss) p.z_loss[0] = static_cast<float>(nan);
+      } else if (p.reduction == 2) {
+        if (p.loss) p.loss[0] = 0.0f;
+        if (p.z_loss) p.z_loss[0] = 0.0f;
+      }
+      if (p.reduction != 0 && p.acc) p.acc[0] = static_cast<float>(nan);
+      if (p.counts) {
+        p.counts[0] = 0;
+        p.counts[1] = 0;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Backward: the stored gradient times grad_output, in place (Liger-Kernel CE
+// profile, Backward Pass). A block whose scale is exactly 1 exits at once.
+// ---------------------------------------------------------------------------
+template <class E, bool VEC>
+__global__ __launch_bounds__(kBwdBlock) void backward_kernel(void* grad, int64_t V, int64_t stride,
+                                                             const float* go, int per_row,
+                                                             int blocks_per_row) {
+  constexpr int EPV = E::EPV;
+  const int64_t row = blockIdx.x / blocks_per_row;
+  const int b = blockIdx.x - static_cast<int>(row) * blocks_per_row;
+  const float g = per_row ? go[row] : go[0];
+  if (g == 1.0f) return;
+  char* rp = static_cast<char*>(grad) + row * stride * E::BYTES;
+  const int tid = threadIdx.x;
+  if constexpr (VEC) {
+    const int nvec = static_cast<int>(V / EPV);
+    u4* vp = reinterpret_cast<u4*>(rp);
+    const int j0 = b * kBwdBlock * kBwdUnroll;
+    u4 v[kBwdUnroll];
+#pragma unroll
+    for (int u = 0; u < kBwdUnroll; ++u) {
+      const int j = j0 + u * kBwdBlock + tid;
+      v[u] = (j < nvec) ? vp[j] : u4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kBwdUnroll; ++u) {
+      const int j = j0 + u * kBwdBlock + tid;
+      if (j < nvec) {
+        float f[EPV];
+        E::unpack(v[u], f);
+#pragma unroll
+        for (int i = 0; i < EPV; ++i) f[i] *= g;
+        __builtin_nontemporal_store(E::pack(f), vp + j);
+      }
+    }
+    if (b == blocks_per_row - 1) {
+      const int64_t tail0 = static_cast<int64_t>(nvec) * EPV;
+      if (tail0 + tid < V) E::st(rp, tail0 + tid, E::ld(rp, tail0 + tid) * g);
+    }
+  } else {
+    const int64_t span = static_cast<int64_t>(kBwdBlock) * kBwdUnroll;
+    const int64_t k0 = static_cast<int64_t>(b) * span;
+    for (int64_t k = k0 + tid; k < V && k < k0 + span; k += kBwdBlock) E::st(rp, k, E::ld(rp, k) * g);
+  }
+}
+
+}  // namespace cedev

@@ -1,0 +1,83 @@
+// Template launchers shared by the per-dtype instantiation units.
+#pragma once
+
+#include "ce_kernels.hpp"
+#include "ce_launch.hpp"
+
+namespace cehost {
+
+using cedev::Params;
+
+template <class E, int SC, int SM>
+hipError_t launch_fused(int shape, const Params& p, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(p.rows));
+  switch (shape) {
+    case 0: cedev::chunk_kernel<E, 256, 4, 0, SC, SM, true><<<grid, 256, 0, st>>>(p); break;
+    case 1: cedev::chunk_kernel<E, 256, 8, 0, SC, SM, true><<<grid, 256, 0, st>>>(p); break;
+    case 2: cedev::chunk_kernel<E, 256, 16, 0, SC, SM, true><<<grid, 256, 0, st>>>(p); break;
+    case 3: cedev::chunk_kernel<E, 512, 16, 0, SC, SM, true><<<grid, 512, 0, st>>>(p); break;
+    case 4: cedev::chunk_kernel<E, 512, 32, 0, SC, SM, true><<<grid, 512, 0, st>>>(p); break;
+    case 5: cedev::chunk_kernel<E, 512, 45, 19, SC, SM, true><<<grid, 512, 0, st>>>(p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <class E, int SC, int SM>
+hipError_t launch_splitv(int shape, const Params& p, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(p.rows * p.S));
+  switch (shape) {
+    case kSplitShapeSmall:
+      cedev::chunk_kernel<E, 256, 4, 0, SC, SM, false><<<grid, 256, 0, st>>>(p);
+      break;
+    case kSplitShapeLarge:
+      cedev::chunk_kernel<E, 512, 16, 0, SC, SM, false><<<grid, 512, 0, st>>>(p);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  cedev::splitv_finish_kernel<E, kSplitBlock, SC, SM><<<grid, kSplitBlock, 0, st>>>(p);
+  return hipGetLastError();
+}
+
+template <class E, int SC, int SM>
+hipError_t launch_path(const Plan& plan, const Params& p, hipStream_t st) {
+  switch (plan.path) {
+    case 1: return launch_fused<E, SC, SM>(plan.shape, p, st);
+    case 2: return launch_splitv<E, SC, SM>(plan.shape, p, st);
+    case 3:
+      cedev::row_scalar_kernel<E, kScalarBlock, SC, SM>
+          <<<dim3(static_cast<unsigned>(p.rows)), kScalarBlock, 0, st>>>(p);
+      return hipGetLastError();
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <class E>
+hipError_t launch_forward(const Plan& plan, const Params& p, hipStream_t st) {
+  const bool sc = p.softcap > 0.0f;
+  const bool sm = p.eps > 0.0f;
+  if (sc) return sm ? launch_path<E, 1, 1>(plan, p, st) : launch_path<E, 1, 0>(plan, p, st);
+  return sm ? launch_path<E, 0, 1>(plan, p, st) : launch_path<E, 0, 0>(plan, p, st);
+}
+
+template <class E>
+hipError_t launch_backward(void* grad, int64_t rows, int64_t V, int64_t stride, const float* go,
+                           int per_row, bool vec, hipStream_t st) {
+  const int64_t span = static_cast<int64_t>(cedev::kBwdBlock) * cedev::kBwdUnroll;
+  int64_t units = vec ? (V / E::EPV) : V;
+  int64_t bpr = (units + span - 1) / span;
+  if (bpr < 1) bpr = 1;
+  const dim3 grid(static_cast<unsigned>(rows * bpr));
+  if (vec) {
+    cedev::backward_kernel<E, true>
+        <<<grid, cedev::kBwdBlock, 0, st>>>(grad, V, stride, go, per_row, static_cast<int>(bpr));
+  } else {
+    cedev::backward_kernel<E, false>
+        <<<grid, cedev::kBwdBlock, 0, st>>>(grad, V, stride, go, per_row, static_cast<int>(bpr));
+  }
+  return hipGetLastError();
+}
+
+}  // namespace cehost

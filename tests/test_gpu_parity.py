@@ -1,0 +1,374 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Every case prints its name, shape, dtype, options and kernel path before it
+touches the GPU. Small cases compare every output element; the full-size
+workloads run in the benchmark's launch configuration (automatic path) and
+compare sampled rows with the oracle plus properties that hold at any size.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import rows_forward, summarize_targets
+from parity import (OracleRef, assert_acc_exact, assert_grad_close, assert_loss_close,
+                    host_logits)
+from softmax_cross_entropy_amd import _lib, backward_, forward_raw
+from softmax_cross_entropy_amd._lib import (CE_F_FORCE_FUSED, CE_F_FORCE_SCALAR,
+                                            CE_F_FORCE_SPLITV)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+PATH_FLAGS = {"auto": 0, "fused": CE_F_FORCE_FUSED, "splitv": CE_F_FORCE_SPLITV,
+              "scalar": CE_F_FORCE_SCALAR}
+
+
+def _announce(**kw):
+    print("CASE " + " ".join(f"{k}={v}" for k, v in kw.items()), flush=True)
+
+
+def _padded(x_cpu: torch.Tensor, stride: int) -> torch.Tensor:
+    """(rows, V) tensor on the GPU inside a (rows, stride) buffer."""
+    rows, V = x_cpu.shape
+    buf = torch.full((rows, stride), float("nan"), dtype=x_cpu.dtype, device=DEV)
+    buf[:, :V].copy_(x_cpu.to(DEV))
+    return buf[:, :V]
+
+
+def _plan(x, weight, eps, flags):
+    rows, V = x.shape
+    return _lib.PATH_NAMES.get(_lib.ce_plan_path(
+        x.data_ptr(), _lib.dtype_code(x.dtype), rows, V, x.stride(0),
+        0 if weight is None else weight.data_ptr(), eps, flags), "?")
+
+
+def run_case(x_cpu, t_cpu, *, weight=None, ignore_index=-100, eps=0.0, lam=0.0, softcap=None,
+             reduction="mean", path="auto", stride=None, name=""):
+    """Run GPU + oracle on the same inputs and compare every output."""
+    rows, V = x_cpu.shape
+    stride = V if stride is None else stride
+    x = _padded(x_cpu, stride)
+    t = t_cpu.to(DEV)
+    w = None if weight is None else weight.to(DEV)
+    flags = PATH_FLAGS[path]
+    _announce(name=name, rows=rows, V=V, stride=stride, dtype=x.dtype, eps=eps, lam=lam,
+              softcap=softcap, weight=weight is not None, reduction=reduction, path=path,
+              plan=_plan(x, w, eps, flags))
+    xh = host_logits(x_cpu)
+    loss, z, acc, arg, counts = forward_raw(
+        x, t, w, ignore_index, eps, lam, softcap, reduction, grad=True, z_loss=True,
+        token_accuracy=True, argmax=True, counts=True, flags=flags)
+    torch.cuda.synchronize()
+    ref = OracleRef(xh, t_cpu.numpy(), weight=None if weight is None else weight.numpy(),
+                    ignore_index=ignore_index, label_smoothing=eps, lse_square_scale=lam,
+                    softcap=softcap, reduction=reduction)
+    assert_loss_close(loss.cpu().numpy(), ref.loss, "loss")
+    assert_loss_close(z.cpu().numpy(), ref.z_loss, "z_loss")
+    np.testing.assert_array_equal(arg.cpu().numpy(), ref.argmax)
+    c = counts.cpu().numpy()
+    assert int(c[0]) == ref.summ.n and int(c[1]) == ref.n_correct
+    if reduction == "none":
+        np.testing.assert_array_equal(acc.cpu().numpy(), ref.acc.astype(np.float32))
+    else:
+        assert_acc_exact(acc.item(), ref.n_correct, ref.summ.n)
+    assert_grad_close(x, ref.grad, ref.mag, zero_rows=ref.not_counted)
+    if stride > V:  # padding columns untouched
+        pad = x.as_strided((rows, stride - V), (stride, 1), x.storage_offset() + V)
+        assert torch.isnan(pad.float()).all()
+    return x, ref
+
+
+# ---------------------------------------------------------------------------
+# The 64 x 4096 fp32 workload, every path and reduction
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("path", ["auto", "fused", "splitv", "scalar"])
+@pytest.mark.parametrize("reduction", ["mean", "sum", "none"])
+def test_small_workload(path, reduction):
+    w = synth.WORKLOADS["ce_64x4096_f32"]
+    inp = synth.make_inputs(w, "cpu")
+    run_case(inp.logits, inp.target, reduction=reduction, path=path, name=w.name)
+
+
+# ---------------------------------------------------------------------------
+# Options x dtype x path, ragged rows (V not a multiple of a vector)
+# ---------------------------------------------------------------------------
+
+OPTS = {
+    "plain": dict(),
+    "weight": dict(weight=True),
+    "smooth": dict(eps=0.1),
+    "weight_smooth": dict(weight=True, eps=0.2),
+    "softcap": dict(softcap=5.0),
+    "zloss": dict(lam=1e-3),
+    "all": dict(weight=True, eps=0.1, softcap=4.0, lam=1e-2),
+}
+
+
+@pytest.mark.parametrize("opt", list(OPTS))
+@pytest.mark.parametrize("path", ["fused", "splitv", "scalar"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("reduction", ["mean", "none"])
+def test_options_matrix(opt, path, dtype, reduction):
+    o = OPTS[opt]
+    rows, V = 37, 3001
+    x = synth.make_logits(rows, V, dtype, 3.0, 7)
+    t = synth.make_targets(rows, V, 7, 4)
+    wt = None
+    if o.get("weight"):
+        wt = 0.5 + 1.5 * torch.rand(V, generator=torch.Generator().manual_seed(9))
+    run_case(x, t, weight=wt, eps=o.get("eps", 0.0), lam=o.get("lam", 0.0),
+             softcap=o.get("softcap"), reduction=reduction, path=path, stride=3008,
+             name=f"opts-{opt}")
+
+
+@pytest.mark.parametrize("V", [1, 2, 3, 17, 4099, 8192])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("pad", [False, True])
+@pytest.mark.parametrize("rows", [1, 7])
+def test_edge_sizes(V, dtype, pad, rows):
+    x = synth.make_logits(rows, V, dtype, 2.0, 11 + V)
+    t = synth.make_targets(rows, V, 11 + V, 1 if rows > 1 else 0)
+    stride = (V + 7) // 8 * 8 + (8 if pad else 0) if pad else V
+    run_case(x, t, eps=0.05, lam=1e-3, reduction="mean", stride=stride, name="edge")
+    run_case(x, t, reduction="none", stride=stride, name="edge-none")
+
+
+def test_ignore_index_is_a_real_class():
+    rows, V = 50, 512
+    x = synth.make_logits(rows, V, torch.float32, 1.0, 21)
+    t = synth.make_targets(rows, V, 21, 0)
+    t[::3] = 5
+    run_case(x, t, ignore_index=5, reduction="mean", name="ignore5")
+
+
+def test_ties_in_argmax_bf16():
+    rows, V = 64, 2048
+    x = torch.randint(-3, 3, (rows, V), generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
+    t = synth.make_targets(rows, V, 3, 0)
+    for path in ("fused", "splitv", "scalar"):
+        run_case(x, t, reduction="none", path=path, name="ties")
+
+
+def test_large_logit_spikes_exact_zero_loss():
+    rows, V = 16, 4096
+    x = synth.make_logits(rows, V, torch.float32, 1.0, 31)
+    t = synth.make_targets(rows, V, 31, 0)
+    for r in range(0, rows, 2):
+        x[r, t[r]] = 80.0
+    for r in range(1, rows, 2):
+        x[r, (int(t[r]) + 7) % V] = 80.0
+    for path in ("fused", "splitv", "scalar"):
+        _, ref = run_case(x, t, reduction="none", path=path, name="spikes")
+        assert np.all(ref.ce[::2] == 0.0)
+
+
+# ---------------------------------------------------------------------------
+# Ignored rows, all-ignored batches, targets out of range
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("path", ["auto", "fused", "splitv", "scalar"])
+def test_all_ignored_nonfinite_small(path):
+    rows, V = 64, 1024
+    x = synth.make_logits(rows, V, torch.bfloat16, 1.0, 41)
+    x[0::4] = float("nan")
+    x[1::4] = float("inf")
+    x[2::4] = float("-inf")
+    t = torch.full((rows,), -100, dtype=torch.int64)
+    _announce(name="all-ignored-small", path=path)
+    xd = x.to(DEV)
+    loss, z, acc, arg, counts = forward_raw(xd, t.to(DEV), lse_square_scale=1e-4, z_loss=True,
+                                            token_accuracy=True, argmax=True, counts=True,
+                                            flags=PATH_FLAGS[path])
+    torch.cuda.synchronize()
+    assert math.isnan(loss.item()) and math.isnan(z.item()) and math.isnan(acc.item())
+    assert counts.tolist() == [0, 0]
+    assert (arg == -1).all()
+    assert (xd.view(torch.int16) == 0).all()
+
+
+def test_all_ignored_full_size():
+    w = synth.WORKLOADS["ce_512x262144_bf16_allignored"]
+    _announce(name=w.name, rows=w.rows, V=w.V)
+    inp = synth.make_inputs(w, DEV)
+    loss, z, acc, arg, counts = forward_raw(inp.logits, inp.target, z_loss=True,
+                                            token_accuracy=True, argmax=True, counts=True)
+    torch.cuda.synchronize()
+    assert math.isnan(loss.item()) and math.isnan(z.item()) and math.isnan(acc.item())
+    assert counts.tolist() == [0, 0]
+    assert (inp.logits.view(torch.int16) == 0).all()
+    s, _, _, _, _ = forward_raw(synth.make_inputs(w, DEV).logits, inp.target, reduction="sum")
+    assert s.item() == 0.0
+
+
+def test_bad_targets():
+    rows, V = 8, 300
+    x = synth.make_logits(rows, V, torch.float32, 1.0, 51)
+    t = torch.tensor([0, 300, -1, -100, 5, 299, 1000, 7])
+    run_case(x, t, reduction="none", name="bad-targets")
+    run_case(x, t, reduction="mean", name="bad-targets-mean")
+    _announce(name="bad-targets-check")
+    with pytest.raises(_lib.CEError) as e:
+        forward_raw(x.to(DEV), t.to(DEV), check_targets=True)
+    assert e.value.status == _lib.CE_E_TARGET_RANGE
+    ok = t.clone()
+    ok[[1, 2, 6]] = 3
+    forward_raw(x.to(DEV), ok.to(DEV), check_targets=True)
+
+
+def test_zero_weight_mean():
+    rows, V = 6, 40
+    x = synth.make_logits(rows, V, torch.float32, 1.0, 53)
+    t = torch.tensor([1, 2, 3, 1, 2, 3])
+    w = torch.ones(V)
+    w[1:4] = 0.0
+    run_case(x, t, weight=w, reduction="mean", name="zero-weight")
+
+
+def test_empty_batch():
+    _announce(name="empty")
+    x = torch.empty((0, 100), device=DEV)
+    t = torch.empty((0,), dtype=torch.int64, device=DEV)
+    loss, _, acc, _, counts = forward_raw(x, t, reduction="mean", token_accuracy=True, counts=True)
+    assert math.isnan(loss.item()) and math.isnan(acc.item()) and counts.tolist() == [0, 0]
+    loss, _, _, _, _ = forward_raw(x, t, reduction="sum")
+    assert loss.item() == 0.0
+
+
+# ---------------------------------------------------------------------------
+# Backward (scale by grad_output), determinism, path cross-check
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("go", [1.0, 2.0, 0.37, "rows"])
+@pytest.mark.parametrize("aligned", [True, False])
+def test_backward_scale(dtype, go, aligned):
+    rows, V = 33, 5003
+    stride = 5008 if aligned else V
+    x = synth.make_logits(rows, V, dtype, 2.0, 61)
+    t = synth.make_targets(rows, V, 61, 3)
+    red = "none" if go == "rows" else "mean"
+    _announce(name="backward", dtype=dtype, go=go, aligned=aligned)
+    xd = _padded(x, stride)
+    forward_raw(xd, t.to(DEV), reduction=red)
+    g0 = xd.detach().clone()
+    if go == "rows":
+        gov = torch.linspace(-2.0, 3.0, rows)
+        gov[5] = 1.0
+    else:
+        gov = torch.tensor(go)
+    backward_(xd, gov.to(DEV), per_row=(go == "rows"))
+    torch.cuda.synchronize()
+    # The backward is one multiply per element in float32, rounded to the dtype.
+    want = (g0.float().cpu() * gov.float().reshape(-1, 1 if go == "rows" else 1)).to(dtype)
+    assert torch.equal(xd.cpu().view(torch.int16 if dtype == torch.bfloat16 else torch.int32),
+                       want.view(torch.int16 if dtype == torch.bfloat16 else torch.int32))
+
+
+def test_determinism_bitwise():
+    x = synth.make_logits(512, 32768, torch.bfloat16, 2.0, 71)
+    t = synth.make_targets(512, 32768, 71, 20)
+    outs = []
+    for path in ("fused", "splitv", "fused", "splitv"):
+        _announce(name="determinism", path=path)
+        xd = x.to(DEV)
+        r = forward_raw(xd, t.to(DEV), label_smoothing=0.1, lse_square_scale=1e-3,
+                        z_loss=True, token_accuracy=True, argmax=True, counts=True,
+                        flags=PATH_FLAGS[path])
+        torch.cuda.synchronize()
+        outs.append((xd.cpu(), [o.cpu() for o in r]))
+    for a, b in ((0, 2), (1, 3)):
+        assert torch.equal(outs[a][0].view(torch.int16), outs[b][0].view(torch.int16))
+        for oa, ob in zip(outs[a][1], outs[b][1]):
+            assert torch.equal(oa, ob)
+    # fused vs split-V: identical integers, floats within the parity bar of each other
+    assert torch.equal(outs[0][1][3], outs[1][1][3])
+    assert torch.equal(outs[0][1][4], outs[1][1][4])
+    assert abs(outs[0][1][0].item() - outs[1][1][0].item()) <= 1e-5 * abs(outs[0][1][0].item())
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads in the benchmark's launch configuration
+# ---------------------------------------------------------------------------
+
+def _sample_rows(rows, k, seed, extra=()):
+    g = np.random.default_rng(seed)
+    s = set(g.choice(rows, size=min(k, rows), replace=False).tolist())
+    s.update([0, rows - 1])
+    s.update(int(e) for e in extra)
+    return np.array(sorted(s))
+
+
+def _full_workload(name, reductions=None, k=48):
+    w = synth.WORKLOADS[name]
+    for red in reductions or w.reductions:
+        _announce(name=w.name, rows=w.rows, V=w.V, dtype=w.dtype, reduction=red)
+        inp = synth.make_inputs(w, DEV)
+        t_host = inp.target.cpu().numpy()
+        ign = np.nonzero(t_host == -100)[0][:4]
+        sel = _sample_rows(w.rows, k, w.seed, list(inp.spike_rows) + list(ign))
+        xh = host_logits(inp.logits[torch.from_numpy(sel).to(DEV)])
+        wh = None if inp.weight is None else inp.weight.cpu().numpy()
+        x = inp.logits
+        loss, z, acc, arg, counts = forward_raw(
+            x, inp.target, inp.weight, -100, w.label_smoothing, w.lse_square_scale,
+            w.softcap or None, red, grad=True, z_loss=True, token_accuracy=True, argmax=True,
+            counts=True)
+        torch.cuda.synchronize()
+        # sampled rows: per-row values (from a "none" run when reducing) and gradients
+        summ = summarize_targets(t_host, w.V, -100, wh, red)
+        rr = rows_forward(xh, t_host[sel], V=w.V, alpha=summ.alpha, beta=summ.beta, weight=wh,
+                          label_smoothing=w.label_smoothing, lse_square_scale=w.lse_square_scale,
+                          softcap=w.softcap or None, want_grad=True, want_mag=True)
+        assert_grad_close(x[torch.from_numpy(sel).to(DEV)], rr.grad, rr.mag,
+                          zero_rows=~summ.counted[sel], what=f"{w.name} grad")
+        np.testing.assert_array_equal(arg.cpu().numpy()[sel], rr.argmax)
+        c = counts.cpu().numpy()
+        am = arg.cpu().numpy()
+        n_correct = int(np.sum((am == t_host) & summ.counted))
+        assert int(c[0]) == summ.n and int(c[1]) == n_correct
+        if red == "none":
+            assert_loss_close(loss.cpu().numpy()[sel], rr.ce + rr.zeta, "per-row loss")
+            assert_loss_close(z.cpu().numpy()[sel], rr.zeta, "per-row z_loss")
+            per_row_ce = loss.double().cpu().numpy() - z.double().cpu().numpy()
+            per_row_z = z.double().cpu().numpy()
+        else:
+            assert_acc_exact(acc.item(), n_correct, summ.n)
+            # per-row values of the same batch from a "none" run
+            inp2 = synth.make_inputs(w, DEV)
+            l2, z2, _, _, _ = forward_raw(inp2.logits, inp2.target, inp2.weight, -100,
+                                          w.label_smoothing, w.lse_square_scale,
+                                          w.softcap or None, "none", grad=False, z_loss=True)
+            del inp2
+            assert_loss_close(l2.cpu().numpy()[sel], rr.ce + rr.zeta, "per-row loss")
+            assert_loss_close(z2.cpu().numpy()[sel], rr.zeta, "per-row z_loss")
+            per_row_z = z2.double().cpu().numpy()
+            per_row_ce = l2.double().cpu().numpy() - per_row_z
+            with np.errstate(divide="ignore", invalid="ignore"):
+                if red == "mean":
+                    want = per_row_ce.sum() / summ.D + per_row_z.sum() / summ.n
+                else:
+                    want = per_row_ce.sum() + per_row_z.sum()
+            # the reduction of the per-row values (each within the parity bar)
+            assert abs(loss.item() - want) <= 2e-6 * abs(want), (loss.item(), want)
+        del inp, x
+
+
+def test_full_c2_bf16_accuracy_argmax():
+    _full_workload("ce_4096x32768_bf16")
+
+
+def test_full_c3_f32_large_vocab():
+    _full_workload("ce_1023x128256_f32")
+
+
+def test_full_c4_bf16_all_options():
+    _full_workload("ce_4096x131072_bf16_opts", k=24)
+
+
+def test_full_c5_bf16_huge():
+    _full_workload("ce_16384x262144_bf16", k=16)
