@@ -143,16 +143,24 @@ class RowResult:
     argmax: np.ndarray    # int64 (r,): first index of the raw maximum, -1 if not counted
     correct: np.ndarray   # bool (r,): argmax == target on counted rows
     grad: Optional[np.ndarray]  # float64 (r, V) d(loss)/d(logits), or None
+    mag: Optional[np.ndarray] = None  # float64 (r, V) sum of |gradient terms| (want_mag)
 
 
 def rows_forward(x_rows, target_rows, *, V: int, alpha: float, beta: float,
                  weight=None, ignore_index: int = -100, label_smoothing: float = 0.0,
                  lse_square_scale: float = 0.0, softcap: Optional[float] = None,
-                 want_grad: bool = True) -> RowResult:
+                 want_grad: bool = True, want_mag: bool = False) -> RowResult:
     """Loss terms, argmax and gradient of a block of rows.
 
     alpha and beta come from summarize_targets over the whole batch, so a
     sample of rows gives the same values as the full computation.
+
+    want_mag also returns, per element, the sum of the absolute values of
+    the gradient's terms (alpha (1-eps) w_y p_k, alpha (1-eps) w_y [k = y],
+    alpha (eps/V) W p_k, alpha (eps/V) w_k, beta 2 lam |lse| p_k) times the
+    softcap factor: the scale at which cancellation between them loses
+    precision in a float32 evaluation. It is used only to size the bfloat16
+    gradient tolerance.
     """
     x = widen(x_rows)
     if x.ndim != 2 or x.shape[1] != V:
@@ -176,6 +184,7 @@ def rows_forward(x_rows, target_rows, *, V: int, alpha: float, beta: float,
     argmax = np.full(r, -1, dtype=np.int64)
     correct = np.zeros(r, dtype=bool)
     grad = np.zeros((r, V)) if want_grad else None
+    mag = np.zeros((r, V)) if want_mag else None
     ce[bad] = np.nan
     zeta[bad] = np.nan
 
@@ -212,7 +221,17 @@ def rows_forward(x_rows, target_rows, *, V: int, alpha: float, beta: float,
             if c > 0.0:
                 g = g * (1.0 - th * th)                       # chain through z = c tanh(x/c)
             grad[idx] = g
-    return RowResult(ce, zeta, lse_out, argmax, correct, grad)
+        if want_mag:
+            p = np.exp(logp)
+            onehot = np.zeros_like(p)
+            onehot[np.arange(idx.size), y] = 1.0
+            mg = (abs(alpha) * (1.0 - eps) * w_y[:, None] * (p + onehot)
+                  + abs(alpha) * (eps / V) * (W * p + w[None, :])
+                  + abs(beta) * 2.0 * lam * np.abs(lse) * p)
+            if c > 0.0:
+                mg = mg * (1.0 - th * th)
+            mag[idx] = mg
+    return RowResult(ce, zeta, lse_out, argmax, correct, grad, mag)
 
 
 @dataclass
