@@ -93,7 +93,9 @@ bool is_aligned(const void* logits, int dtype, int64_t row_stride, const float* 
 
 void make_plan(const void* logits, int dtype, int64_t rows, int64_t V, int64_t row_stride,
                const float* weight, float eps, uint32_t flags, Plan* pl) {
-  if ((flags & CE_F_FORCE_SCALAR) || !is_aligned(logits, dtype, row_stride, weight, eps)) {
+  // The vector paths need at least one whole 16-byte vector per row.
+  if ((flags & CE_F_FORCE_SCALAR) || V < elems_per_vec(dtype) ||
+      !is_aligned(logits, dtype, row_stride, weight, eps)) {
     pl->path = CE_PATH_SCALAR;
     pl->shape = 0;
     pl->S = 1;

@@ -288,29 +288,47 @@ __device__ __forceinline__ void row_scalars(RowScalars& r, float m, float s, flo
 }
 
 // ---------------------------------------------------------------------------
-// Last-block epilogue: every participating block bumps the arrival counter
-// after publishing its per-row values; the block that arrives last reduces
+// Last-block epilogue: every participating block publishes its per-row
+// values and bumps an arrival counter; the block that arrives last reduces
 // the per-row arrays in a fixed order (bitwise deterministic) in fp64.
 // Reductions: Liger-Kernel CE profile, forward_outputs (scalar loss, or per
 // row for "none"); the PR #9324 page's fallback lowering (none returns rows,
 // sum and mean reduce); IEEE 0/0 = NaN keeps the all-ignored mean NaN.
+//
+// Publication without an L2 write-back: the per-row values are written with
+// device-scope atomic stores (they write through the per-XCD L2 to the
+// device-coherent level), the writer waits for those stores to complete
+// (s_waitcnt 0) before its arrival atomic, and the last block reads them
+// back with device-scope atomic loads. An agent-scope release fence would
+// instead write back the whole L2 of the XCD once per block. The single
+// publishing thread does this right after the row scalars are known, so
+// the wait covers only its loads and these three stores (not the row's
+// gradient stores) and the other waves go on with the gradient meanwhile.
 // ---------------------------------------------------------------------------
+
+// One thread per block. has_row: the block owns the row's values (a split-V
+// row is owned by its chunk 0). Returns true in the block that arrives last.
+__device__ __forceinline__ bool epilogue_publish(const Params& p, int64_t row, bool has_row,
+                                                 float ce, float zl, int ok, int counted,
+                                                 uint32_t total_blocks) {
+  if (has_row) {
+    __hip_atomic_store(p.row_ce + row, ce, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(p.row_z + row, zl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(p.row_ok + row, (ok ? 1 : 0) | (counted ? 2 : 0), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  const uint32_t prev =
+      __hip_atomic_fetch_add(&p.hdr->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return prev == total_blocks - 1u;
+}
+
+// Whole block, in the block that arrived last only.
 template <int BLOCK>
-__device__ void epilogue_arrive(const Params& p, uint32_t total_blocks) {
-  __shared__ int s_last;
+__device__ void epilogue_reduce(const Params& p) {
   __shared__ double s_red[2][BLOCK / 64];
   __shared__ int64_t s_cnt[2][BLOCK / 64];
   const int tid = threadIdx.x;
-  if (tid == 0) {
-    // Publish this block's per-row values, then count the arrival.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    const uint32_t prev =
-        __hip_atomic_fetch_add(&p.hdr->done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (prev == total_blocks - 1u);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   double ce = 0.0, zl = 0.0;
   int64_t ok = 0, cnt = 0;
   for (int64_t r = tid; r < p.rows; r += BLOCK) {
@@ -362,14 +380,10 @@ __device__ void epilogue_arrive(const Params& p, uint32_t total_blocks) {
   }
 }
 
-// Per-row outputs of one row (thread 0 of the row's block).
+// Per-row outputs of one row (thread 0 of the row's block); the reduced
+// outputs go through epilogue_publish.
 __device__ __forceinline__ void write_row_outputs(const Params& p, int64_t row, float ce, float zl,
-                                                  int ok, int counted, int64_t arg) {
-  if (p.epilogue) {
-    p.row_ce[row] = ce;
-    p.row_z[row] = zl;
-    p.row_ok[row] = (ok ? 1 : 0) | (counted ? 2 : 0);
-  }
+                                                  int ok, int64_t arg) {
   if (p.reduction == 0) {
     if (p.loss) p.loss[row] = ce + zl;
     if (p.z_loss) p.z_loss[row] = zl;

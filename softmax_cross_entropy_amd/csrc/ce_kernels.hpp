@@ -29,6 +29,17 @@ namespace cedev {
 
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
+// Raw buffer descriptor over nvec 16-byte vectors at base (stride 0: byte
+// offsets; the fourth word selects 32-bit data on gfx9-family GPUs). Loads
+// past the end return 0 and stores past the end are dropped by the hardware.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kStoreNT = 2;  // non-temporal store (streaming gradient)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int nvec) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           nvec * 16, kRsrcWord3);
+}
+
 // Softcapped value z = c tanh(x / c) (Liger-Kernel CE profile, Forward Pass:
 // softcap; the tanh form is the reading taken for "softcapping").
 template <int SC>
@@ -63,7 +74,8 @@ __device__ __forceinline__ void pass1_vec(const Params& p, Acc& a, const float (
   float vm = f[0];
 #pragma unroll
   for (int i = 1; i < EPV; ++i) vm = __builtin_fmaxf(vm, f[i]);
-  const bool take = vm > a.bv;
+  // Slots are visited LDS-first, so the tie-break compares indices.
+  const bool take = (vm > a.bv) || (vm == a.bv && slot < a.bi);
   a.bv = take ? vm : a.bv;
   a.bi = take ? slot : a.bi;
 
@@ -114,7 +126,7 @@ __device__ __forceinline__ void pass1_vec(const Params& p, Acc& a, const float (
 // Pass 1 over one scalar element (row tails and the unaligned path).
 template <int SC, int SM>
 __device__ __forceinline__ void pass1_one(const Params& p, Acc& a, float x, int slot, int64_t k) {
-  const bool take = x > a.bv;
+  const bool take = (x > a.bv) || (x == a.bv && slot < a.bi);
   a.bv = take ? x : a.bv;
   a.bi = take ? slot : a.bi;
   const float z = zval<SC>(p, x);
@@ -154,7 +166,7 @@ __device__ __forceinline__ float grad_one(const Params& p, const RowScalars& rs,
 
 template <class E, int SC, int SM>
 __device__ __forceinline__ u4 grad_vec(const Params& p, const RowScalars& rs, const u4 v,
-                                       int64_t jg, int64_t y) {
+                                       int64_t jg, int yi) {
   constexpr int EPV = E::EPV;
   float f[EPV], wk[EPV];
   E::unpack(v, f);
@@ -169,7 +181,6 @@ __device__ __forceinline__ u4 grad_vec(const Params& p, const RowScalars& rs, co
 #pragma unroll
     for (int i = 0; i < EPV; ++i) wk[i] = 1.0f;
   }
-  const int64_t d = y - jg * EPV;  // position of the target inside this vector, if any
   float t[EPV];
   if constexpr (SC) {
     float u[EPV];
@@ -182,7 +193,14 @@ __device__ __forceinline__ u4 grad_vec(const Params& p, const RowScalars& rs, co
   }
   float g[EPV];
 #pragma unroll
-  for (int i = 0; i < EPV; ++i) g[i] = grad_elem<SC, SM>(p, rs, f[i], t[i], wk[i], d == i);
+  for (int i = 0; i < EPV; ++i) g[i] = grad_elem<SC, SM>(p, rs, f[i], t[i], wk[i], false);
+  if (yi >= 0) {
+    // The one element of the row at the target class: recompute it with the
+    // one-hot term (same arithmetic as grad_one on that element).
+#pragma unroll
+    for (int i = 0; i < EPV; ++i)
+      if (i == yi) g[i] = grad_elem<SC, SM>(p, rs, f[i], t[i], wk[i], true);
+  }
   return E::pack(g);
 }
 
@@ -270,39 +288,45 @@ __global__ __launch_bounds__(BLOCK) void chunk_kernel(Params p) {
         for (int j = tid; j < nv; j += BLOCK) vp[j] = u4{0u, 0u, 0u, 0u};
         if (has_tail && tid < tail) E::st(rp, static_cast<int64_t>(nvec_row) * EPV + tid, 0.0f);
       }
+      __shared__ int s_last0;
       if (tid == 0) {
         const float q = bad ? __builtin_nanf("") : 0.0f;
-        write_row_outputs(p, row, q, q, 0, 0, -1);
+        write_row_outputs(p, row, q, q, 0, -1);
+        if (p.epilogue) s_last0 = epilogue_publish(p, row, true, q, q, 0, 0, gridDim.x);
       }
-      if (p.epilogue) epilogue_arrive<BLOCK>(p, gridDim.x);
+      if (p.epilogue) {
+        __syncthreads();
+        if (s_last0) epilogue_reduce<BLOCK>(p);
+      }
     }
     return;
   }
 
   // ---- issue every load of the chunk up front ----
-  u4 r[NREG > 0 ? NREG : 1];
-#pragma unroll
-  for (int k = 0; k < NREG; ++k) {
-    const int j = k * BLOCK + tid;
-    r[k] = (j < nv) ? vp[j] : u4{0u, 0u, 0u, 0u};
-  }
-#pragma unroll
-  for (int k = 0; k < NLDS; ++k) {
-    const int j = (NREG + k) * BLOCK + tid;
-    if (j < nv) {
-      __builtin_amdgcn_global_load_lds(
-          static_cast<const void*>(vp + j),
-          (lds_void_ptr)(lds_rows + k * BLOCK + wave * 64), 16, 0, 0);
-    }
-  }
+  // Raw buffer loads over a descriptor that spans exactly this chunk: one
+  // VGPR offset for every slot (the slot offset is scalar) and hardware
+  // bounds checking (lanes past the chunk read 0 and their stores are
+  // dropped), so the loads are unconditional and the compiler can wait, for
+  // each register slot, only for that slot's data. Order: the two scalar
+  // loads, the register slots, then the LDS slots (consumed last).
   const int64_t tail0 = static_cast<int64_t>(nvec_row) * EPV;
-  float xt = 0.0f;
-  if (has_tail && tid < tail) xt = E::ld(rp, tail0 + tid);
   const bool y_here = FUSED || (y >= static_cast<int64_t>(v0) * EPV &&
                                 y < static_cast<int64_t>(v1) * EPV) ||
                       (has_tail && y >= tail0);
   float xy = 0.0f;
   if (tid == 0 && y_here) xy = E::ld(rp, y);
+  float xt = 0.0f;
+  if (has_tail && tid < tail) xt = E::ld(rp, tail0 + tid);
+  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(vp, nv);
+  const int voff = tid * 16;
+  u4 r[NREG > 0 ? NREG : 1];
+#pragma unroll
+  for (int k = 0; k < NREG; ++k)
+    r[k] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, k * BLOCK * 16, 0);
+#pragma unroll
+  for (int k = 0; k < NLDS; ++k)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_ptr)(lds_rows + k * BLOCK + wave * 64),
+                                             16, voff, (NREG + k) * BLOCK * 16, 0, 0);
 
   // ---- pass 1: online max / sum, argmax, smoothing sum ----
   Acc a;
@@ -310,7 +334,7 @@ __global__ __launch_bounds__(BLOCK) void chunk_kernel(Params p) {
 #pragma unroll
   for (int k = 0; k < NS; ++k) {
     const int j = k * BLOCK + tid;
-    if (j < nv) {
+    if (k * BLOCK < nv && j < nv) {
       const u4 v = (k < NREG) ? r[k < NREG ? k : 0] : lds_rows[(k - NREG) * BLOCK + tid];
       float f[EPV];
       E::unpack(v, f);
@@ -374,20 +398,36 @@ __global__ __launch_bounds__(BLOCK) void chunk_kernel(Params p) {
       rs.arg = arg;
       rs.ok = (arg == y);
       s_rs = rs;
-      write_row_outputs(p, row, rs.ce, rs.zl, rs.ok, 1, arg);
+      write_row_outputs(p, row, rs.ce, rs.zl, rs.ok, arg);
     }
     __syncthreads();
+    __shared__ int s_last;
+    if (tid == 0 && p.epilogue) {
+      const RowScalars& rs = s_rs;
+      s_last = epilogue_publish(p, row, true, rs.ce, rs.zl, rs.ok, 1, gridDim.x);
+    }
 
     // ---- pass 2: gradient from on-chip data, written over the logits ----
     if (p.grad) {
       const RowScalars rs = s_rs;
+      // Which of this thread's slots holds the target's vector, and where.
+      int ky = -1, yi = -1;
+      if (y < tail0) {
+        const int jy = static_cast<int>(y / EPV) - v0;
+        if (jy >= 0 && jy < nv && jy % BLOCK == tid) {
+          ky = jy / BLOCK;
+          yi = static_cast<int>(y % EPV);
+        }
+      }
 #pragma unroll
       for (int k = 0; k < NS; ++k) {
         const int j = k * BLOCK + tid;
-        if (j < nv) {
+        if (k * BLOCK < nv) {  // uniform: skip slots past the chunk
           const u4 v = (k < NREG) ? r[k < NREG ? k : 0] : lds_rows[(k - NREG) * BLOCK + tid];
-          const u4 g = grad_vec<E, SC, SM>(p, rs, v, j, y);
-          __builtin_nontemporal_store(g, vp + j);
+          const u4 g = grad_vec<E, SC, SM>(p, rs, v, static_cast<int64_t>(v0) + j,
+                                           k == ky ? yi : -1);
+          // lanes past the chunk are outside the descriptor: the store is dropped
+          __builtin_amdgcn_raw_buffer_store_b128(g, rsrc, voff, k * BLOCK * 16, kStoreNT);
         }
       }
       if (has_tail && tid < tail) {
@@ -396,7 +436,10 @@ __global__ __launch_bounds__(BLOCK) void chunk_kernel(Params p) {
         E::st(rp, k, grad_one<SC, SM>(p, rs, xt, wk, k == y));
       }
     }
-    if (p.epilogue) epilogue_arrive<BLOCK>(p, gridDim.x);
+    if (p.epilogue) {
+      __syncthreads();
+      if (s_last) epilogue_reduce<BLOCK>(p);
+    }
   }
 }
 
@@ -431,11 +474,16 @@ __global__ __launch_bounds__(BLOCK) void splitv_finish_kernel(Params p) {
       for (int j = tid; j < nv; j += BLOCK) vp[j] = u4{0u, 0u, 0u, 0u};
       if (has_tail && tid < tail) E::st(rp, tail0 + tid, 0.0f);
     }
-    if (c == 0 && tid == 0) {
+    __shared__ int s_last0;
+    if (tid == 0) {
       const float q = bad ? __builtin_nanf("") : 0.0f;
-      write_row_outputs(p, row, q, q, 0, 0, -1);
+      if (c == 0) write_row_outputs(p, row, q, q, 0, -1);
+      if (p.epilogue) s_last0 = epilogue_publish(p, row, c == 0, q, q, 0, 0, gridDim.x);
     }
-    if (p.epilogue) epilogue_arrive<BLOCK>(p, gridDim.x);
+    if (p.epilogue) {
+      __syncthreads();
+      if (s_last0) epilogue_reduce<BLOCK>(p);
+    }
     return;
   }
 
@@ -458,9 +506,14 @@ __global__ __launch_bounds__(BLOCK) void splitv_finish_kernel(Params p) {
     rs.arg = bi;
     rs.ok = (bi == y);
     s_rs = rs;
-    if (c == 0) write_row_outputs(p, row, rs.ce, rs.zl, rs.ok, 1, bi);
+    if (c == 0) write_row_outputs(p, row, rs.ce, rs.zl, rs.ok, bi);
   }
   __syncthreads();
+  __shared__ int s_last;
+  if (tid == 0 && p.epilogue) {
+    const RowScalars& rs = s_rs;
+    s_last = epilogue_publish(p, row, c == 0, rs.ce, rs.zl, rs.ok, 1, gridDim.x);
+  }
   if (p.grad) {
     const RowScalars rs = s_rs;
     for (int j0 = 0; j0 < nv; j0 += BLOCK * U) {
@@ -474,7 +527,10 @@ __global__ __launch_bounds__(BLOCK) void splitv_finish_kernel(Params p) {
       for (int u = 0; u < U; ++u) {
         const int j = j0 + u * BLOCK + tid;
         if (j < nv) {
-          const u4 g = grad_vec<E, SC, SM>(p, rs, v[u], static_cast<int64_t>(v0) + j, y);
+          const int64_t jg = static_cast<int64_t>(v0) + j;
+          const int64_t d = y - jg * EPV;
+          const u4 g = grad_vec<E, SC, SM>(p, rs, v[u], jg,
+                                           (d >= 0 && d < EPV) ? static_cast<int>(d) : -1);
           __builtin_nontemporal_store(g, vp + j);
         }
       }
@@ -486,7 +542,10 @@ __global__ __launch_bounds__(BLOCK) void splitv_finish_kernel(Params p) {
       E::st(rp, k, grad_one<SC, SM>(p, rs, xk, wk, k == y));
     }
   }
-  if (p.epilogue) epilogue_arrive<BLOCK>(p, gridDim.x);
+  if (p.epilogue) {
+    __syncthreads();
+    if (s_last) epilogue_reduce<BLOCK>(p);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -509,11 +568,16 @@ __global__ __launch_bounds__(BLOCK) void row_scalar_kernel(Params p) {
   if (ignored || bad) {
     if (p.grad)
       for (int64_t k = tid; k < p.V; k += BLOCK) E::st(rp, k, 0.0f);
+    __shared__ int s_last0;
     if (tid == 0) {
       const float q = bad ? __builtin_nanf("") : 0.0f;
-      write_row_outputs(p, row, q, q, 0, 0, -1);
+      write_row_outputs(p, row, q, q, 0, -1);
+      if (p.epilogue) s_last0 = epilogue_publish(p, row, true, q, q, 0, 0, gridDim.x);
     }
-    if (p.epilogue) epilogue_arrive<BLOCK>(p, gridDim.x);
+    if (p.epilogue) {
+      __syncthreads();
+      if (s_last0) epilogue_reduce<BLOCK>(p);
+    }
     return;
   }
   Acc a;
@@ -533,9 +597,14 @@ __global__ __launch_bounds__(BLOCK) void row_scalar_kernel(Params p) {
     rs.arg = t.bi;
     rs.ok = (t.bi == y);
     s_rs = rs;
-    write_row_outputs(p, row, rs.ce, rs.zl, rs.ok, 1, t.bi);
+    write_row_outputs(p, row, rs.ce, rs.zl, rs.ok, t.bi);
   }
   __syncthreads();
+  __shared__ int s_last;
+  if (tid == 0 && p.epilogue) {
+    const RowScalars& rs = s_rs;
+    s_last = epilogue_publish(p, row, true, rs.ce, rs.zl, rs.ok, 1, gridDim.x);
+  }
   if (p.grad) {
     const RowScalars rs = s_rs;
     for (int64_t k = tid; k < p.V; k += BLOCK) {
@@ -543,7 +612,10 @@ __global__ __launch_bounds__(BLOCK) void row_scalar_kernel(Params p) {
       E::st(rp, k, grad_one<SC, SM>(p, rs, E::ld(rp, k), wk, k == y));
     }
   }
-  if (p.epilogue) epilogue_arrive<BLOCK>(p, gridDim.x);
+  if (p.epilogue) {
+    __syncthreads();
+    if (s_last) epilogue_reduce<BLOCK>(p);
+  }
 }
 
 // ---------------------------------------------------------------------------
