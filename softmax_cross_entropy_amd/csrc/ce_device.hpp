@@ -115,6 +115,14 @@ struct F32 {
   __device__ static __forceinline__ void st(void* row, int64_t i, float v) {
     static_cast<float*>(row)[i] = v;
   }
+  __device__ static __forceinline__ void st_nt(void* row, int64_t i, float v) {
+    __builtin_nontemporal_store(v, static_cast<float*>(row) + i);
+  }
+  // Store element i through a buffer descriptor with cache policy AUX.
+  template <int AUX>
+  __device__ static __forceinline__ void st_buf(__amdgpu_buffer_rsrc_t r, int i, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, i * 4, 0, AUX);
+  }
 };
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -145,21 +153,36 @@ struct BF16 {
   __device__ static __forceinline__ void st(void* row, int64_t i, float v) {
     static_cast<uint16_t*>(row)[i] = static_cast<uint16_t>(pack_bf16x2(v, 0.0f) & 0xffffu);
   }
+  __device__ static __forceinline__ void st_nt(void* row, int64_t i, float v) {
+    __builtin_nontemporal_store(static_cast<uint16_t>(pack_bf16x2(v, 0.0f) & 0xffffu),
+                                static_cast<uint16_t*>(row) + i);
+  }
+  template <int AUX>
+  __device__ static __forceinline__ void st_buf(__amdgpu_buffer_rsrc_t r, int i, float v) {
+    __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(pack_bf16x2(v, 0.0f) & 0xffffu),
+                                          r, i * 2, 0, AUX);
+  }
 };
 
 // ---------------------------------------------------------------------------
 // Launch-wide parameters (kernel argument, passed by value).
 // ---------------------------------------------------------------------------
-struct Header {          // first 64 bytes of the workspace, written by the prologue
+// First 256 bytes of the workspace. The fields the prologue writes (read by
+// every row block) and the arrival counter (an atomic per row block) sit on
+// different 128-byte lines, so the counter's traffic does not evict or
+// serialize the reads of the scales.
+struct Header {
   double D;              // sum of w[target] over counted rows
   double W;              // sum of all class weights (V when unweighted)
   int64_t n;             // counted rows
   float alpha;           // gradient scale of the cross-entropy part
   float beta;            // gradient scale of the z-loss part
   uint32_t err;          // bit 0: a target outside [0, V) that is not ignore_index
-  uint32_t done;         // arrival counter of the last-block epilogue
-  uint32_t pad[4];
+  uint32_t pad0[23];
+  uint32_t done;         // arrival counter of the last-block epilogue (byte 128)
+  uint32_t pad1[31];
 };
+static_assert(sizeof(Header) == 256, "the header fills the workspace's first 256 bytes");
 
 struct Partial {         // one (row, chunk) of the split-V first stage: 32 bytes
   float m;               // running max of softcapped logits over the chunk

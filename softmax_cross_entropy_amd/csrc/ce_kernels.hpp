@@ -7,15 +7,17 @@
 // only rescales that gradient by grad_output.
 //
 // MI355X design (not the page's Triton loop):
-//  * chunk_kernel<FUSED=true>: one workgroup per row. The whole row is read
-//    from HBM once with dwordx4 loads and kept on chip (VGPRs, plus LDS
-//    filled by global_load_lds for the largest rows), so the gradient pass
-//    reads registers instead of re-reading HBM: 1 read + 1 write per logit.
-//  * chunk_kernel<FUSED=false> + splitv_finish_kernel: the row is split into
-//    S chunks held by different workgroups; stage 1 writes per-chunk
-//    partials (max, sum, argmax, target logit), stage 2 combines them in a
-//    fixed order and writes its chunk's gradient. For rows that exceed one
-//    CU's on-chip storage or for batches with too few rows to fill 256 CUs.
+//  * row_kernel: one workgroup per row. The whole row is read from HBM once
+//    with non-temporal dwordx4 buffer loads and kept on chip (VGPRs, plus
+//    LDS filled by buffer_load ... lds for the largest rows), so the
+//    gradient pass reads registers instead of re-reading HBM: 1 read + 1
+//    write per logit. fp32 rows keep exp(x - group max) in place of x, so
+//    the gradient pass is one multiply per element.
+//  * splitv_partial_kernel + splitv_finish_kernel: the row is split into S
+//    chunks held by different workgroups; stage 1 writes per-chunk partials
+//    (max, sum, argmax, target logit), stage 2 combines them in a fixed
+//    order and writes its chunk's gradient. For rows that exceed one CU's
+//    on-chip storage or for batches with too few rows to fill 256 CUs.
 //  * row_scalar_kernel: rows that are not 16-byte aligned (any V, any
 //    stride); element loads, same math.
 //  * prologue_kernel: n, D = sum w[target], W = sum w, the mean scales and
@@ -34,6 +36,7 @@ typedef __attribute__((address_space(3))) void* lds_void_ptr;
 // past the end return 0 and stores past the end are dropped by the hardware.
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kStoreNT = 2;  // non-temporal store (streaming gradient)
+constexpr int kLoadNT = 2;   // non-temporal load (each logit is read once)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int nvec) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
@@ -232,86 +235,408 @@ __device__ __forceinline__ void load_scales(const Params& p, double& W, double& 
   }
 }
 
+// Register / LDS slot k of thread tid (k is a compile-time constant once the
+// slot loops are unrolled).
+template <int NREG, int BLOCK>
+__device__ __forceinline__ u4 slot_get(const u4 (&r)[NREG > 0 ? NREG : 1], const u4* lds, int k,
+                                       int tid) {
+  return (k < NREG) ? r[k < NREG ? k : 0] : lds[(k - NREG) * BLOCK + tid];
+}
+
+template <int NREG, int BLOCK>
+__device__ __forceinline__ void slot_put(u4 (&r)[NREG > 0 ? NREG : 1], u4* lds, int k, int tid,
+                                         u4 v) {
+  if (k < NREG) {
+    r[k < NREG ? k : 0] = v;
+  } else {
+    lds[(k - NREG) * BLOCK + tid] = v;
+  }
+}
+
+template <int EPV>
+__device__ __forceinline__ float vec_max(const float (&f)[EPV]) {
+  float m = f[0];
+#pragma unroll
+  for (int i = 1; i < EPV; ++i) m = __builtin_fmaxf(m, f[i]);
+  return m;
+}
+
+// Gradient of one fp32 vector from its stored exponentials e = 2^((x - m_g) log2 e):
+// p_k = e sc / A with sc = A 2^((m_g - m) log2 e - log2 s), so
+// g = e sc - B w_k - C [k = y].
+template <int SM>
+__device__ __forceinline__ u4 grad_vec_e(const Params& p, const RowScalars& rs, const u4 v,
+                                         float sc, int64_t jg, int yi) {
+  float e[4], g[4];
+  F32::unpack(v, e);
+  if constexpr (SM) {
+    if (p.weight) {
+      float wk[4];
+      load_w<F32>(p.weight, jg, wk);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) g[i] = __builtin_fmaf(e[i], sc, -(rs.B * wk[i]));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) g[i] = __builtin_fmaf(e[i], sc, -rs.B);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) g[i] = e[i] * sc;
+  }
+  if (yi >= 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (i == yi) g[i] -= rs.C;
+  }
+  return F32::pack(g);
+}
+
+// Outputs of a row that is ignored (gradient exactly +0.0, never read) or
+// whose target is out of range (NaN loss); shared by the one-row-per-block
+// kernels.
+template <class E, int BLOCK>
+__device__ __forceinline__ void skipped_row(const Params& p, int64_t row, bool bad, char* rp,
+                                            int nv, int tail) {
+  const int tid = threadIdx.x;
+  if (p.grad) {
+    u4* vp = reinterpret_cast<u4*>(rp);
+    for (int j = tid; j < nv; j += BLOCK) __builtin_nontemporal_store(u4{0u, 0u, 0u, 0u}, vp + j);
+    if (tid < tail) E::st(rp, static_cast<int64_t>(nv) * E::EPV + tid, 0.0f);
+  }
+  __shared__ int s_last0;
+  if (tid == 0) {
+    const float q = bad ? __builtin_nanf("") : 0.0f;
+    write_row_outputs(p, row, q, q, 0, -1);
+    if (p.epilogue) s_last0 = epilogue_publish(p, row, true, q, q, 0, 0, gridDim.x);
+  }
+  if (p.epilogue) {
+    __syncthreads();
+    if (s_last0) epilogue_reduce<BLOCK>(p);
+  }
+}
+
 // ---------------------------------------------------------------------------
-// chunk_kernel: FUSED = whole row per workgroup, single HBM read;
-//               !FUSED = split-V stage 1 (partials only).
-// Slots: thread tid owns vectors j = k * BLOCK + tid of its chunk for
-// k < NREG (registers) and NREG <= k < NREG + NLDS (LDS); the row tail
-// (V % EPV elements) is held by threads tid < tail.
+// row_kernel: one workgroup per row; the row is read from HBM once and kept
+// on chip. Slots: thread tid owns vectors j = k * BLOCK + tid, for k < NREG
+// in VGPRs and for NREG <= k < NREG + NLDS in LDS; the row tail (V % EPV
+// elements) is held by threads tid < tail.
+//
+// Pass 1 takes the slots in groups of GS: first the group's raw maximum,
+// then the exponentials relative to the group's softcapped maximum and their
+// sum, folded into the thread's (max, sum) once per group. Each thread also
+// keeps the first group that holds its raw maximum; once the row maximum is
+// known, only threads holding it look for its first position (no
+// per-element argmax work). Rows of fp32 logits without softcap keep the
+// exponentials on chip in place of the logits, so the gradient pass is one
+// multiply (or fma) per element by a per-group scale; other rows keep the
+// logits and the gradient pass recomputes the exponential.
 // ---------------------------------------------------------------------------
-template <class E, int BLOCK, int NREG, int NLDS, int SC, int SM, bool FUSED>
-__global__ __launch_bounds__(BLOCK) void chunk_kernel(Params p) {
+template <class E, int BLOCK, int NREG, int NLDS, int SC, int SM>
+__global__ __launch_bounds__(BLOCK) void row_kernel(Params p) {
   constexpr int EPV = E::EPV;
   constexpr int NS = NREG + NLDS;
   constexpr int NW = BLOCK / 64;
+  constexpr bool KEEP_E = (EPV == 4) && !SC;
+  constexpr int GS = (EPV == 4) ? 8 : 2;
+  constexpr int NG = (NS + GS - 1) / GS;
+  constexpr int kRegPolicy = (NLDS == 0 || EPV == 8) ? kLoadNT : 0;
   __shared__ u4 lds_rows[NLDS > 0 ? NLDS * BLOCK : 1];
   __shared__ Acc s_acc[NW];
+  __shared__ int s_cand[NW];
   __shared__ RowScalars s_rs;
+  __shared__ float s_xy;
+  __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int64_t row;
-  int c;
-  if constexpr (FUSED) {
-    row = blockIdx.x;
-    c = 0;
-  } else {
-    row = blockIdx.x / p.S;
-    c = blockIdx.x - static_cast<int>(row) * p.S;
-  }
+  const int64_t row = blockIdx.x;
   const int64_t y = p.target[row];
   const bool ignored = (y == p.ignore_index);
   const bool bad = !ignored && (y < 0 || y >= p.V);
   char* rp = row_ptr(p, row, E::BYTES);
-  const int nvec_row = static_cast<int>(p.V / EPV);
-  const int tail = static_cast<int>(p.V - static_cast<int64_t>(nvec_row) * EPV);
-  int v0, v1;
-  bool has_tail;
-  if constexpr (FUSED) {
-    v0 = 0;
-    v1 = nvec_row;
-    has_tail = tail > 0;
-  } else {
-    v0 = c * p.chunk_vec;
-    v1 = min(v0 + p.chunk_vec, nvec_row);
-    has_tail = (c == p.S - 1) && tail > 0;
-  }
-  const int nv = v1 - v0;
-  u4* vp = reinterpret_cast<u4*>(rp) + v0;
+  const int nv = static_cast<int>(p.V / EPV);
+  const int tail = static_cast<int>(p.V - static_cast<int64_t>(nv) * EPV);
+  const int64_t tail0 = static_cast<int64_t>(nv) * EPV;
 
   if (ignored || bad) {
-    if constexpr (FUSED) {
-      // Ignored rows are never read; their gradient is exactly +0.0
-      // (tt-mlir PR #9324 page: ignored rows, also with non-finite logits).
-      if (p.grad) {
-        for (int j = tid; j < nv; j += BLOCK) vp[j] = u4{0u, 0u, 0u, 0u};
-        if (has_tail && tid < tail) E::st(rp, static_cast<int64_t>(nvec_row) * EPV + tid, 0.0f);
-      }
-      __shared__ int s_last0;
-      if (tid == 0) {
-        const float q = bad ? __builtin_nanf("") : 0.0f;
-        write_row_outputs(p, row, q, q, 0, -1);
-        if (p.epilogue) s_last0 = epilogue_publish(p, row, true, q, q, 0, 0, gridDim.x);
-      }
-      if (p.epilogue) {
-        __syncthreads();
-        if (s_last0) epilogue_reduce<BLOCK>(p);
-      }
-    }
+    // Ignored rows are never read; their gradient is exactly +0.0
+    // (tt-mlir PR #9324 page: ignored rows, also with non-finite logits).
+    skipped_row<E, BLOCK>(p, row, bad, rp, nv, tail);
     return;
   }
 
-  // ---- issue every load of the chunk up front ----
-  // Raw buffer loads over a descriptor that spans exactly this chunk: one
-  // VGPR offset for every slot (the slot offset is scalar) and hardware
-  // bounds checking (lanes past the chunk read 0 and their stores are
-  // dropped), so the loads are unconditional and the compiler can wait, for
+  // ---- issue every load of the row up front ----
+  // Raw buffer loads over a descriptor that spans exactly the row's vectors:
+  // one VGPR offset for every slot (the slot offset is scalar) and hardware
+  // bounds checking (lanes past the row read 0 and their stores are
+  // dropped), so the loads are unconditional and the compiler waits, for
   // each register slot, only for that slot's data. Order: the two scalar
   // loads, the register slots, then the LDS slots (consumed last).
+  // Cache policy, as measured on MI355X: non-temporal register-slot loads
+  // (each logit is read once, and the class weights of weighted rows stay
+  // in L2), except for fp32 rows that also use LDS slots, which ran faster
+  // with the default policy; LDS slots always use the default policy.
+  float xy = 0.0f;
+  if (tid == 0) xy = E::ld(rp, y);
+  float xt = 0.0f;
+  if (tid < tail) xt = E::ld(rp, tail0 + tid);
+  const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(rp, nv);
+  const int voff = tid * 16;
+  u4 r[NREG > 0 ? NREG : 1];
+#pragma unroll
+  for (int k = 0; k < NREG; ++k)
+    r[k] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, k * BLOCK * 16, kRegPolicy);
+#pragma unroll
+  for (int k = 0; k < NLDS; ++k)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_ptr)(lds_rows + k * BLOCK + wave * 64),
+                                             16, voff, (NREG + k) * BLOCK * 16, 0, 0);
+
+  // ---- pass 1 ----
+  // Thread state: (tm, ts) = max of z and sum of exp(z - tm), tsz = smoothing
+  // sum, tb = raw maximum and tg = first group holding it (NG: the tail).
+  float tm = kLowest, ts = 0.0f, tsz = 0.0f, tb = -__builtin_inff();
+  int tg = -1;
+  float gm[KEEP_E ? NG : 1];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    if (g * GS * BLOCK < nv) {  // uniform: skip groups past the row
+      float gx = -__builtin_inff();
+#pragma unroll
+      for (int q = 0; q < GS; ++q) {
+        const int k = g * GS + q;
+        if (k < NS && k * BLOCK < nv) {
+          float f[EPV];
+          E::unpack(slot_get<NREG, BLOCK>(r, lds_rows, k, tid), f);
+          if ((k + 1) * BLOCK > nv) {  // the row's last, partial slot (a scalar branch)
+            asm volatile("");
+            const bool ok = k * BLOCK + tid < nv;
+#pragma unroll
+            for (int i = 0; i < EPV; ++i) f[i] = ok ? f[i] : -__builtin_inff();
+          }
+#pragma unroll
+          for (int i = 0; i < EPV; ++i) gx = __builtin_fmaxf(gx, f[i]);
+        }
+      }
+      const bool take = gx > tb;  // strict: the first group holding the max stays
+      tg = take ? g : tg;
+      tb = take ? gx : tb;
+      const float zg = zval<SC>(p, __builtin_fmaxf(gx, kLowest));
+      float gsum = 0.0f;
+#pragma unroll
+      for (int q = 0; q < GS; ++q) {
+        const int k = g * GS + q;
+        if (k < NS && k * BLOCK < nv) {
+          float f[EPV];
+          E::unpack(slot_get<NREG, BLOCK>(r, lds_rows, k, tid), f);
+          float z[EPV];
+          if constexpr (SC) {
+            float u[EPV], t[EPV];
+#pragma unroll
+            for (int i = 0; i < EPV; ++i) u[i] = f[i] * p.inv_softcap;
+            tanh_vec<EPV>(u, t);
+#pragma unroll
+            for (int i = 0; i < EPV; ++i) z[i] = p.softcap * t[i];
+          } else {
+#pragma unroll
+            for (int i = 0; i < EPV; ++i) z[i] = f[i];
+          }
+          float e[EPV];
+#pragma unroll
+          for (int i = 0; i < EPV; ++i) e[i] = ex2((z[i] - zg) * kLog2e);
+          if constexpr (KEEP_E) slot_put<NREG, BLOCK>(r, lds_rows, k, tid, F32::pack(e));
+          float es = e[0];
+#pragma unroll
+          for (int i = 1; i < EPV; ++i) es += e[i];
+          float zs = 0.0f;
+          if constexpr (SM) {
+            if (p.weight) {
+              float wk[EPV];
+              load_w<E>(p.weight, k * BLOCK + tid, wk);
+#pragma unroll
+              for (int i = 0; i < EPV; ++i) zs = __builtin_fmaf(wk[i], z[i], zs);
+            } else {
+#pragma unroll
+              for (int i = 0; i < EPV; ++i) zs += z[i];
+            }
+          }
+          if ((k + 1) * BLOCK > nv) {  // lanes past the row add nothing
+            asm volatile("");
+            const bool ok = k * BLOCK + tid < nv;
+            es = ok ? es : 0.0f;
+            zs = ok ? zs : 0.0f;
+          }
+          gsum += es;
+          if constexpr (SM) tsz += zs;
+        }
+      }
+      ms_combine(tm, ts, zg, gsum);
+      if constexpr (KEEP_E) gm[g] = zg;
+    }
+  }
+  if (tid < tail) {
+    // the row tail: one element per thread, after every vector in index order
+    const bool take = xt > tb;
+    tg = take ? NG : tg;
+    tb = take ? xt : tb;
+    const float z = zval<SC>(p, xt);
+    ms_combine(tm, ts, z, 1.0f);
+    if constexpr (SM) tsz = p.weight ? __builtin_fmaf(p.weight[tail0 + tid], z, tsz) : tsz + z;
+  }
+
+  Acc a;
+  a.m = tm;
+  a.s = ts;
+  a.sz = tsz;
+  a.bv = tb;
+  a.bi = 0;
+  wave_reduce(a);
+  if (lane == 0) s_acc[wave] = a;
+  __syncthreads();
+  const Acc t = block_combine<NW>(s_acc);
+
+  // ---- argmax: threads holding the row maximum find its first position in
+  // their first group holding it; the block takes the lowest index. With
+  // exponentials kept on chip the maximum sits at e == 1 exactly, and for
+  // 2 <= |max| < inf no other value can round to 1 (neighbouring floats
+  // there differ by at least 2^-22); otherwise the group's raw logits are
+  // read back (before any gradient store).
+  int cand = kNoIndex;
+  if (tg >= 0 && tb == t.bv) {
+    if (tg == NG) {
+      cand = static_cast<int>(tail0) + tid;
+    } else {
+      const bool by_e = !KEEP_E || (__builtin_fabsf(t.bv) >= 2.0f && t.bv < __builtin_inff());
+      const float want = KEEP_E && by_e ? 1.0f : t.bv;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        if (g == tg) {
+#pragma unroll
+          for (int q = GS - 1; q >= 0; --q) {
+            const int k = g * GS + q;
+            if (k < NS && k * BLOCK + tid < nv) {
+              u4 v;
+              if (KEEP_E && !by_e) {
+                v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, k * BLOCK * 16, 0);
+              } else {
+                v = slot_get<NREG, BLOCK>(r, lds_rows, k, tid);
+              }
+              float f[EPV];
+              E::unpack(v, f);
+#pragma unroll
+              for (int i = EPV - 1; i >= 0; --i)
+                cand = (f[i] == want) ? (k * BLOCK + tid) * EPV + i : cand;
+            }
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) cand = min(cand, __shfl_xor(cand, off, 64));
+  if (lane == 0) s_cand[wave] = cand;
+  __syncthreads();
+
+  if (tid == 0) {
+    int arg = s_cand[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) arg = min(arg, s_cand[w]);
+    if (arg == kNoIndex) arg = 0;  // no finite or infinite value: index 0
+    double W, alpha, beta;
+    load_scales(p, W, alpha, beta);
+    const float wy = p.weight ? p.weight[y] : 1.0f;
+    RowScalars rs;
+    row_scalars(rs, t.m, t.s, t.sz, zval<SC>(p, xy), wy, W, static_cast<double>(p.V), p.eps,
+                p.lam, alpha, beta);
+    rs.arg = arg;
+    rs.ok = (arg == y);
+    s_rs = rs;
+    s_xy = xy;
+    write_row_outputs(p, row, rs.ce, rs.zl, rs.ok, arg);
+  }
+  __syncthreads();
+  if (tid == 0 && p.epilogue) {
+    const RowScalars& rs = s_rs;
+    s_last = epilogue_publish(p, row, true, rs.ce, rs.zl, rs.ok, 1, gridDim.x);
+  }
+
+  // ---- pass 2: gradient from on-chip data, written over the logits ----
+  if (p.grad) {
+    const RowScalars rs = s_rs;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      if (g * GS * BLOCK < nv) {
+        float sc = 0.0f;
+        if constexpr (KEEP_E) sc = rs.A * ex2(__builtin_fmaf(gm[g] - rs.m, kLog2e, -rs.l2s));
+#pragma unroll
+        for (int q = 0; q < GS; ++q) {
+          const int k = g * GS + q;
+          if (k < NS && k * BLOCK < nv) {
+            const u4 v = slot_get<NREG, BLOCK>(r, lds_rows, k, tid);
+            u4 gv;
+            if constexpr (KEEP_E) {
+              gv = grad_vec_e<SM>(p, rs, v, sc, k * BLOCK + tid, -1);
+            } else {
+              gv = grad_vec<E, SC, SM>(p, rs, v, k * BLOCK + tid, -1);
+            }
+            // lanes past the row are outside the descriptor: the store is dropped
+            __builtin_amdgcn_raw_buffer_store_b128(gv, rsrc, voff, k * BLOCK * 16, kStoreNT);
+          }
+        }
+      }
+    }
+    if (tid < tail) {
+      const int64_t k = tail0 + tid;
+      const float wk = (SM && p.weight) ? p.weight[k] : 1.0f;
+      E::st(rp, k, grad_one<SC, SM>(p, rs, xt, wk, k == y));
+    }
+    // The one-hot term: the vectors above were written without it; the
+    // thread that wrote the target's vector rewrites that one element (its
+    // own later store to the same address, same path and policy, so it
+    // lands last). No per-element test for the target in the loop above.
+    if (y < tail0 && tid == static_cast<int>((y / EPV) % BLOCK)) {
+      const float wy = (SM && p.weight) ? p.weight[y] : 1.0f;
+      E::template st_buf<kStoreNT>(rsrc, static_cast<int>(y), grad_one<SC, SM>(p, rs, s_xy, wy, true));
+    }
+  }
+  if (p.epilogue) {
+    __syncthreads();
+    if (s_last) epilogue_reduce<BLOCK>(p);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split-V stage 1: workgroup (row, c) reads chunk c of the row once and
+// writes its partial (max, sum, smoothing sum, argmax, target logit). Slots
+// as in row_kernel, over the chunk's vectors.
+// ---------------------------------------------------------------------------
+template <class E, int BLOCK, int NREG, int SC, int SM>
+__global__ __launch_bounds__(BLOCK) void splitv_partial_kernel(Params p) {
+  constexpr int EPV = E::EPV;
+  constexpr int NW = BLOCK / 64;
+  __shared__ Acc s_acc[NW];
+  __shared__ int s_arg;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t row = blockIdx.x / p.S;
+  const int c = blockIdx.x - static_cast<int>(row) * p.S;
+  const int64_t y = p.target[row];
+  const bool ignored = (y == p.ignore_index);
+  const bool bad = !ignored && (y < 0 || y >= p.V);
+  if (ignored || bad) return;  // stage 2 writes the outputs of skipped rows
+  char* rp = row_ptr(p, row, E::BYTES);
+  const int nvec_row = static_cast<int>(p.V / EPV);
+  const int tail = static_cast<int>(p.V - static_cast<int64_t>(nvec_row) * EPV);
+  const int v0 = c * p.chunk_vec;
+  const int v1 = min(v0 + p.chunk_vec, nvec_row);
+  const bool has_tail = (c == p.S - 1) && tail > 0;
+  const int nv = v1 - v0;
+  u4* vp = reinterpret_cast<u4*>(rp) + v0;
   const int64_t tail0 = static_cast<int64_t>(nvec_row) * EPV;
-  const bool y_here = FUSED || (y >= static_cast<int64_t>(v0) * EPV &&
-                                y < static_cast<int64_t>(v1) * EPV) ||
+
+  const bool y_here = (y >= static_cast<int64_t>(v0) * EPV && y < static_cast<int64_t>(v1) * EPV) ||
                       (has_tail && y >= tail0);
   float xy = 0.0f;
   if (tid == 0 && y_here) xy = E::ld(rp, y);
@@ -319,25 +644,19 @@ __global__ __launch_bounds__(BLOCK) void chunk_kernel(Params p) {
   if (has_tail && tid < tail) xt = E::ld(rp, tail0 + tid);
   const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(vp, nv);
   const int voff = tid * 16;
-  u4 r[NREG > 0 ? NREG : 1];
+  u4 r[NREG];
 #pragma unroll
   for (int k = 0; k < NREG; ++k)
     r[k] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, k * BLOCK * 16, 0);
-#pragma unroll
-  for (int k = 0; k < NLDS; ++k)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_ptr)(lds_rows + k * BLOCK + wave * 64),
-                                             16, voff, (NREG + k) * BLOCK * 16, 0, 0);
 
-  // ---- pass 1: online max / sum, argmax, smoothing sum ----
   Acc a;
   acc_init(a);
 #pragma unroll
-  for (int k = 0; k < NS; ++k) {
+  for (int k = 0; k < NREG; ++k) {
     const int j = k * BLOCK + tid;
     if (k * BLOCK < nv && j < nv) {
-      const u4 v = (k < NREG) ? r[k < NREG ? k : 0] : lds_rows[(k - NREG) * BLOCK + tid];
       float f[EPV];
-      E::unpack(v, f);
+      E::unpack(r[k], f);
       pass1_vec<E, SC, SM>(p, a, f, v0 + j, static_cast<int64_t>(v0) + j);
     }
   }
@@ -348,8 +667,7 @@ __global__ __launch_bounds__(BLOCK) void chunk_kernel(Params p) {
   __syncthreads();
   const Acc t = block_combine<NW>(s_acc);
 
-  // ---- argmax: the owner of the winning slot finds the first position ----
-  __shared__ int s_arg;
+  // argmax: the owner of the winning slot finds the first position
   if (t.bi >= nvec_row) {
     if (tid == 0) s_arg = (t.bi == kNoIndex) ? 0 : static_cast<int>(tail0) + (t.bi - nvec_row);
   } else {
@@ -358,11 +676,10 @@ __global__ __launch_bounds__(BLOCK) void chunk_kernel(Params p) {
       const int kk = jl / BLOCK;
       int pos = 0;
 #pragma unroll
-      for (int k = 0; k < NS; ++k) {
+      for (int k = 0; k < NREG; ++k) {
         if (k == kk) {
-          const u4 v = (k < NREG) ? r[k < NREG ? k : 0] : lds_rows[(k - NREG) * BLOCK + tid];
           float f[EPV];
-          E::unpack(v, f);
+          E::unpack(r[k], f);
 #pragma unroll
           for (int i = EPV - 1; i >= 0; --i) pos = (f[i] == t.bv) ? i : pos;
         }
@@ -371,75 +688,17 @@ __global__ __launch_bounds__(BLOCK) void chunk_kernel(Params p) {
     }
   }
   __syncthreads();
-  const int arg = s_arg;
-
-  if constexpr (!FUSED) {
-    if (tid == 0) {
-      Partial q;
-      q.m = t.m;
-      q.s = t.s;
-      q.sz = t.sz;
-      q.bv = t.bv;
-      q.bi = arg;
-      q.xy = xy;
-      q.has_y = y_here ? 1 : 0;
-      q.pad = 0;
-      p.part[row * p.S + c] = q;
-    }
-    return;
-  } else {
-    if (tid == 0) {
-      double W, alpha, beta;
-      load_scales(p, W, alpha, beta);
-      const float wy = p.weight ? p.weight[y] : 1.0f;
-      RowScalars rs;
-      row_scalars(rs, t.m, t.s, t.sz, zval<SC>(p, xy), wy, W, static_cast<double>(p.V),
-                  p.eps, p.lam, alpha, beta);
-      rs.arg = arg;
-      rs.ok = (arg == y);
-      s_rs = rs;
-      write_row_outputs(p, row, rs.ce, rs.zl, rs.ok, arg);
-    }
-    __syncthreads();
-    __shared__ int s_last;
-    if (tid == 0 && p.epilogue) {
-      const RowScalars& rs = s_rs;
-      s_last = epilogue_publish(p, row, true, rs.ce, rs.zl, rs.ok, 1, gridDim.x);
-    }
-
-    // ---- pass 2: gradient from on-chip data, written over the logits ----
-    if (p.grad) {
-      const RowScalars rs = s_rs;
-      // Which of this thread's slots holds the target's vector, and where.
-      int ky = -1, yi = -1;
-      if (y < tail0) {
-        const int jy = static_cast<int>(y / EPV) - v0;
-        if (jy >= 0 && jy < nv && jy % BLOCK == tid) {
-          ky = jy / BLOCK;
-          yi = static_cast<int>(y % EPV);
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < NS; ++k) {
-        const int j = k * BLOCK + tid;
-        if (k * BLOCK < nv) {  // uniform: skip slots past the chunk
-          const u4 v = (k < NREG) ? r[k < NREG ? k : 0] : lds_rows[(k - NREG) * BLOCK + tid];
-          const u4 g = grad_vec<E, SC, SM>(p, rs, v, static_cast<int64_t>(v0) + j,
-                                           k == ky ? yi : -1);
-          // lanes past the chunk are outside the descriptor: the store is dropped
-          __builtin_amdgcn_raw_buffer_store_b128(g, rsrc, voff, k * BLOCK * 16, kStoreNT);
-        }
-      }
-      if (has_tail && tid < tail) {
-        const int64_t k = tail0 + tid;
-        const float wk = (SM && p.weight) ? p.weight[k] : 1.0f;
-        E::st(rp, k, grad_one<SC, SM>(p, rs, xt, wk, k == y));
-      }
-    }
-    if (p.epilogue) {
-      __syncthreads();
-      if (s_last) epilogue_reduce<BLOCK>(p);
-    }
+  if (tid == 0) {
+    Partial q;
+    q.m = t.m;
+    q.s = t.s;
+    q.sz = t.sz;
+    q.bv = t.bv;
+    q.bi = s_arg;
+    q.xy = xy;
+    q.has_y = y_here ? 1 : 0;
+    q.pad = 0;
+    p.part[row * p.S + c] = q;
   }
 }
 
@@ -453,6 +712,7 @@ __global__ __launch_bounds__(BLOCK) void splitv_finish_kernel(Params p) {
   constexpr int EPV = E::EPV;
   constexpr int U = 4;
   __shared__ RowScalars s_rs;
+  __shared__ float s_xy;
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.x / p.S;
   const int c = blockIdx.x - static_cast<int>(row) * p.S;
@@ -471,7 +731,7 @@ __global__ __launch_bounds__(BLOCK) void splitv_finish_kernel(Params p) {
 
   if (ignored || bad) {
     if (p.grad) {
-      for (int j = tid; j < nv; j += BLOCK) vp[j] = u4{0u, 0u, 0u, 0u};
+      for (int j = tid; j < nv; j += BLOCK) __builtin_nontemporal_store(u4{0u, 0u, 0u, 0u}, vp + j);
       if (has_tail && tid < tail) E::st(rp, tail0 + tid, 0.0f);
     }
     __shared__ int s_last0;
@@ -506,6 +766,7 @@ __global__ __launch_bounds__(BLOCK) void splitv_finish_kernel(Params p) {
     rs.arg = bi;
     rs.ok = (bi == y);
     s_rs = rs;
+    s_xy = xy;
     if (c == 0) write_row_outputs(p, row, rs.ce, rs.zl, rs.ok, bi);
   }
   __syncthreads();
@@ -528,9 +789,7 @@ __global__ __launch_bounds__(BLOCK) void splitv_finish_kernel(Params p) {
         const int j = j0 + u * BLOCK + tid;
         if (j < nv) {
           const int64_t jg = static_cast<int64_t>(v0) + j;
-          const int64_t d = y - jg * EPV;
-          const u4 g = grad_vec<E, SC, SM>(p, rs, v[u], jg,
-                                           (d >= 0 && d < EPV) ? static_cast<int>(d) : -1);
+          const u4 g = grad_vec<E, SC, SM>(p, rs, v[u], jg, -1);
           __builtin_nontemporal_store(g, vp + j);
         }
       }
@@ -540,6 +799,13 @@ __global__ __launch_bounds__(BLOCK) void splitv_finish_kernel(Params p) {
       const float xk = E::ld(rp, k);
       const float wk = (SM && p.weight) ? p.weight[k] : 1.0f;
       E::st(rp, k, grad_one<SC, SM>(p, rs, xk, wk, k == y));
+    }
+    // The one-hot term, rewritten by the thread that stored the target's
+    // vector (its own later store to the same address).
+    const int64_t jy = y / EPV - v0;
+    if (y < tail0 && jy >= 0 && jy < nv && tid == static_cast<int>(jy % BLOCK)) {
+      const float wy = (SM && p.weight) ? p.weight[y] : 1.0f;
+      E::st_nt(rp, y, grad_one<SC, SM>(p, rs, s_xy, wy, true));
     }
   }
   if (p.epilogue) {

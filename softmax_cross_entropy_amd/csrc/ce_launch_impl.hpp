@@ -12,12 +12,12 @@ template <class E, int SC, int SM>
 hipError_t launch_fused(int shape, const Params& p, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(p.rows));
   switch (shape) {
-    case 0: cedev::chunk_kernel<E, 256, 4, 0, SC, SM, true><<<grid, 256, 0, st>>>(p); break;
-    case 1: cedev::chunk_kernel<E, 256, 8, 0, SC, SM, true><<<grid, 256, 0, st>>>(p); break;
-    case 2: cedev::chunk_kernel<E, 256, 16, 0, SC, SM, true><<<grid, 256, 0, st>>>(p); break;
-    case 3: cedev::chunk_kernel<E, 512, 16, 0, SC, SM, true><<<grid, 512, 0, st>>>(p); break;
-    case 4: cedev::chunk_kernel<E, 512, 32, 0, SC, SM, true><<<grid, 512, 0, st>>>(p); break;
-    case 5: cedev::chunk_kernel<E, 512, 45, 19, SC, SM, true><<<grid, 512, 0, st>>>(p); break;
+    case 0: cedev::row_kernel<E, 256, 4, 0, SC, SM><<<grid, 256, 0, st>>>(p); break;
+    case 1: cedev::row_kernel<E, 256, 8, 0, SC, SM><<<grid, 256, 0, st>>>(p); break;
+    case 2: cedev::row_kernel<E, 256, 16, 0, SC, SM><<<grid, 256, 0, st>>>(p); break;
+    case 3: cedev::row_kernel<E, 512, 16, 0, SC, SM><<<grid, 512, 0, st>>>(p); break;
+    case 4: cedev::row_kernel<E, 512, 32, 0, SC, SM><<<grid, 512, 0, st>>>(p); break;
+    case 5: cedev::row_kernel<E, 512, 45, 19, SC, SM><<<grid, 512, 0, st>>>(p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -28,10 +28,10 @@ hipError_t launch_splitv(int shape, const Params& p, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(p.rows * p.S));
   switch (shape) {
     case kSplitShapeSmall:
-      cedev::chunk_kernel<E, 256, 4, 0, SC, SM, false><<<grid, 256, 0, st>>>(p);
+      cedev::splitv_partial_kernel<E, 256, 4, SC, SM><<<grid, 256, 0, st>>>(p);
       break;
     case kSplitShapeLarge:
-      cedev::chunk_kernel<E, 512, 16, 0, SC, SM, false><<<grid, 512, 0, st>>>(p);
+      cedev::splitv_partial_kernel<E, 512, 16, SC, SM><<<grid, 512, 0, st>>>(p);
       break;
     default: return hipErrorInvalidValue;
   }
