@@ -184,6 +184,9 @@ CE_API ce_status ce_forward(void* logits, int dtype, int64_t rows, int64_t V, in
   p.ignore_index = ignore_index;
   p.eps = label_smoothing;
   p.lam = lse_square_scale;
+  p.one_minus_eps = 1.0 - static_cast<double>(label_smoothing);
+  p.eps_over_v = static_cast<double>(label_smoothing) / static_cast<double>(V);
+  p.lam_d = lse_square_scale;
   p.softcap = softcap;
   p.inv_softcap = softcap > 0.0f ? 1.0f / softcap : 0.0f;
   p.reduction = reduction;

@@ -180,7 +180,9 @@ struct Header {
   uint32_t err;          // bit 0: a target outside [0, V) that is not ignore_index
   uint32_t pad0[23];
   uint32_t done;         // arrival counter of the last-block epilogue (byte 128)
-  uint32_t pad1[31];
+  uint32_t pad1[15];
+  uint32_t next;         // row claims of the persistent row kernel (byte 192)
+  uint32_t pad2[15];
 };
 static_assert(sizeof(Header) == 256, "the header fills the workspace's first 256 bytes");
 
@@ -202,6 +204,7 @@ struct Params {
   const float* weight;                 // (V) or null
   int64_t ignore_index;
   float eps, lam, softcap, inv_softcap;
+  double one_minus_eps, eps_over_v, lam_d;  // host-computed row-invariant terms
   int reduction;                       // 0 none, 1 mean, 2 sum
   int grad;                            // write d loss / d logits in place
   int epilogue;                        // run the last-block reduction
@@ -293,21 +296,22 @@ struct RowScalars {
 // z-loss each contribute to loss and gradient; PyTorch's convention for how
 // smoothing mass and class weights combine.)
 __device__ __forceinline__ void row_scalars(RowScalars& r, float m, float s, float sz, float zy,
-                                            float wy, double W, double V, double eps,
-                                            double lam, double alpha, double beta) {
+                                            float wy, double W, const Params& p, double alpha,
+                                            double beta) {
   const float l2s = lg2(s);
   const double lns = static_cast<double>(l2s) * static_cast<double>(kLn2);
   const double lse = static_cast<double>(m) + lns;
   const double wyd = wy;
-  const double ce = wyd * (1.0 - eps) * ((static_cast<double>(m) - zy) + lns) +
-                    (eps / V) * (W * lse - static_cast<double>(sz));
+  const double ome = p.one_minus_eps, epv = p.eps_over_v, lam = p.lam_d;
+  const double ce = wyd * ome * ((static_cast<double>(m) - zy) + lns) +
+                    epv * (W * lse - static_cast<double>(sz));
   r.m = m;
   r.l2s = l2s;
   r.ce = static_cast<float>(ce);
   r.zl = static_cast<float>(lam * lse * lse);
-  r.A = static_cast<float>(alpha * (wyd * (1.0 - eps) + (eps / V) * W) + beta * 2.0 * lam * lse);
-  r.B = static_cast<float>(alpha * eps / V);
-  r.C = static_cast<float>(alpha * wyd * (1.0 - eps));
+  r.A = static_cast<float>(alpha * (wyd * ome + epv * W) + beta * 2.0 * lam * lse);
+  r.B = static_cast<float>(alpha * epv);
+  r.C = static_cast<float>(alpha * wyd * ome);
 }
 
 // ---------------------------------------------------------------------------
@@ -348,7 +352,7 @@ __device__ __forceinline__ bool epilogue_publish(const Params& p, int64_t row, b
 
 // Whole block, in the block that arrived last only.
 template <int BLOCK>
-__device__ void epilogue_reduce(const Params& p) {
+__device__ __forceinline__ void epilogue_reduce(const Params& p) {
   __shared__ double s_red[2][BLOCK / 64];
   __shared__ int64_t s_cnt[2][BLOCK / 64];
   const int tid = threadIdx.x;

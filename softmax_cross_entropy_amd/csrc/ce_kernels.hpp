@@ -7,7 +7,8 @@
 // only rescales that gradient by grad_output.
 //
 // MI355X design (not the page's Triton loop):
-//  * row_kernel: one workgroup per row. The whole row is read from HBM once
+//  * rows_kernel: persistent workgroups, one row at a time each, rows claimed
+//    in the order workgroups finish. The whole row is read from HBM once
 //    with non-temporal dwordx4 buffer loads and kept on chip (VGPRs, plus
 //    LDS filled by buffer_load ... lds for the largest rows), so the
 //    gradient pass reads registers instead of re-reading HBM: 1 read + 1
@@ -209,6 +210,18 @@ __device__ __forceinline__ u4 grad_vec(const Params& p, const RowScalars& rs, co
 
 // Combine the per-wave Acc records in wave order (fixed, deterministic).
 template <int NW>
+__device__ __forceinline__ Acc block_combine_p(const Acc* s) {
+  Acc t = s[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) {
+    ms_combine(t.m, t.s, s[w].m, s[w].s);
+    t.sz += s[w].sz;
+    arg_combine(t.bv, t.bi, s[w].bv, s[w].bi);
+  }
+  return t;
+}
+
+template <int NW>
 __device__ __forceinline__ Acc block_combine(const Acc (&s)[NW]) {
   Acc t = s[0];
 #pragma unroll
@@ -292,10 +305,10 @@ __device__ __forceinline__ u4 grad_vec_e(const Params& p, const RowScalars& rs, 
 }
 
 // Outputs of a row that is ignored (gradient exactly +0.0, never read) or
-// whose target is out of range (NaN loss); shared by the one-row-per-block
-// kernels.
+// whose target is out of range (NaN loss). Returns, in thread 0, whether
+// this row's publication was the last of the launch.
 template <class E, int BLOCK>
-__device__ __forceinline__ void skipped_row(const Params& p, int64_t row, bool bad, char* rp,
+__device__ __forceinline__ bool skipped_row(const Params& p, int64_t row, bool bad, char* rp,
                                             int nv, int tail) {
   const int tid = threadIdx.x;
   if (p.grad) {
@@ -303,20 +316,28 @@ __device__ __forceinline__ void skipped_row(const Params& p, int64_t row, bool b
     for (int j = tid; j < nv; j += BLOCK) __builtin_nontemporal_store(u4{0u, 0u, 0u, 0u}, vp + j);
     if (tid < tail) E::st(rp, static_cast<int64_t>(nv) * E::EPV + tid, 0.0f);
   }
-  __shared__ int s_last0;
+  bool last = false;
   if (tid == 0) {
     const float q = bad ? __builtin_nanf("") : 0.0f;
     write_row_outputs(p, row, q, q, 0, -1);
-    if (p.epilogue) s_last0 = epilogue_publish(p, row, true, q, q, 0, 0, gridDim.x);
+    if (p.epilogue) last = epilogue_publish(p, row, true, q, q, 0, 0, static_cast<uint32_t>(p.rows));
   }
-  if (p.epilogue) {
-    __syncthreads();
-    if (s_last0) epilogue_reduce<BLOCK>(p);
-  }
+  return last;
 }
 
+// Block-shared state of one row in flight.
+template <int BLOCK, int NLDS>
+struct RowShared {
+  u4 rows[NLDS > 0 ? NLDS * BLOCK : 1];  // LDS slots
+  Acc acc[BLOCK / 64];
+  int cand[BLOCK / 64];
+  RowScalars rs;
+  float xy;
+  int64_t next_row, next_y;  // persistent kernel: the row claimed next and its target
+};
+
 // ---------------------------------------------------------------------------
-// row_kernel: one workgroup per row; the row is read from HBM once and kept
+// fused_row: one row in one workgroup; the row is read from HBM once and kept
 // on chip. Slots: thread tid owns vectors j = k * BLOCK + tid, for k < NREG
 // in VGPRs and for NREG <= k < NREG + NLDS in LDS; the row tail (V % EPV
 // elements) is held by threads tid < tail.
@@ -331,8 +352,28 @@ __device__ __forceinline__ void skipped_row(const Params& p, int64_t row, bool b
 // multiply (or fma) per element by a per-group scale; other rows keep the
 // logits and the gradient pass recomputes the exponential.
 // ---------------------------------------------------------------------------
+// Row claims of the persistent kernel: workgroup b starts with row b; once
+// a row's pass 1 is done, thread 0 claims the next one (gridDim.x + the
+// claim counter), so rows go to workgroups in the order they finish. Every
+// row processed takes exactly one claim, so the claim that returns rows - 1
+// is the launch's last: it resets the counter for the next launch.
+struct RowClaim {
+  uint32_t c;
+  __device__ __forceinline__ void issue(const Params& p) {
+    c = __hip_atomic_fetch_add(&p.hdr->next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // Thread 0, once the claim has returned: the next row (>= rows: none), the
+  // load of its target, and the counter reset by the last claim.
+  __device__ __forceinline__ int64_t row(const Params& p) const {
+    if (c == static_cast<uint32_t>(p.rows - 1))
+      __hip_atomic_store(&p.hdr->next, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return static_cast<int64_t>(gridDim.x) + c;
+  }
+};
+
 template <class E, int BLOCK, int NREG, int NLDS, int SC, int SM>
-__global__ __launch_bounds__(BLOCK) void row_kernel(Params p) {
+__device__ __forceinline__ bool fused_row(const Params& p, int64_t row, int64_t y,
+                                          RowShared<BLOCK, NLDS>& sh) {
   constexpr int EPV = E::EPV;
   constexpr int NS = NREG + NLDS;
   constexpr int NW = BLOCK / 64;
@@ -340,31 +381,42 @@ __global__ __launch_bounds__(BLOCK) void row_kernel(Params p) {
   constexpr int GS = (EPV == 4) ? 8 : 2;
   constexpr int NG = (NS + GS - 1) / GS;
   constexpr int kRegPolicy = (NLDS == 0 || EPV == 8) ? kLoadNT : 0;
-  __shared__ u4 lds_rows[NLDS > 0 ? NLDS * BLOCK : 1];
-  __shared__ Acc s_acc[NW];
-  __shared__ int s_cand[NW];
-  __shared__ RowScalars s_rs;
-  __shared__ float s_xy;
-  __shared__ int s_last;
+  u4* lds_rows = sh.rows;
+  Acc* s_acc = sh.acc;
+  int* s_cand = sh.cand;
 
-  const int tid = threadIdx.x;
+  // Opaque per call: in the persistent loop, values derived from the thread
+  // index and the row length are recomputed per row instead of being
+  // hoisted out of the loop into registers (which would spill).
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t row = blockIdx.x;
-  const int64_t y = p.target[row];
   const bool ignored = (y == p.ignore_index);
   const bool bad = !ignored && (y < 0 || y >= p.V);
   char* rp = row_ptr(p, row, E::BYTES);
-  const int nv = static_cast<int>(p.V / EPV);
+  int nv = __builtin_amdgcn_readfirstlane(static_cast<int>(p.V / EPV));
+  asm volatile("" : "+s"(nv));
   const int tail = static_cast<int>(p.V - static_cast<int64_t>(nv) * EPV);
   const int64_t tail0 = static_cast<int64_t>(nv) * EPV;
 
   if (ignored || bad) {
     // Ignored rows are never read; their gradient is exactly +0.0
     // (tt-mlir PR #9324 page: ignored rows, also with non-finite logits).
-    skipped_row<E, BLOCK>(p, row, bad, rp, nv, tail);
-    return;
+    // Every wave has read the previous row's next_row before it is
+    // overwritten (this path has no other barrier before the write).
+    __syncthreads();
+    if (tid == 0) {
+      RowClaim cl;
+      cl.issue(p);
+      const int64_t nr = cl.row(p);
+      sh.next_row = nr;
+      sh.next_y = nr < p.rows ? p.target[nr] : 0;
+    }
+    __syncthreads();
+    return skipped_row<E, BLOCK>(p, row, bad, rp, nv, tail);
   }
+  RowClaim claim;
 
   // ---- issue every load of the row up front ----
   // Raw buffer loads over a descriptor that spans exactly the row's vectors:
@@ -484,6 +536,12 @@ __global__ __launch_bounds__(BLOCK) void row_kernel(Params p) {
     if constexpr (SM) tsz = p.weight ? __builtin_fmaf(p.weight[tail0 + tid], z, tsz) : tsz + z;
   }
 
+  // Claim the next row now that this one is almost done (claiming earlier
+  // would hold rows back from workgroups that finish first); thread 0 reads
+  // the claim back while it computes the row scalars.
+  int64_t next_row = 0, next_y = 0;
+  if (tid == 0) claim.issue(p);
+
   Acc a;
   a.m = tm;
   a.s = ts;
@@ -493,7 +551,7 @@ __global__ __launch_bounds__(BLOCK) void row_kernel(Params p) {
   wave_reduce(a);
   if (lane == 0) s_acc[wave] = a;
   __syncthreads();
-  const Acc t = block_combine<NW>(s_acc);
+  const Acc t = block_combine_p<NW>(s_acc);
 
   // ---- argmax: threads holding the row maximum find its first position in
   // their first group holding it; the block takes the lowest index. With
@@ -538,6 +596,8 @@ __global__ __launch_bounds__(BLOCK) void row_kernel(Params p) {
   __syncthreads();
 
   if (tid == 0) {
+    next_row = claim.row(p);
+    if (next_row < p.rows) next_y = p.target[next_row];
     int arg = s_cand[0];
 #pragma unroll
     for (int w = 1; w < NW; ++w) arg = min(arg, s_cand[w]);
@@ -546,23 +606,25 @@ __global__ __launch_bounds__(BLOCK) void row_kernel(Params p) {
     load_scales(p, W, alpha, beta);
     const float wy = p.weight ? p.weight[y] : 1.0f;
     RowScalars rs;
-    row_scalars(rs, t.m, t.s, t.sz, zval<SC>(p, xy), wy, W, static_cast<double>(p.V), p.eps,
-                p.lam, alpha, beta);
+    row_scalars(rs, t.m, t.s, t.sz, zval<SC>(p, xy), wy, W, p, alpha, beta);
     rs.arg = arg;
     rs.ok = (arg == y);
-    s_rs = rs;
-    s_xy = xy;
+    sh.rs = rs;
+    sh.xy = xy;
+    sh.next_row = next_row;
+    sh.next_y = next_y;
     write_row_outputs(p, row, rs.ce, rs.zl, rs.ok, arg);
   }
   __syncthreads();
+  bool last = false;
   if (tid == 0 && p.epilogue) {
-    const RowScalars& rs = s_rs;
-    s_last = epilogue_publish(p, row, true, rs.ce, rs.zl, rs.ok, 1, gridDim.x);
+    const RowScalars& rs = sh.rs;
+    last = epilogue_publish(p, row, true, rs.ce, rs.zl, rs.ok, 1, static_cast<uint32_t>(p.rows));
   }
 
   // ---- pass 2: gradient from on-chip data, written over the logits ----
   if (p.grad) {
-    const RowScalars rs = s_rs;
+    const RowScalars rs = sh.rs;
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
       if (g * GS * BLOCK < nv) {
@@ -596,10 +658,37 @@ __global__ __launch_bounds__(BLOCK) void row_kernel(Params p) {
     // lands last). No per-element test for the target in the loop above.
     if (y < tail0 && tid == static_cast<int>((y / EPV) % BLOCK)) {
       const float wy = (SM && p.weight) ? p.weight[y] : 1.0f;
-      E::template st_buf<kStoreNT>(rsrc, static_cast<int>(y), grad_one<SC, SM>(p, rs, s_xy, wy, true));
+      E::template st_buf<kStoreNT>(rsrc, static_cast<int>(y), grad_one<SC, SM>(p, rs, sh.xy, wy, true));
     }
   }
+  return last;
+}
+
+__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<int>(v >> 32));
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<int>(v));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// Persistent variant: gridDim.x resident workgroups take rows in the order
+// they finish (RowClaim), so the loads of a workgroup's next row are issued
+// as soon as the gradient stores of its current one are (they drain while
+// the next row arrives) instead of after a workgroup teardown and launch.
+template <class E, int BLOCK, int NREG, int NLDS, int SC, int SM>
+__global__ __launch_bounds__(BLOCK) void rows_kernel(Params p) {
+  __shared__ RowShared<BLOCK, NLDS> sh;
+  __shared__ int s_last;
+  bool last = false;
+  int64_t row = blockIdx.x;
+  int64_t y = p.target[row];
+  while (true) {
+    last |= fused_row<E, BLOCK, NREG, NLDS, SC, SM>(p, row, y, sh);
+    row = uniform_i64(sh.next_row);
+    y = uniform_i64(sh.next_y);
+    if (row >= p.rows) break;
+  }
   if (p.epilogue) {
+    if (threadIdx.x == 0) s_last = last;
     __syncthreads();
     if (s_last) epilogue_reduce<BLOCK>(p);
   }
@@ -608,7 +697,7 @@ __global__ __launch_bounds__(BLOCK) void row_kernel(Params p) {
 // ---------------------------------------------------------------------------
 // Split-V stage 1: workgroup (row, c) reads chunk c of the row once and
 // writes its partial (max, sum, smoothing sum, argmax, target logit). Slots
-// as in row_kernel, over the chunk's vectors.
+// as in fused_row, over the chunk's vectors.
 // ---------------------------------------------------------------------------
 template <class E, int BLOCK, int NREG, int SC, int SM>
 __global__ __launch_bounds__(BLOCK) void splitv_partial_kernel(Params p) {
@@ -761,8 +850,7 @@ __global__ __launch_bounds__(BLOCK) void splitv_finish_kernel(Params p) {
     load_scales(p, W, alpha, beta);
     const float wy = p.weight ? p.weight[y] : 1.0f;
     RowScalars rs;
-    row_scalars(rs, m, s, sz, zval<SC>(p, xy), wy, W, static_cast<double>(p.V), p.eps, p.lam,
-                alpha, beta);
+    row_scalars(rs, m, s, sz, zval<SC>(p, xy), wy, W, p, alpha, beta);
     rs.arg = bi;
     rs.ok = (bi == y);
     s_rs = rs;
@@ -858,8 +946,7 @@ __global__ __launch_bounds__(BLOCK) void row_scalar_kernel(Params p) {
     load_scales(p, W, alpha, beta);
     const float wy = p.weight ? p.weight[y] : 1.0f;
     RowScalars rs;
-    row_scalars(rs, t.m, t.s, t.sz, zval<SC>(p, E::ld(rp, y)), wy, W, static_cast<double>(p.V),
-                p.eps, p.lam, alpha, beta);
+    row_scalars(rs, t.m, t.s, t.sz, zval<SC>(p, E::ld(rp, y)), wy, W, p, alpha, beta);
     rs.arg = t.bi;
     rs.ok = (t.bi == y);
     s_rs = rs;

@@ -14,13 +14,14 @@ struct Shape {
   int block, nreg, nlds;
   int cap() const { return block * (nreg + nlds); }
 };
-constexpr int kNumShapes = 6;
+constexpr int kNumShapes = 7;
 constexpr Shape kShapes[kNumShapes] = {
     {256, 4, 0},    // 1024 vectors:  16 KiB rows
     {256, 8, 0},    // 2048 vectors:  32 KiB
     {256, 16, 0},   // 4096 vectors:  64 KiB
     {512, 16, 0},   // 8192 vectors: 128 KiB
     {512, 32, 0},   // 16384 vectors: 256 KiB
+    {512, 44, 19},  // 32256 vectors: 504 KiB (176 VGPRs + 152 KiB LDS)
     {512, 45, 19},  // 32768 vectors: 512 KiB (180 VGPRs + 152 KiB LDS)
 };
 constexpr int kSplitShapeSmall = 0;  // split-V chunk shapes

@@ -8,19 +8,44 @@ namespace cehost {
 
 using cedev::Params;
 
+// Persistent row kernel: as many workgroups as fit on the device at once
+// (occupancy x compute units, cached per device), at most one per row.
+template <class E, int SC, int SM, int BLOCK, int NREG, int NLDS>
+hipError_t launch_rows(const Params& p, hipStream_t st) {
+  constexpr int kMaxDevices = 64;
+  static int resident[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  int r = (dev >= 0 && dev < kMaxDevices) ? resident[dev] : 0;
+  if (r == 0) {
+    int per_cu = 0, ncu = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &per_cu, cedev::rows_kernel<E, BLOCK, NREG, NLDS, SC, SM>, BLOCK, 0);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    r = (per_cu > 0 ? per_cu : 1) * (ncu > 0 ? ncu : 1);
+    if (dev >= 0 && dev < kMaxDevices) resident[dev] = r;
+  }
+  const int64_t grid = p.rows < r ? p.rows : r;
+  cedev::rows_kernel<E, BLOCK, NREG, NLDS, SC, SM>
+      <<<dim3(static_cast<unsigned>(grid)), BLOCK, 0, st>>>(p);
+  return hipGetLastError();
+}
+
 template <class E, int SC, int SM>
 hipError_t launch_fused(int shape, const Params& p, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>(p.rows));
   switch (shape) {
-    case 0: cedev::row_kernel<E, 256, 4, 0, SC, SM><<<grid, 256, 0, st>>>(p); break;
-    case 1: cedev::row_kernel<E, 256, 8, 0, SC, SM><<<grid, 256, 0, st>>>(p); break;
-    case 2: cedev::row_kernel<E, 256, 16, 0, SC, SM><<<grid, 256, 0, st>>>(p); break;
-    case 3: cedev::row_kernel<E, 512, 16, 0, SC, SM><<<grid, 512, 0, st>>>(p); break;
-    case 4: cedev::row_kernel<E, 512, 32, 0, SC, SM><<<grid, 512, 0, st>>>(p); break;
-    case 5: cedev::row_kernel<E, 512, 45, 19, SC, SM><<<grid, 512, 0, st>>>(p); break;
+    case 0: return launch_rows<E, SC, SM, 256, 4, 0>(p, st);
+    case 1: return launch_rows<E, SC, SM, 256, 8, 0>(p, st);
+    case 2: return launch_rows<E, SC, SM, 256, 16, 0>(p, st);
+    case 3: return launch_rows<E, SC, SM, 512, 16, 0>(p, st);
+    case 4: return launch_rows<E, SC, SM, 512, 32, 0>(p, st);
+    case 5: return launch_rows<E, SC, SM, 512, 44, 19>(p, st);
+    case 6: return launch_rows<E, SC, SM, 512, 45, 19>(p, st);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 template <class E, int SC, int SM>

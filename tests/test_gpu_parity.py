@@ -292,6 +292,63 @@ def test_determinism_bitwise():
 
 
 # ---------------------------------------------------------------------------
+# Every fused row shape, with more rows than workgroups fit on the device at
+# once (so the persistent row kernel claims rows dynamically), a ragged row
+# tail, a partial last slot and many ignored rows; every element compared.
+# ---------------------------------------------------------------------------
+
+SHAPE_CASES = [
+    # (dtype, V, rows, options): V picks the shape, rows exceed its resident grid
+    (torch.float32, 4001, 2600, dict()),                              # 256 x 4
+    (torch.float32, 16001, 1100, dict(eps=0.1, lam=1e-3)),            # 256 x 16
+    (torch.float32, 65001, 300, dict(weight=True, eps=0.05)),         # 512 x 32
+    (torch.float32, 129001, 300, dict(lam=1e-4)),                     # 512 x 44 + 19 LDS
+    (torch.bfloat16, 16001, 2600, dict(softcap=20.0)),                # 256 x 8
+    (torch.bfloat16, 65001, 600, dict()),                             # 512 x 16
+    (torch.bfloat16, 131001, 300, dict(weight=True, eps=0.1, softcap=30.0, lam=1e-4)),  # 512 x 32
+]
+
+
+@pytest.mark.parametrize("case", range(len(SHAPE_CASES)))
+@pytest.mark.parametrize("reduction", ["mean", "none"])
+def test_fused_shapes_many_rows(case, reduction):
+    dtype, V, rows, o = SHAPE_CASES[case]
+    seed = 100 + case
+    x = synth.make_logits(rows, V, dtype, 2.5, seed)
+    t = synth.make_targets(rows, V, seed, rows * 3 // 10)
+    wt = None
+    if o.get("weight"):
+        wt = 0.5 + 1.5 * torch.rand(V, generator=torch.Generator().manual_seed(seed))
+    stride = (V + 7) // 8 * 8  # 16-byte aligned rows: the vector path
+    run_case(x, t, weight=wt, eps=o.get("eps", 0.0), lam=o.get("lam", 0.0),
+             softcap=o.get("softcap"), reduction=reduction, path="fused", stride=stride,
+             name=f"shape-{case}")
+
+
+def test_persistent_claims_reset_between_calls():
+    """Row claims start from zero on every call: the same batch gives the same
+    bits after calls of other sizes share the workspace."""
+    V = 129001
+    xa = synth.make_logits(600, V, torch.float32, 2.0, 91)
+    ta = synth.make_targets(600, V, 91, 40)
+    xb = synth.make_logits(290, V, torch.float32, 2.0, 92)
+    tb = synth.make_targets(290, V, 92, 200)
+    outs = []
+    for x, t in ((xa, ta), (xb, tb), (xa, ta), (xb, tb), (xa, ta)):
+        _announce(name="claims", rows=x.shape[0], V=V)
+        xd = _padded(x, V + 7)
+        assert _plan(xd, None, 0.0, 0) == "fused"
+        r = forward_raw(xd, t.to(DEV), reduction="sum", z_loss=True, token_accuracy=True,
+                        argmax=True, counts=True)
+        torch.cuda.synchronize()
+        outs.append((xd.cpu(), [o.cpu() for o in r if o is not None]))
+    for a, b in ((0, 2), (0, 4), (1, 3)):
+        assert torch.equal(outs[a][0].view(torch.int32), outs[b][0].view(torch.int32))
+        for oa, ob in zip(outs[a][1], outs[b][1]):
+            assert torch.equal(oa, ob)
+
+
+# ---------------------------------------------------------------------------
 # Full-size workloads in the benchmark's launch configuration
 # ---------------------------------------------------------------------------
 
