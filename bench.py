@@ -74,6 +74,51 @@ def traffic_from_profiles(workload: str, kernel_key: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def _pmc_per_kernel(csv_path: str, counter: str):
+    """Per-dispatch values (KiB) of one rocprofv3 --pmc counter, by kernel name."""
+    import csv
+    out = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def write_traffic(workload: str, fetch_csv: str, write_csv: str) -> dict:
+    """HBM bytes per launch of the fused kernel from two rocprofv3 --pmc runs of
+    this benchmark (FETCH_SIZE, then WRITE_SIZE). Each counter is scaled by
+    what it reads for the runtime's copy kernel moving the logits buffer (a
+    known size: every step's pristine copy of the batch), and the result is
+    stored under profiles/ with the hash of the kernel sources it was taken on."""
+    import synth
+    w = synth.WORKLOADS[workload]
+    nbytes = w.rows * w.V * w.elem_bytes
+    rec = {"workload": workload, "source_hash": source_hash(), "copy_bytes": nbytes}
+    total = 0.0
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        per = _pmc_per_kernel(path, counter)
+        copies = [v for k, vs in per.items() if "copyBuffer" in k for v in vs]
+        big = [v for v in copies if v >= 0.9 * max(copies)]
+        factor = nbytes / (sum(big) / len(big) * 1024.0)
+        kern = {k: vs for k, vs in per.items() if "rows_kernel" in k}
+        if len(kern) != 1:
+            raise SystemExit(f"expected one fused kernel in {path}, found {list(kern)}")
+        name, vs = next(iter(kern.items()))
+        raw = sum(vs) / len(vs) * 1024.0
+        rec[counter] = {"kernel": name, "dispatches": len(vs), "raw_bytes": raw,
+                        "copy_dispatches": len(big), "copy_factor": factor,
+                        "bytes": raw * factor}
+        total += raw * factor
+    rec["hbm_bytes_per_launch"] = total
+    os.makedirs(PROFILES, exist_ok=True)
+    out = os.path.join(PROFILES, f"ce_fused_{workload}_traffic.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+    return rec
+
+
 def cpu_baseline(x_host, t_host, weight_host, w, reduction, budget_s=12.0):
     """Time the float64 oracle, as it is, on a bounded sample of the rows."""
     import numpy as np
@@ -113,7 +158,13 @@ def main(argv=None) -> int:
     ap.add_argument("--reduction", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the fused kernel's HBM traffic from two rocprofv3 --pmc "
+                         "counter_collection.csv files of this benchmark, then exit")
     a = ap.parse_args(argv)
+    if a.traffic:
+        write_traffic(a.workload, *a.traffic)
+        return 0
 
     if a.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (the path shards "
