@@ -306,6 +306,10 @@ SHAPE_CASES = [
     (torch.bfloat16, 16001, 2600, dict(softcap=20.0)),                # 256 x 8
     (torch.bfloat16, 65001, 600, dict()),                             # 512 x 16
     (torch.bfloat16, 131001, 300, dict(weight=True, eps=0.1, softcap=30.0, lam=1e-4)),  # 512 x 32
+    # the two largest shapes with every per-element option (fewer rows: oracle time)
+    (torch.float32, 130001, 40, dict(weight=True, eps=0.1, softcap=15.0)),    # 512 x 45 + 19 LDS
+    (torch.bfloat16, 250001, 40, dict(eps=0.1, softcap=30.0, lam=1e-4)),      # 512 x 44 + 19 LDS
+    (torch.bfloat16, 262001, 24, dict(weight=True, eps=0.2)),                 # 512 x 45 + 19 LDS
 ]
 
 
