@@ -1,12 +1,15 @@
 """Benchmark of the fused softmax cross-entropy forward + gradient on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--mode MODE]
 
 A step is one pass of the whole hot path over one batch of synthetic logits
 already resident in HBM: ce_forward (loss + gradient written over the
 logits) followed by ce_backward with grad_output = 1 (the training call
 pattern). Every step gets its own pristine copy of the batch (prepared
 before the timed region), so no step reads a gradient left by another.
+--mode nograd times the forward without the gradient (an evaluation pass);
+--mode recompute keeps the logits and times the gradient recomputed from
+them (ce_backward_recompute) after that forward.
 
 The default workload is 1023 rows x V = 128256 fp32 logits, reduction
 "sum" (the tt-mlir PR #9324 page's before/after shape). Prints one JSON
@@ -47,11 +50,18 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(w, reduction: str, n_counted: int) -> int:
-    """Bytes the method itself must move: each counted row read once, every
-    row's gradient written once, targets, class weights and the outputs."""
+def algorithmic_bytes(w, reduction: str, n_counted: int, mode: str = "fused") -> int:
+    """Bytes the method itself must move in the timed kernel: each counted row
+    read once, every row's gradient written once (not in the no-gradient
+    forward), targets, class weights and the outputs; the recomputing
+    backward also reads the per-row statistics."""
     e = w.elem_bytes
-    b = n_counted * w.V * e + w.rows * w.V * e + w.rows * 8
+    b = n_counted * w.V * e + w.rows * 8
+    if mode != "nograd":
+        b += w.rows * w.V * e
+    if mode == "recompute":
+        b += w.rows * 8
+        return b
     if w.weights:
         b += w.V * 4
     n_out = 1 + (1 if w.want_z_loss else 0) + (1 if w.want_accuracy else 0)
@@ -119,6 +129,69 @@ def write_traffic(workload: str, fetch_csv: str, write_csv: str) -> dict:
     return rec
 
 
+def sweep(steps: int, warmup: int) -> None:
+    """Context numbers: the Liger CE profile's benchmark sweep shape (B=8, T=512
+    rows, bf16, V from 4096 to 131072, mean) for this library's fused forward +
+    gradient + backward step, next to PyTorch eager F.cross_entropy forward +
+    backward on the same GPU and batch. One JSON line per V."""
+    import torch
+    import torch.nn.functional as F
+    import synth
+    from softmax_cross_entropy_amd import _lib
+    from softmax_cross_entropy_amd.functional import _workspace
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    rows = 8 * 512
+    for V in (4096, 8192, 16384, 32768, 65536, 131072):
+        x0 = synth.make_logits(rows, V, torch.bfloat16, 1.0, 200 + V, dev)
+        t = synth.make_targets(rows, V, 200 + V, rows // 20).to(dev)
+        nb = steps + warmup
+        bufs = [x0.clone() for _ in range(nb)]
+        loss = torch.empty((), device=dev, dtype=torch.float32)
+        go = torch.ones((), device=dev, dtype=torch.float32)
+        dt = _lib.CE_BF16
+        wsb = _lib.ce_workspace_bytes(rows, V, dt, _lib.CE_F_GRAD)
+        ws = _workspace(dev, wsb)
+        s = stream.cuda_stream
+
+        def ours(b):
+            _lib.check(_lib.ce_forward(b.data_ptr(), dt, rows, V, V, t.data_ptr(), 0, -100, 0.0,
+                                       0.0, 0.0, _lib.CE_RED_MEAN, _lib.CE_F_GRAD,
+                                       loss.data_ptr(), 0, 0, 0, 0, 0, ws.data_ptr(), wsb, s),
+                       "ce_forward")
+            _lib.check(_lib.ce_backward(b.data_ptr(), dt, rows, V, V, go.data_ptr(), 0, s),
+                       "ce_backward")
+
+        def eager(b):
+            xb = b.requires_grad_(True)
+            F.cross_entropy(xb, t, ignore_index=-100).backward()
+            xb.grad = None
+            xb.requires_grad_(False)
+
+        res = {}
+        for name, fn in (("this_library", ours), ("torch_eager", eager)):
+            for i in range(warmup):
+                fn(bufs[i])
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(steps):
+                fn(bufs[warmup + i])
+            e1.record(stream)
+            torch.cuda.synchronize()
+            res[name] = e0.elapsed_time(e1) / steps
+            bufs = [x0.clone() for _ in range(nb)]
+        nbytes = 2 * rows * V * 2
+        print(json.dumps({"sweep": "Liger CE profile benchmark shape (B=8, T=512, bf16, mean)",
+                          "V": V, "rows": rows,
+                          "ms_per_step": res,
+                          "speedup_vs_torch_eager": res["torch_eager"] / res["this_library"],
+                          "GBps_1R1W": {k: nbytes / (v * 1e-3) / 1e9 for k, v in res.items()}}),
+              flush=True)
+        del bufs, x0
+
+
 def cpu_baseline(x_host, t_host, weight_host, w, reduction, budget_s=12.0):
     """Time the float64 oracle, as it is, on a bounded sample of the rows."""
     import numpy as np
@@ -158,12 +231,27 @@ def main(argv=None) -> int:
     ap.add_argument("--reduction", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--mode", choices=("fused", "nograd", "recompute"), default="fused",
+                    help="fused: forward + gradient in place, then the scaling backward "
+                         "(default); nograd: forward without the gradient (logits only "
+                         "read); recompute: forward without the gradient, then the gradient "
+                         "recomputed from the kept logits into another buffer (roofline of "
+                         "the recomputing kernel)")
+    ap.add_argument("--path", choices=("auto", "fused", "splitv", "scalar"), default="auto",
+                    help="force a kernel path (default: the library's choice)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="context sweep over V at the Liger benchmark shape, this library "
+                         "against PyTorch eager F.cross_entropy (JSON line per V), then exit")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the fused kernel's HBM traffic from two rocprofv3 --pmc "
                          "counter_collection.csv files of this benchmark, then exit")
     a = ap.parse_args(argv)
     if a.traffic:
         write_traffic(a.workload, *a.traffic)
+        return 0
+
+    if a.sweep:
+        sweep(a.steps, a.warmup)
         return 0
 
     if a.gpus != 1:
@@ -193,7 +281,9 @@ def main(argv=None) -> int:
         sample_host = (x.view(torch.int16).numpy().view("uint16") if x.dtype == torch.bfloat16
                        else x.numpy(), t_host[:256])
     dt = _lib.dtype_code(w.dtype)
-    flags = _lib.CE_F_GRAD
+    flags = _lib.CE_F_GRAD if a.mode == "fused" else 0
+    flags |= {"auto": 0, "fused": _lib.CE_F_FORCE_FUSED, "splitv": _lib.CE_F_FORCE_SPLITV,
+              "scalar": _lib.CE_F_FORCE_SCALAR}[a.path]
     rows, V = w.rows, w.V
     f32 = dict(device=dev, dtype=torch.float32)
     loss = torch.empty((rows,) if red == "none" else (), **f32)
@@ -201,6 +291,8 @@ def main(argv=None) -> int:
     acc = torch.empty_like(loss) if w.want_accuracy else None
     arg = torch.empty((rows,), device=dev, dtype=torch.int64) if w.want_argmax else None
     go = torch.ones((), **f32)
+    stats = torch.empty((rows, 2), **f32) if a.mode == "recompute" else None
+    gbuf = torch.empty_like(inp.logits) if a.mode == "recompute" else None
     ws_bytes = _lib.ce_workspace_bytes(rows, V, dt, flags)
     ws = _workspace(dev, ws_bytes)
     P = lambda t: 0 if t is None else t.data_ptr()  # noqa: E731
@@ -210,20 +302,30 @@ def main(argv=None) -> int:
                                              w.label_smoothing, flags)]
     red_code = _lib.REDUCTION_CODES[red]
 
-    def step(buf):
+    def fwd(buf):
         st = _lib.ce_forward(P(buf), dt, rows, V, buf.stride(0), tgt, wt, -100,
                              w.label_smoothing, w.lse_square_scale, w.softcap, red_code, flags,
-                             P(loss), P(z_loss), P(acc), P(arg), 0, P(ws), ws_bytes, s)
+                             P(loss), P(z_loss), P(acc), P(arg), 0, P(stats), P(ws), ws_bytes, s)
         if st:
             raise _lib.CEError(st, "ce_forward")
 
     def bwd(buf):
-        st = _lib.ce_backward(P(buf), dt, rows, V, buf.stride(0), P(go), 0, s)
+        if a.mode == "fused":
+            st = _lib.ce_backward(P(buf), dt, rows, V, buf.stride(0), P(go), 0, s)
+        elif a.mode == "recompute":
+            st = _lib.ce_backward_recompute(P(buf), dt, rows, V, buf.stride(0), tgt, wt, -100,
+                                            w.label_smoothing, w.lse_square_scale, w.softcap,
+                                            red_code, P(stats), P(go), 0, P(gbuf),
+                                            gbuf.stride(0), P(ws), ws_bytes, s)
+        else:
+            st = 0
         if st:
-            raise _lib.CEError(st, "ce_backward")
+            raise _lib.CEError(st, "backward")
 
+    # The timed kernel: the fused forward, or the recomputing backward.
+    timed_first = a.mode != "recompute"
     for i in range(a.warmup):
-        step(bufs[i])
+        fwd(bufs[i])
         bwd(bufs[i])
     torch.cuda.synchronize()
 
@@ -234,10 +336,16 @@ def main(argv=None) -> int:
     start.record(stream)
     for i in range(a.steps):
         b = bufs[a.warmup + i]
-        ev[i][0].record(stream)
-        step(b)
-        ev[i][1].record(stream)
-        bwd(b)
+        if timed_first:
+            ev[i][0].record(stream)
+            fwd(b)
+            ev[i][1].record(stream)
+            bwd(b)
+        else:
+            fwd(b)
+            ev[i][0].record(stream)
+            bwd(b)
+            ev[i][1].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
@@ -260,10 +368,10 @@ def main(argv=None) -> int:
     copy_gbps = 2 * src.numel() * src.element_size() * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
     del dst
 
-    alg = algorithmic_bytes(w, red, n_counted)
+    alg = algorithmic_bytes(w, red, n_counted, a.mode)
     achieved = alg / (kernel_ms * 1e-3) / 1e9
     kernel_key = "ce_fused" if path == "fused" else f"ce_{path}"
-    traffic = traffic_from_profiles(w.name, kernel_key)
+    traffic = traffic_from_profiles(w.name, kernel_key) if a.mode == "fused" else None
     out = {
         "metric": "fused CE fwd+grad rows/s and achieved HBM GB/s (% of peak), V=128256",
         "value": rows * a.steps / (total_ms * 1e-3),
@@ -277,7 +385,8 @@ def main(argv=None) -> int:
         "vs_baseline": None,
         "dtype": "f32" if w.dtype == torch.float32 else "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "rows": rows, "V": V, "reduction": red, "path": path,
+        "config": {"workload": w.name, "mode": a.mode, "rows": rows, "V": V,
+                   "reduction": red, "path": path,
                    "label_smoothing": w.label_smoothing, "softcap": w.softcap,
                    "lse_square_scale": w.lse_square_scale, "class_weights": w.weights,
                    "parallelism": "single GPU"},
@@ -286,7 +395,7 @@ def main(argv=None) -> int:
                      "kernel_ms": kernel_ms, "algorithmic_bytes": alg},
         "copy_ceiling_GBps": copy_gbps,
     }
-    if sample_host is not None:
+    if sample_host is not None and a.mode == "fused":
         wh = None if inp.weight is None else inp.weight.cpu().numpy()
         out["cpu_baseline"] = cpu_baseline(sample_host[0], sample_host[1], wh, w, red,
                                            a.cpu_budget)

@@ -111,6 +111,9 @@ int ce_plan_path(const void* logits, int dtype, int64_t rows, int64_t V, int64_t
  *  token_accuracy [device] fp32, same shape as loss, or NULL.
  *  argmax     [device] int64 (rows), or NULL.
  *  counts     [device] int64 [n_counted, n_correct], or NULL.
+ *  row_stats  [device] fp32 (rows, 2): per row the shift m = max z and
+ *             log2 sum_k exp(z_k - m), kept for ce_backward_recompute; rows
+ *             that are not counted get (0, 0). NULL = not written.
  *  workspace  [device] >= ce_workspace_bytes(...) bytes, 256-byte aligned,
  *             zero-filled before its first use (one hipMemset). Every call
  *             leaves it reusable: later calls on the same stream may pass it
@@ -121,14 +124,41 @@ ce_status ce_forward(void* logits, int dtype, int64_t rows, int64_t V, int64_t r
                      const int64_t* target, const float* weight, int64_t ignore_index,
                      float label_smoothing, float lse_square_scale, float softcap,
                      int reduction, uint32_t flags, float* loss, float* z_loss,
-                     float* token_accuracy, int64_t* argmax, int64_t* counts, void* workspace,
-                     size_t workspace_bytes, void* stream);
+                     float* token_accuracy, int64_t* argmax, int64_t* counts, float* row_stats,
+                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Backward: grad (rows, row_stride) [device] *= grad_output in place.
  *  grad_output [device] fp32: one value, or rows values when per_row != 0
  *  (reduction none). Rows whose scale is exactly 1.0 are left untouched. */
 ce_status ce_backward(void* grad, int dtype, int64_t rows, int64_t V, int64_t row_stride,
                       const float* grad_output, int per_row, void* stream);
+
+/* Backward from kept logits: the gradient is recomputed instead of stored
+ * by the forward. The tt-mlir PR #9324 page's cross_entropy_bw composite
+ * (before/after table) takes the saved logits and target; here a forward
+ * without CE_F_GRAD leaves the logits intact and fills row_stats, and this
+ * call writes grad = grad_output * d loss / d logits (the same formula and
+ * options as the fused forward's gradient) for every row, +0.0 for rows
+ * that are not counted.
+ *  logits, dtype, rows, V, row_stride, target, weight, ignore_index,
+ *  label_smoothing, lse_square_scale, softcap, reduction
+ *             as for the ce_forward call that produced row_stats.
+ *  row_stats  [device] fp32 (rows, 2) from that ce_forward call.
+ *  grad_output [device] fp32: one value, or rows values when per_row != 0.
+ *  grad       [device] (rows, grad_stride), the logits' dtype; may be the
+ *             logits themselves (in place, then grad_stride == row_stride),
+ *             otherwise must not overlap them.
+ *  workspace  [device] >= 256 bytes, 256-byte aligned; its first 256 bytes
+ *             are overwritten (any ce_forward workspace will do).
+ * Errors as ce_forward; CE_E_SHAPE also when grad_stride < V or when grad
+ * is the logits with another stride. */
+ce_status ce_backward_recompute(const void* logits, int dtype, int64_t rows, int64_t V,
+                                int64_t row_stride, const int64_t* target, const float* weight,
+                                int64_t ignore_index, float label_smoothing,
+                                float lse_square_scale, float softcap, int reduction,
+                                const float* row_stats, const float* grad_output, int per_row,
+                                void* grad, int64_t grad_stride, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /* Static, human-readable text of a ce_status value. */
 const char* ce_status_string(int status);

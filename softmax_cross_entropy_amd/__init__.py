@@ -7,7 +7,7 @@ is missing -- there is no CPU or PyTorch fallback.
 """
 
 from .functional import (CEOutput, CrossEntropyFunction, CrossEntropyLoss, backward_,
-                         cross_entropy, forward_raw)
+                         backward_recompute, cross_entropy, forward_raw)
 
-__all__ = ["CEOutput", "CrossEntropyFunction", "CrossEntropyLoss", "backward_", "cross_entropy",
-           "forward_raw"]
+__all__ = ["CEOutput", "CrossEntropyFunction", "CrossEntropyLoss", "backward_",
+           "backward_recompute", "cross_entropy", "forward_raw"]

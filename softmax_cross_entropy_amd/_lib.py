@@ -56,8 +56,13 @@ _SIGNATURES = {
                                     ctypes.c_uint32]),
     "ce_forward": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I64, _P, _P, _I64,
                                   ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_int,
-                                  ctypes.c_uint32, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+                                  ctypes.c_uint32, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                                  _P]),
     "ce_backward": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I64, _P, ctypes.c_int, _P]),
+    "ce_backward_recompute": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I64, _P, _P, _I64,
+                                             ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                             ctypes.c_int, _P, _P, ctypes.c_int, _P, _I64, _P,
+                                             ctypes.c_size_t, _P]),
     "ce_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 SYMBOLS = tuple(_SIGNATURES)
@@ -111,13 +116,27 @@ def ce_plan_path(logits: int, dtype: int, rows: int, V: int, row_stride: int, we
 def ce_forward(logits: int, dtype: int, rows: int, V: int, row_stride: int, target: int,
                weight: int, ignore_index: int, label_smoothing: float, lse_square_scale: float,
                softcap: float, reduction: int, flags: int, loss: int, z_loss: int,
-               token_accuracy: int, argmax: int, counts: int, workspace: int,
+               token_accuracy: int, argmax: int, counts: int, row_stats: int, workspace: int,
                workspace_bytes: int, stream: int) -> int:
     """Raw call; returns the ce_status (0 = CE_OK)."""
     return int(lib().ce_forward(logits, dtype, rows, V, row_stride, target, weight,
                                 ignore_index, label_smoothing, lse_square_scale, softcap,
                                 reduction, flags, loss, z_loss, token_accuracy, argmax, counts,
-                                workspace, workspace_bytes, stream))
+                                row_stats, workspace, workspace_bytes, stream))
+
+
+def ce_backward_recompute(logits: int, dtype: int, rows: int, V: int, row_stride: int,
+                          target: int, weight: int, ignore_index: int, label_smoothing: float,
+                          lse_square_scale: float, softcap: float, reduction: int,
+                          row_stats: int, grad_output: int, per_row: int, grad: int,
+                          grad_stride: int, workspace: int, workspace_bytes: int,
+                          stream: int) -> int:
+    """Raw call; returns the ce_status (0 = CE_OK)."""
+    return int(lib().ce_backward_recompute(logits, dtype, rows, V, row_stride, target, weight,
+                                           ignore_index, label_smoothing, lse_square_scale,
+                                           softcap, reduction, row_stats, grad_output, per_row,
+                                           grad, grad_stride, workspace, workspace_bytes,
+                                           stream))
 
 
 def ce_backward(grad: int, dtype: int, rows: int, V: int, row_stride: int, grad_output: int,

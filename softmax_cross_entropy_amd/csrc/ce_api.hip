@@ -148,12 +148,12 @@ CE_API int ce_plan_path(const void* logits, int dtype, int64_t rows, int64_t V,
   return pl.path;
 }
 
-CE_API ce_status ce_forward(void* logits, int dtype, int64_t rows, int64_t V, int64_t row_stride,
-                            const int64_t* target, const float* weight, int64_t ignore_index,
-                            float label_smoothing, float lse_square_scale, float softcap,
-                            int reduction, uint32_t flags, float* loss, float* z_loss,
-                            float* token_accuracy, int64_t* argmax, int64_t* counts,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+// Checks shared by the forward and the recomputed backward.
+ce_status check_options(int dtype, int64_t rows, int64_t V, int64_t row_stride,
+                        float label_smoothing, float lse_square_scale, float softcap,
+                        int reduction) {
   if (dtype != CE_F32 && dtype != CE_BF16) return CE_E_DTYPE;
   if (!valid_shape(rows, V, row_stride)) return CE_E_SHAPE;
   if (reduction != CE_RED_NONE && reduction != CE_RED_MEAN && reduction != CE_RED_SUM)
@@ -161,19 +161,13 @@ CE_API ce_status ce_forward(void* logits, int dtype, int64_t rows, int64_t V, in
   if (!(label_smoothing >= 0.0f && label_smoothing <= 1.0f)) return CE_E_PARAM;
   if (!(softcap >= 0.0f) || !isfinite(softcap)) return CE_E_PARAM;
   if (!(lse_square_scale >= 0.0f) || !isfinite(lse_square_scale)) return CE_E_PARAM;
-  if (loss == nullptr) return CE_E_NULL;
-  if (rows > 0 && (logits == nullptr || target == nullptr)) return CE_E_NULL;
+  return CE_OK;
+}
 
-  Plan pl;
-  make_plan(logits, dtype, rows, V, row_stride, weight, label_smoothing, flags, &pl);
-  if (pl.path == CE_PATH_SPLITV && rows * pl.S > kMaxInt) return CE_E_SHAPE;
-  const Layout L = layout(rows, pl.path == CE_PATH_SPLITV ? pl.S : 0);
-  if (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
-    return CE_E_WORKSPACE;
-  if (workspace_bytes < L.total) return CE_E_WORKSPACE;
-
-  char* ws = static_cast<char*>(workspace);
-  cedev::Params p;
+// The launch parameters of the per-row options (both directions).
+void fill_options(cedev::Params& p, void* logits, int64_t rows, int64_t V, int64_t row_stride,
+                  const int64_t* target, const float* weight, int64_t ignore_index,
+                  float label_smoothing, float lse_square_scale, float softcap, int reduction) {
   memset(&p, 0, sizeof(p));
   p.logits = logits;
   p.rows = rows;
@@ -190,6 +184,35 @@ CE_API ce_status ce_forward(void* logits, int dtype, int64_t rows, int64_t V, in
   p.softcap = softcap;
   p.inv_softcap = softcap > 0.0f ? 1.0f / softcap : 0.0f;
   p.reduction = reduction;
+}
+
+}  // namespace
+
+CE_API ce_status ce_forward(void* logits, int dtype, int64_t rows, int64_t V, int64_t row_stride,
+                            const int64_t* target, const float* weight, int64_t ignore_index,
+                            float label_smoothing, float lse_square_scale, float softcap,
+                            int reduction, uint32_t flags, float* loss, float* z_loss,
+                            float* token_accuracy, int64_t* argmax, int64_t* counts,
+                            float* row_stats, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  const ce_status bad = check_options(dtype, rows, V, row_stride, label_smoothing,
+                                      lse_square_scale, softcap, reduction);
+  if (bad != CE_OK) return bad;
+  if (loss == nullptr) return CE_E_NULL;
+  if (rows > 0 && (logits == nullptr || target == nullptr)) return CE_E_NULL;
+
+  Plan pl;
+  make_plan(logits, dtype, rows, V, row_stride, weight, label_smoothing, flags, &pl);
+  if (pl.path == CE_PATH_SPLITV && rows * pl.S > kMaxInt) return CE_E_SHAPE;
+  const Layout L = layout(rows, pl.path == CE_PATH_SPLITV ? pl.S : 0);
+  if (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
+    return CE_E_WORKSPACE;
+  if (workspace_bytes < L.total) return CE_E_WORKSPACE;
+
+  char* ws = static_cast<char*>(workspace);
+  cedev::Params p;
+  fill_options(p, logits, rows, V, row_stride, target, weight, ignore_index, label_smoothing,
+               lse_square_scale, softcap, reduction);
   p.grad = (flags & CE_F_GRAD) ? 1 : 0;
   p.epilogue = (reduction != CE_RED_NONE || counts != nullptr) ? 1 : 0;
   // The prologue is needed before any gradient is written only for the mean
@@ -204,6 +227,7 @@ CE_API ce_status ce_forward(void* logits, int dtype, int64_t rows, int64_t V, in
   p.acc = token_accuracy;
   p.argmax = argmax;
   p.counts = counts;
+  p.row_stats = row_stats;
   p.hdr = reinterpret_cast<cedev::Header*>(ws);
   p.row_ce = reinterpret_cast<float*>(ws + L.row_ce);
   p.row_z = reinterpret_cast<float*>(ws + L.row_z);
@@ -247,6 +271,54 @@ CE_API ce_status ce_backward(void* grad, int dtype, int64_t rows, int64_t V, int
       dtype == CE_BF16
           ? cehost::launch_backward_bf16(grad, rows, V, row_stride, grad_output, per_row, vec, st)
           : cehost::launch_backward_f32(grad, rows, V, row_stride, grad_output, per_row, vec, st);
+  return e == hipSuccess ? CE_OK : CE_E_HIP;
+}
+
+CE_API ce_status ce_backward_recompute(const void* logits, int dtype, int64_t rows, int64_t V,
+                                       int64_t row_stride, const int64_t* target,
+                                       const float* weight, int64_t ignore_index,
+                                       float label_smoothing, float lse_square_scale,
+                                       float softcap, int reduction, const float* row_stats,
+                                       const float* grad_output, int per_row, void* grad,
+                                       int64_t grad_stride, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  const ce_status bad = check_options(dtype, rows, V, row_stride, label_smoothing,
+                                      lse_square_scale, softcap, reduction);
+  if (bad != CE_OK) return bad;
+  if (!valid_shape(rows, V, grad_stride)) return CE_E_SHAPE;
+  if (grad_output == nullptr) return CE_E_NULL;
+  if (rows > 0 && (logits == nullptr || target == nullptr || row_stats == nullptr ||
+                   grad == nullptr))
+    return CE_E_NULL;
+  if (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % kAlign != 0 ||
+      workspace_bytes < kAlign)
+    return CE_E_WORKSPACE;
+  if (grad == logits && grad_stride != row_stride) return CE_E_SHAPE;
+  if (rows == 0) return CE_OK;
+  const int eb = elem_bytes(dtype);
+  const bool vec = reinterpret_cast<uintptr_t>(logits) % 16 == 0 &&
+                   reinterpret_cast<uintptr_t>(grad) % 16 == 0 && (row_stride * eb) % 16 == 0 &&
+                   (grad_stride * eb) % 16 == 0 &&
+                   !(weight && label_smoothing > 0.0f && reinterpret_cast<uintptr_t>(weight) % 16);
+  const int64_t span = static_cast<int64_t>(cedev::kBwdBlock) * cedev::kBwdUnroll;
+  const int64_t units = vec ? V / elems_per_vec(dtype) : V;
+  const int64_t bpr = units / span + 1;
+  if (rows * bpr > kMaxInt) return CE_E_SHAPE;
+
+  cedev::Params p;
+  fill_options(p, const_cast<void*>(logits), rows, V, row_stride, target, weight, ignore_index,
+               label_smoothing, lse_square_scale, softcap, reduction);
+  p.row_stats = const_cast<float*>(row_stats);
+  p.hdr = reinterpret_cast<cedev::Header*>(workspace);
+  // The same scales as the forward: the mean's 1/D and 1/n, and W for
+  // weighted smoothing, from the prologue.
+  p.has_hdr = (reduction == CE_RED_MEAN || (weight != nullptr && label_smoothing > 0.0f)) ? 1 : 0;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (p.has_hdr && cehost::launch_prologue(p, st) != hipSuccess) return CE_E_HIP;
+  const hipError_t e =
+      dtype == CE_BF16
+          ? cehost::launch_recompute_bf16(p, grad, grad_stride, grad_output, per_row, vec, st)
+          : cehost::launch_recompute_f32(p, grad, grad_stride, grad_output, per_row, vec, st);
   return e == hipSuccess ? CE_OK : CE_E_HIP;
 }
 

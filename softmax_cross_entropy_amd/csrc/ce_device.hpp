@@ -218,6 +218,7 @@ struct Params {
   float* row_ce;                       // (rows) cross-entropy term per row
   float* row_z;                        // (rows) z-loss term per row
   int32_t* row_ok;                     // (rows) bit 0: argmax == target, bit 1: counted
+  float* row_stats;                    // (rows, 2) shift m and log2 s per row, or null
   Partial* part;                       // (rows, S) split-V partials
   int S;                               // chunks per row (split-V)
   int chunk_vec;                       // vectors per chunk (split-V)
@@ -295,23 +296,35 @@ struct RowScalars {
 // (Liger-Kernel CE profile, Key Patterns: cross entropy, label smoothing and
 // z-loss each contribute to loss and gradient; PyTorch's convention for how
 // smoothing mass and class weights combine.)
-__device__ __forceinline__ void row_scalars(RowScalars& r, float m, float s, float sz, float zy,
-                                            float wy, double W, const Params& p, double alpha,
-                                            double beta) {
-  const float l2s = lg2(s);
+// The gradient coefficients A, B, C of a row from its shift m and the log2 of
+// its shifted sum; returns lse. Shared by the forward (row_scalars) and the
+// gradient recomputed from kept logits, so both use identical coefficients.
+__device__ __forceinline__ double grad_scalars(RowScalars& r, float m, float l2s, float wy,
+                                               double W, const Params& p, double alpha,
+                                               double beta) {
   const double lns = static_cast<double>(l2s) * static_cast<double>(kLn2);
   const double lse = static_cast<double>(m) + lns;
   const double wyd = wy;
   const double ome = p.one_minus_eps, epv = p.eps_over_v, lam = p.lam_d;
-  const double ce = wyd * ome * ((static_cast<double>(m) - zy) + lns) +
-                    epv * (W * lse - static_cast<double>(sz));
   r.m = m;
   r.l2s = l2s;
-  r.ce = static_cast<float>(ce);
-  r.zl = static_cast<float>(lam * lse * lse);
   r.A = static_cast<float>(alpha * (wyd * ome + epv * W) + beta * 2.0 * lam * lse);
   r.B = static_cast<float>(alpha * epv);
   r.C = static_cast<float>(alpha * wyd * ome);
+  return lse;
+}
+
+__device__ __forceinline__ void row_scalars(RowScalars& r, float m, float s, float sz, float zy,
+                                            float wy, double W, const Params& p, double alpha,
+                                            double beta) {
+  const float l2s = lg2(s);
+  const double lse = grad_scalars(r, m, l2s, wy, W, p, alpha, beta);
+  const double lns = static_cast<double>(l2s) * static_cast<double>(kLn2);
+  const double wyd = wy;
+  const double ce = wyd * p.one_minus_eps * ((static_cast<double>(m) - zy) + lns) +
+                    p.eps_over_v * (W * lse - static_cast<double>(sz));
+  r.ce = static_cast<float>(ce);
+  r.zl = static_cast<float>(p.lam_d * lse * lse);
 }
 
 // ---------------------------------------------------------------------------
@@ -333,21 +346,31 @@ __device__ __forceinline__ void row_scalars(RowScalars& r, float m, float s, flo
 // gradient stores) and the other waves go on with the gradient meanwhile.
 // ---------------------------------------------------------------------------
 
+// The row's values for the epilogue (device-scope atomic stores, no wait).
+__device__ __forceinline__ void publish_row(const Params& p, int64_t row, float ce, float zl,
+                                            int ok, int counted) {
+  __hip_atomic_store(p.row_ce + row, ce, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(p.row_z + row, zl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(p.row_ok + row, (ok ? 1 : 0) | (counted ? 2 : 0), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The calling thread's stores are complete, then it bumps the arrival
+// counter. Returns true in the block that arrives last of total_blocks.
+__device__ __forceinline__ bool arrive(const Params& p, uint32_t total_blocks) {
+  __builtin_amdgcn_s_waitcnt(0);
+  const uint32_t prev =
+      __hip_atomic_fetch_add(&p.hdr->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return prev == total_blocks - 1u;
+}
+
 // One thread per block. has_row: the block owns the row's values (a split-V
 // row is owned by its chunk 0). Returns true in the block that arrives last.
 __device__ __forceinline__ bool epilogue_publish(const Params& p, int64_t row, bool has_row,
                                                  float ce, float zl, int ok, int counted,
                                                  uint32_t total_blocks) {
-  if (has_row) {
-    __hip_atomic_store(p.row_ce + row, ce, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(p.row_z + row, zl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(p.row_ok + row, (ok ? 1 : 0) | (counted ? 2 : 0), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  const uint32_t prev =
-      __hip_atomic_fetch_add(&p.hdr->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return prev == total_blocks - 1u;
+  if (has_row) publish_row(p, row, ce, zl, ok, counted);
+  return arrive(p, total_blocks);
 }
 
 // Whole block, in the block that arrived last only.
@@ -358,12 +381,31 @@ __device__ __forceinline__ void epilogue_reduce(const Params& p) {
   const int tid = threadIdx.x;
   double ce = 0.0, zl = 0.0;
   int64_t ok = 0, cnt = 0;
-  for (int64_t r = tid; r < p.rows; r += BLOCK) {
-    ce += static_cast<double>(__hip_atomic_load(p.row_ce + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    zl += static_cast<double>(__hip_atomic_load(p.row_z + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    const int32_t f = __hip_atomic_load(p.row_ok + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    ok += f & 1;
-    cnt += (f >> 1) & 1;
+  // kEpiUnroll rows per thread in flight (the loads are device-coherent, so
+  // each has the full memory latency); the sums still run in row order.
+  constexpr int kEpiUnroll = 8;
+  for (int64_t r0 = tid; r0 < p.rows; r0 += static_cast<int64_t>(BLOCK) * kEpiUnroll) {
+    float vce[kEpiUnroll], vz[kEpiUnroll];
+    int32_t vf[kEpiUnroll];
+#pragma unroll
+    for (int u = 0; u < kEpiUnroll; ++u) {
+      const int64_t r = r0 + static_cast<int64_t>(u) * BLOCK;
+      const bool in = r < p.rows;
+      vce[u] = in ? __hip_atomic_load(p.row_ce + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                  : 0.0f;
+      vz[u] = in ? __hip_atomic_load(p.row_z + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                 : 0.0f;
+      vf[u] = in ? __hip_atomic_load(p.row_ok + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kEpiUnroll; ++u) {
+      if (r0 + static_cast<int64_t>(u) * BLOCK < p.rows) {
+        ce += static_cast<double>(vce[u]);
+        zl += static_cast<double>(vz[u]);
+        ok += vf[u] & 1;
+        cnt += (vf[u] >> 1) & 1;
+      }
+    }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
@@ -409,6 +451,14 @@ __device__ __forceinline__ void epilogue_reduce(const Params& p) {
 
 // Per-row outputs of one row (thread 0 of the row's block); the reduced
 // outputs go through epilogue_publish.
+// The row's (m, log2 s), kept for a later gradient recomputed from the logits.
+__device__ __forceinline__ void write_row_stats(const Params& p, int64_t row, float m, float l2s) {
+  if (p.row_stats) {
+    p.row_stats[2 * row] = m;
+    p.row_stats[2 * row + 1] = l2s;
+  }
+}
+
 __device__ __forceinline__ void write_row_outputs(const Params& p, int64_t row, float ce, float zl,
                                                   int ok, int64_t arg) {
   if (p.reduction == 0) {

@@ -305,10 +305,9 @@ __device__ __forceinline__ u4 grad_vec_e(const Params& p, const RowScalars& rs, 
 }
 
 // Outputs of a row that is ignored (gradient exactly +0.0, never read) or
-// whose target is out of range (NaN loss). Returns, in thread 0, whether
-// this row's publication was the last of the launch.
+// whose target is out of range (NaN loss).
 template <class E, int BLOCK>
-__device__ __forceinline__ bool skipped_row(const Params& p, int64_t row, bool bad, char* rp,
+__device__ __forceinline__ void skipped_row(const Params& p, int64_t row, bool bad, char* rp,
                                             int nv, int tail) {
   const int tid = threadIdx.x;
   if (p.grad) {
@@ -316,13 +315,12 @@ __device__ __forceinline__ bool skipped_row(const Params& p, int64_t row, bool b
     for (int j = tid; j < nv; j += BLOCK) __builtin_nontemporal_store(u4{0u, 0u, 0u, 0u}, vp + j);
     if (tid < tail) E::st(rp, static_cast<int64_t>(nv) * E::EPV + tid, 0.0f);
   }
-  bool last = false;
   if (tid == 0) {
     const float q = bad ? __builtin_nanf("") : 0.0f;
     write_row_outputs(p, row, q, q, 0, -1);
-    if (p.epilogue) last = epilogue_publish(p, row, true, q, q, 0, 0, static_cast<uint32_t>(p.rows));
+    write_row_stats(p, row, 0.0f, 0.0f);
+    if (p.epilogue) publish_row(p, row, q, q, 0, 0);
   }
-  return last;
 }
 
 // Block-shared state of one row in flight.
@@ -371,8 +369,8 @@ struct RowClaim {
   }
 };
 
-template <class E, int BLOCK, int NREG, int NLDS, int SC, int SM>
-__device__ __forceinline__ bool fused_row(const Params& p, int64_t row, int64_t y,
+template <class E, int BLOCK, int NREG, int NLDS, int SC, int SM, bool DYN>
+__device__ __forceinline__ void fused_row(const Params& p, int64_t row, int64_t y,
                                           RowShared<BLOCK, NLDS>& sh) {
   constexpr int EPV = E::EPV;
   constexpr int NS = NREG + NLDS;
@@ -403,18 +401,21 @@ __device__ __forceinline__ bool fused_row(const Params& p, int64_t row, int64_t 
   if (ignored || bad) {
     // Ignored rows are never read; their gradient is exactly +0.0
     // (tt-mlir PR #9324 page: ignored rows, also with non-finite logits).
-    // Every wave has read the previous row's next_row before it is
-    // overwritten (this path has no other barrier before the write).
-    __syncthreads();
-    if (tid == 0) {
-      RowClaim cl;
-      cl.issue(p);
-      const int64_t nr = cl.row(p);
-      sh.next_row = nr;
-      sh.next_y = nr < p.rows ? p.target[nr] : 0;
+    if constexpr (DYN) {
+      // Every wave has read the previous row's next_row before it is
+      // overwritten (this path has no other barrier before the write).
+      __syncthreads();
+      if (tid == 0) {
+        RowClaim cl;
+        cl.issue(p);
+        const int64_t nr = cl.row(p);
+        sh.next_row = nr;
+        sh.next_y = nr < p.rows ? p.target[nr] : 0;
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    return skipped_row<E, BLOCK>(p, row, bad, rp, nv, tail);
+    skipped_row<E, BLOCK>(p, row, bad, rp, nv, tail);
+    return;
   }
   RowClaim claim;
 
@@ -540,7 +541,7 @@ __device__ __forceinline__ bool fused_row(const Params& p, int64_t row, int64_t 
   // would hold rows back from workgroups that finish first); thread 0 reads
   // the claim back while it computes the row scalars.
   int64_t next_row = 0, next_y = 0;
-  if (tid == 0) claim.issue(p);
+  if (DYN && tid == 0) claim.issue(p);
 
   Acc a;
   a.m = tm;
@@ -596,8 +597,10 @@ __device__ __forceinline__ bool fused_row(const Params& p, int64_t row, int64_t 
   __syncthreads();
 
   if (tid == 0) {
-    next_row = claim.row(p);
-    if (next_row < p.rows) next_y = p.target[next_row];
+    if constexpr (DYN) {
+      next_row = claim.row(p);
+      if (next_row < p.rows) next_y = p.target[next_row];
+    }
     int arg = s_cand[0];
 #pragma unroll
     for (int w = 1; w < NW; ++w) arg = min(arg, s_cand[w]);
@@ -611,15 +614,17 @@ __device__ __forceinline__ bool fused_row(const Params& p, int64_t row, int64_t 
     rs.ok = (arg == y);
     sh.rs = rs;
     sh.xy = xy;
-    sh.next_row = next_row;
-    sh.next_y = next_y;
+    if constexpr (DYN) {
+      sh.next_row = next_row;
+      sh.next_y = next_y;
+    }
     write_row_outputs(p, row, rs.ce, rs.zl, rs.ok, arg);
+    write_row_stats(p, row, rs.m, rs.l2s);
   }
   __syncthreads();
-  bool last = false;
   if (tid == 0 && p.epilogue) {
     const RowScalars& rs = sh.rs;
-    last = epilogue_publish(p, row, true, rs.ce, rs.zl, rs.ok, 1, static_cast<uint32_t>(p.rows));
+    publish_row(p, row, rs.ce, rs.zl, rs.ok, 1);
   }
 
   // ---- pass 2: gradient from on-chip data, written over the logits ----
@@ -661,7 +666,6 @@ __device__ __forceinline__ bool fused_row(const Params& p, int64_t row, int64_t 
       E::template st_buf<kStoreNT>(rsrc, static_cast<int>(y), grad_one<SC, SM>(p, rs, sh.xy, wy, true));
     }
   }
-  return last;
 }
 
 __device__ __forceinline__ int64_t uniform_i64(int64_t v) {
@@ -670,25 +674,48 @@ __device__ __forceinline__ int64_t uniform_i64(int64_t v) {
   return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
 }
 
-// Persistent variant: gridDim.x resident workgroups take rows in the order
-// they finish (RowClaim), so the loads of a workgroup's next row are issued
-// as soon as the gradient stores of its current one are (they drain while
-// the next row arrives) instead of after a workgroup teardown and launch.
+// Persistent variant: gridDim.x resident workgroups. For long rows (DYN)
+// workgroups take rows in the order they finish (RowClaim); for short rows
+// workgroup b takes rows b, b + gridDim.x, ... (a claim's latency would be
+// a large share of a short row), with the targets staged in LDS. Either way
+// the loads of a workgroup's next row are issued as soon as the gradient
+// stores of its current one are (they drain while the next row arrives).
+// Each row's values for the epilogue are stored as the row completes; the
+// workgroup arrives once, at its end.
+constexpr int kRowsStaged = 256;
 template <class E, int BLOCK, int NREG, int NLDS, int SC, int SM>
 __global__ __launch_bounds__(BLOCK) void rows_kernel(Params p) {
+  constexpr bool DYN = NLDS > 0 || NREG >= 32;
   __shared__ RowShared<BLOCK, NLDS> sh;
+  __shared__ int64_t s_y[DYN ? 1 : kRowsStaged];
   __shared__ int s_last;
-  bool last = false;
-  int64_t row = blockIdx.x;
-  int64_t y = p.target[row];
-  while (true) {
-    last |= fused_row<E, BLOCK, NREG, NLDS, SC, SM>(p, row, y, sh);
-    row = uniform_i64(sh.next_row);
-    y = uniform_i64(sh.next_y);
-    if (row >= p.rows) break;
+  const int64_t G = gridDim.x;
+  if constexpr (DYN) {
+    int64_t row = blockIdx.x;
+    int64_t y = p.target[row];
+    while (true) {
+      fused_row<E, BLOCK, NREG, NLDS, SC, SM, true>(p, row, y, sh);
+      row = uniform_i64(sh.next_row);
+      y = uniform_i64(sh.next_y);
+      if (row >= p.rows) break;
+    }
+  } else {
+    int64_t i = 0;
+    for (int64_t row = blockIdx.x; row < p.rows; row += G, ++i) {
+      const int q = static_cast<int>(i % kRowsStaged);
+      if (q == 0) {
+        __syncthreads();  // every thread is done with the previous batch
+        for (int t = threadIdx.x; t < kRowsStaged; t += BLOCK) {
+          const int64_t r = row + static_cast<int64_t>(t) * G;
+          if (r < p.rows) s_y[t] = p.target[r];
+        }
+        __syncthreads();
+      }
+      fused_row<E, BLOCK, NREG, NLDS, SC, SM, false>(p, row, uniform_i64(s_y[q]), sh);
+    }
   }
   if (p.epilogue) {
-    if (threadIdx.x == 0) s_last = last;
+    if (threadIdx.x == 0) s_last = arrive(p, static_cast<uint32_t>(G));
     __syncthreads();
     if (s_last) epilogue_reduce<BLOCK>(p);
   }
@@ -826,7 +853,10 @@ __global__ __launch_bounds__(BLOCK) void splitv_finish_kernel(Params p) {
     __shared__ int s_last0;
     if (tid == 0) {
       const float q = bad ? __builtin_nanf("") : 0.0f;
-      if (c == 0) write_row_outputs(p, row, q, q, 0, -1);
+      if (c == 0) {
+        write_row_outputs(p, row, q, q, 0, -1);
+        write_row_stats(p, row, 0.0f, 0.0f);
+      }
       if (p.epilogue) s_last0 = epilogue_publish(p, row, c == 0, q, q, 0, 0, gridDim.x);
     }
     if (p.epilogue) {
@@ -855,7 +885,10 @@ __global__ __launch_bounds__(BLOCK) void splitv_finish_kernel(Params p) {
     rs.ok = (bi == y);
     s_rs = rs;
     s_xy = xy;
-    if (c == 0) write_row_outputs(p, row, rs.ce, rs.zl, rs.ok, bi);
+    if (c == 0) {
+      write_row_outputs(p, row, rs.ce, rs.zl, rs.ok, bi);
+      write_row_stats(p, row, rs.m, rs.l2s);
+    }
   }
   __syncthreads();
   __shared__ int s_last;
@@ -926,6 +959,7 @@ __global__ __launch_bounds__(BLOCK) void row_scalar_kernel(Params p) {
     if (tid == 0) {
       const float q = bad ? __builtin_nanf("") : 0.0f;
       write_row_outputs(p, row, q, q, 0, -1);
+      write_row_stats(p, row, 0.0f, 0.0f);
       if (p.epilogue) s_last0 = epilogue_publish(p, row, true, q, q, 0, 0, gridDim.x);
     }
     if (p.epilogue) {
@@ -951,6 +985,7 @@ __global__ __launch_bounds__(BLOCK) void row_scalar_kernel(Params p) {
     rs.ok = (t.bi == y);
     s_rs = rs;
     write_row_outputs(p, row, rs.ce, rs.zl, rs.ok, t.bi);
+    write_row_stats(p, row, rs.m, rs.l2s);
   }
   __syncthreads();
   __shared__ int s_last;
@@ -1053,6 +1088,114 @@ __global__ __launch_bounds__(kPrologueBlock) void prologue_kernel(Params p) {
         p.counts[0] = 0;
         p.counts[1] = 0;
       }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Gradient recomputed from kept logits (the backward of a forward that did
+// not overwrite them; PR #9324 page, the cross_entropy_bw composite takes
+// the saved logits and target): grad = grad_output * d loss / d logits, from
+// the logits, the target and the row's (m, log2 s) that the forward saved.
+// Grid: rows x blocks_per_row, each block kBwdBlock x kBwdUnroll vectors (or
+// elements) of its row. grad may be the logits themselves (same stride).
+// ---------------------------------------------------------------------------
+template <class E, int SC, int SM, bool VEC>
+__global__ __launch_bounds__(kBwdBlock) void recompute_kernel(Params p, void* grad,
+                                                              int64_t grad_stride, const float* go,
+                                                              int per_row, int blocks_per_row) {
+  constexpr int EPV = E::EPV;
+  constexpr int U = kBwdUnroll;
+  __shared__ RowScalars s_rs;
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x / blocks_per_row;
+  const int b = blockIdx.x - static_cast<int>(row) * blocks_per_row;
+  const int64_t y = p.target[row];
+  const bool skip = (y == p.ignore_index) || y < 0 || y >= p.V;
+  const char* xp = row_ptr(p, row, E::BYTES);
+  char* gp = static_cast<char*>(grad) + row * grad_stride * E::BYTES;
+  const float scale = per_row ? go[row] : go[0];
+  if (!skip && tid == 0) {
+    double W, alpha, beta;
+    load_scales(p, W, alpha, beta);
+    const float wy = p.weight ? p.weight[y] : 1.0f;
+    RowScalars rs;
+    grad_scalars(rs, p.row_stats[2 * row], p.row_stats[2 * row + 1], wy, W, p, alpha, beta);
+    s_rs = rs;
+  }
+  __syncthreads();
+  const RowScalars rs = s_rs;
+  if constexpr (VEC) {
+    const int nvec = static_cast<int>(p.V / EPV);
+    const u4* xv = reinterpret_cast<const u4*>(xp);
+    u4* gv = reinterpret_cast<u4*>(gp);
+    const int j0 = b * kBwdBlock * U;
+    const int64_t tail0 = static_cast<int64_t>(nvec) * EPV;
+    // The owner of the target's vector reads the target logit before any
+    // store (grad may be the logits).
+    const int jy = static_cast<int>(y / EPV);
+    const bool owns_y = !skip && y < tail0 && jy >= j0 && jy < j0 + kBwdBlock * U &&
+                        (jy - j0) % kBwdBlock == tid;
+    const float xy = owns_y ? E::ld(xp, y) : 0.0f;
+    u4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + u * kBwdBlock + tid;
+      v[u] = (!skip && j < nvec) ? __builtin_nontemporal_load(xv + j) : u4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + u * kBwdBlock + tid;
+      if (j < nvec) {
+        u4 g = u4{0u, 0u, 0u, 0u};
+        if (!skip) {
+          float f[EPV], wk[EPV], t[EPV], out[EPV];
+          E::unpack(v[u], f);
+#pragma unroll
+          for (int i = 0; i < EPV; ++i) wk[i] = 1.0f;
+          if (SM && p.weight) load_w<E>(p.weight, j, wk);
+          if constexpr (SC) {
+            float uu[EPV];
+#pragma unroll
+            for (int i = 0; i < EPV; ++i) uu[i] = f[i] * p.inv_softcap;
+            tanh_vec<EPV>(uu, t);
+          } else {
+#pragma unroll
+            for (int i = 0; i < EPV; ++i) t[i] = 0.0f;
+          }
+#pragma unroll
+          for (int i = 0; i < EPV; ++i)
+            out[i] = grad_elem<SC, SM>(p, rs, f[i], t[i], wk[i], false) * scale;
+          g = E::pack(out);
+        }
+        __builtin_nontemporal_store(g, gv + j);
+      }
+    }
+    if (b == blocks_per_row - 1 && tail0 + tid < p.V) {
+      const int64_t k = tail0 + tid;
+      float gk = 0.0f;
+      if (!skip) {
+        const float wk = (SM && p.weight) ? p.weight[k] : 1.0f;
+        gk = grad_one<SC, SM>(p, rs, E::ld(xp, k), wk, k == y) * scale;
+      }
+      E::st_nt(gp, k, gk);
+    }
+    // The one-hot term, rewritten by the thread that stored the target's
+    // vector (its own later store to the same address).
+    if (owns_y) {
+      const float wy = (SM && p.weight) ? p.weight[y] : 1.0f;
+      E::st_nt(gp, y, grad_one<SC, SM>(p, rs, xy, wy, true) * scale);
+    }
+  } else {
+    const int64_t span = static_cast<int64_t>(kBwdBlock) * U;
+    const int64_t k0 = static_cast<int64_t>(b) * span;
+    for (int64_t k = k0 + tid; k < p.V && k < k0 + span; k += kBwdBlock) {
+      float gk = 0.0f;
+      if (!skip) {
+        const float wk = (SM && p.weight) ? p.weight[k] : 1.0f;
+        gk = grad_one<SC, SM>(p, rs, E::ld(xp, k), wk, k == y) * scale;
+      }
+      E::st(gp, k, gk);
     }
   }
 }

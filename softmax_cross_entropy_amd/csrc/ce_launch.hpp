@@ -39,6 +39,10 @@ struct Plan {
 hipError_t launch_prologue(const cedev::Params& p, hipStream_t st);
 hipError_t launch_forward_f32(const Plan& plan, const cedev::Params& p, hipStream_t st);
 hipError_t launch_forward_bf16(const Plan& plan, const cedev::Params& p, hipStream_t st);
+hipError_t launch_recompute_f32(const cedev::Params& p, void* grad, int64_t grad_stride,
+                                const float* go, int per_row, bool vec, hipStream_t st);
+hipError_t launch_recompute_bf16(const cedev::Params& p, void* grad, int64_t grad_stride,
+                                 const float* go, int per_row, bool vec, hipStream_t st);
 hipError_t launch_backward_f32(void* grad, int64_t rows, int64_t V, int64_t stride,
                                const float* go, int per_row, bool vec, hipStream_t st);
 hipError_t launch_backward_bf16(void* grad, int64_t rows, int64_t V, int64_t stride,

@@ -87,6 +87,37 @@ hipError_t launch_forward(const Plan& plan, const Params& p, hipStream_t st) {
   return sm ? launch_path<E, 0, 1>(plan, p, st) : launch_path<E, 0, 0>(plan, p, st);
 }
 
+template <class E, int SC, int SM>
+hipError_t launch_recompute_t(const Params& p, void* grad, int64_t grad_stride, const float* go,
+                              int per_row, bool vec, hipStream_t st) {
+  const int64_t span = static_cast<int64_t>(cedev::kBwdBlock) * cedev::kBwdUnroll;
+  const int64_t units = vec ? (p.V / E::EPV) : p.V;
+  int64_t bpr = (units + span - 1) / span;
+  if (bpr < 1) bpr = 1;
+  const dim3 grid(static_cast<unsigned>(p.rows * bpr));
+  if (vec) {
+    cedev::recompute_kernel<E, SC, SM, true><<<grid, cedev::kBwdBlock, 0, st>>>(
+        p, grad, grad_stride, go, per_row, static_cast<int>(bpr));
+  } else {
+    cedev::recompute_kernel<E, SC, SM, false><<<grid, cedev::kBwdBlock, 0, st>>>(
+        p, grad, grad_stride, go, per_row, static_cast<int>(bpr));
+  }
+  return hipGetLastError();
+}
+
+template <class E>
+hipError_t launch_recompute(const Params& p, void* grad, int64_t grad_stride, const float* go,
+                            int per_row, bool vec, hipStream_t st) {
+  const bool sc = p.softcap > 0.0f;
+  const bool sm = p.eps > 0.0f;
+  if (sc) {
+    return sm ? launch_recompute_t<E, 1, 1>(p, grad, grad_stride, go, per_row, vec, st)
+              : launch_recompute_t<E, 1, 0>(p, grad, grad_stride, go, per_row, vec, st);
+  }
+  return sm ? launch_recompute_t<E, 0, 1>(p, grad, grad_stride, go, per_row, vec, st)
+            : launch_recompute_t<E, 0, 0>(p, grad, grad_stride, go, per_row, vec, st);
+}
+
 template <class E>
 hipError_t launch_backward(void* grad, int64_t rows, int64_t V, int64_t stride, const float* go,
                            int per_row, bool vec, hipStream_t st) {

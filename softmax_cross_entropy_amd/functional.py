@@ -10,7 +10,10 @@ Gradient-in-forward (the page's Key Patterns): when the logits require a
 gradient, the forward overwrites their storage with d loss / d logits and
 the backward rescales that buffer by grad_output in place. The logits tensor
 passed in must therefore not be used again after the call; pass
-``inplace=False`` to work on a private copy instead.
+``inplace=False`` to work on a private copy instead, or ``keep_logits=True``
+to leave the logits untouched and recompute the gradient in the backward from
+the logits and the per-row (max, log-sum) the forward keeps (the saved-logits
+backward of the tt-mlir PR #9324 page's cross_entropy_bw composite).
 """
 
 from __future__ import annotations
@@ -69,7 +72,8 @@ def _forward_raw(x2: torch.Tensor, t: torch.Tensor, weight: Optional[torch.Tenso
                  ignore_index: int, label_smoothing: float, lse_square_scale: float,
                  softcap: Optional[float], reduction: str, want_grad: bool,
                  want_z: bool, want_acc: bool, want_arg: bool, want_counts: bool = False,
-                 check_targets: bool = False, extra_flags: int = 0):
+                 check_targets: bool = False, extra_flags: int = 0,
+                 row_stats: Optional[torch.Tensor] = None):
     if not x2.is_cuda:
         raise ValueError("logits must be a CUDA (HIP) tensor")
     if reduction not in REDUCTION_CODES:
@@ -103,10 +107,37 @@ def _forward_raw(x2: torch.Tensor, t: torch.Tensor, weight: Optional[torch.Tenso
     status = _lib.ce_forward(ptr(x2), dt, rows, V, x2.stride(0) if rows > 0 else V, ptr(t),
                              ptr(w), int(ignore_index), float(label_smoothing),
                              float(lse_square_scale), float(softcap or 0.0), red, flags,
-                             ptr(loss), ptr(z_loss), ptr(acc), ptr(arg), ptr(counts), ptr(ws),
-                             ws_bytes, _stream(dev))
+                             ptr(loss), ptr(z_loss), ptr(acc), ptr(arg), ptr(counts),
+                             ptr(row_stats), ptr(ws), ws_bytes, _stream(dev))
     check(status, "ce_forward")
     return loss, z_loss, acc, arg, counts
+
+
+def backward_recompute(x2: torch.Tensor, t: torch.Tensor, weight: Optional[torch.Tensor],
+                       ignore_index: int, label_smoothing: float, lse_square_scale: float,
+                       softcap: Optional[float], reduction: str, row_stats: torch.Tensor,
+                       grad_output: torch.Tensor, grad: Optional[torch.Tensor] = None
+                       ) -> torch.Tensor:
+    """grad (rows, V) = grad_output * d loss / d logits, recomputed from the kept
+    logits x2 and the forward's row_stats; a new tensor unless ``grad`` is given
+    (which may be x2 itself)."""
+    dev = x2.device
+    dt = dtype_code(x2.dtype)
+    rows, V = x2.shape
+    if grad is None:
+        grad = torch.empty((rows, V), device=dev, dtype=x2.dtype)
+    t = t.to(device=dev, dtype=torch.int64).contiguous()
+    w = None if weight is None else weight.to(device=dev, dtype=torch.float32).contiguous()
+    go = grad_output.to(device=dev, dtype=torch.float32).contiguous().reshape(-1)
+    ws = _workspace(dev, 256)
+    status = _lib.ce_backward_recompute(
+        x2.data_ptr(), dt, rows, V, x2.stride(0) if rows > 0 else V, t.data_ptr(),
+        0 if w is None else w.data_ptr(), int(ignore_index), float(label_smoothing),
+        float(lse_square_scale), float(softcap or 0.0), REDUCTION_CODES[reduction],
+        row_stats.data_ptr(), go.data_ptr(), 1 if reduction == "none" else 0, grad.data_ptr(),
+        grad.stride(0) if rows > 0 else V, ws.data_ptr(), ws.numel(), _stream(dev))
+    check(status, "ce_backward_recompute")
+    return grad
 
 
 def backward_(grad2: torch.Tensor, grad_output: torch.Tensor, per_row: bool) -> torch.Tensor:
@@ -126,16 +157,19 @@ class CrossEntropyFunction(torch.autograd.Function):
     @staticmethod
     def forward(ctx, logits, target, weight, ignore_index, lse_square_scale, label_smoothing,
                 reduction, softcap, return_z_loss, return_token_accuracy,
-                return_predicted_tokens, inplace):
+                return_predicted_tokens, inplace, keep_logits=False):
         want_grad = logits.requires_grad
         x2, t = _flatten(logits, target)
         work = x2.detach()
-        if want_grad and not inplace:
+        if want_grad and not inplace and not keep_logits:
             work = work.clone()
+        stats = None
+        if want_grad and keep_logits:
+            stats = torch.empty((x2.shape[0], 2), device=x2.device, dtype=torch.float32)
         loss, z_loss, acc, arg, _ = _forward_raw(
             work, t, weight, ignore_index, label_smoothing, lse_square_scale, softcap,
-            reduction, want_grad, return_z_loss, return_token_accuracy,
-            return_predicted_tokens)
+            reduction, want_grad and not keep_logits, return_z_loss, return_token_accuracy,
+            return_predicted_tokens, row_stats=stats)
         lead = logits.shape[:-1]
         if reduction == "none":
             loss = loss.reshape(lead)
@@ -145,7 +179,11 @@ class CrossEntropyFunction(torch.autograd.Function):
             arg = arg.reshape(lead)
         ctx.reduction = reduction
         ctx.shape = logits.shape
-        if want_grad:
+        ctx.keep_logits = keep_logits
+        if want_grad and keep_logits:
+            ctx.options = (ignore_index, label_smoothing, lse_square_scale, softcap)
+            ctx.save_for_backward(work, t, stats, weight)
+        elif want_grad:
             ctx.save_for_backward(work)
         for o in (z_loss, acc, arg):
             if o is not None:
@@ -154,9 +192,15 @@ class CrossEntropyFunction(torch.autograd.Function):
 
     @staticmethod
     def backward(ctx, grad_loss, *_):
-        (g,) = ctx.saved_tensors
-        backward_(g, grad_loss, per_row=(ctx.reduction == "none"))
-        return (g.view(ctx.shape),) + (None,) * 11
+        if ctx.keep_logits:
+            x2, t, stats, weight = ctx.saved_tensors
+            ii, eps, lam, cap = ctx.options
+            g = backward_recompute(x2, t, weight, ii, eps, lam, cap, ctx.reduction, stats,
+                                   grad_loss)
+        else:
+            (g,) = ctx.saved_tensors
+            backward_(g, grad_loss, per_row=(ctx.reduction == "none"))
+        return (g.view(ctx.shape),) + (None,) * 12
 
 
 def cross_entropy(logits: torch.Tensor, target: torch.Tensor, weight: Optional[torch.Tensor] = None,
@@ -164,14 +208,16 @@ def cross_entropy(logits: torch.Tensor, target: torch.Tensor, weight: Optional[t
                   label_smoothing: float = 0.0, reduction: str = "mean",
                   softcap: Optional[float] = None, return_z_loss: bool = False,
                   return_token_accuracy: bool = False, return_predicted_tokens: bool = False,
-                  inplace: bool = True):
+                  inplace: bool = True, keep_logits: bool = False):
     """Fused softmax cross-entropy. Returns the loss, or a CEOutput when any
-    ``return_*`` flag is set (fields not requested are None)."""
+    ``return_*`` flag is set (fields not requested are None). ``keep_logits``:
+    the logits are left intact and the backward recomputes the gradient."""
     if softcap is not None and softcap <= 0:
         raise ValueError("softcap must be None or > 0")
     loss, z, acc, arg = CrossEntropyFunction.apply(
         logits, target, weight, ignore_index, lse_square_scale, label_smoothing, reduction,
-        softcap, return_z_loss, return_token_accuracy, return_predicted_tokens, inplace)
+        softcap, return_z_loss, return_token_accuracy, return_predicted_tokens, inplace,
+        keep_logits)
     if return_z_loss or return_token_accuracy or return_predicted_tokens:
         return CEOutput(loss, z, acc, arg)
     return loss
@@ -184,7 +230,8 @@ class CrossEntropyLoss(torch.nn.Module):
                  lse_square_scale: float = 0.0, label_smoothing: float = 0.0,
                  reduction: str = "mean", softcap: Optional[float] = None,
                  return_z_loss: bool = False, return_token_accuracy: bool = False,
-                 return_predicted_tokens: bool = False, inplace: bool = True):
+                 return_predicted_tokens: bool = False, inplace: bool = True,
+                 keep_logits: bool = False):
         super().__init__()
         if reduction not in REDUCTION_CODES:
             raise ValueError(f"reduction must be one of {tuple(REDUCTION_CODES)}")
@@ -202,22 +249,24 @@ class CrossEntropyLoss(torch.nn.Module):
         self.return_token_accuracy = return_token_accuracy
         self.return_predicted_tokens = return_predicted_tokens
         self.inplace = inplace
+        self.keep_logits = keep_logits
 
     def forward(self, logits: torch.Tensor, target: torch.Tensor):
         return cross_entropy(logits, target, self.weight, self.ignore_index,
                              self.lse_square_scale, self.label_smoothing, self.reduction,
                              self.softcap, self.return_z_loss, self.return_token_accuracy,
-                             self.return_predicted_tokens, self.inplace)
+                             self.return_predicted_tokens, self.inplace, self.keep_logits)
 
 
 def forward_raw(logits2d: torch.Tensor, target: torch.Tensor, weight=None, ignore_index=-100,
                 label_smoothing=0.0, lse_square_scale=0.0, softcap=None, reduction="mean",
                 grad=True, z_loss=False, token_accuracy=False, argmax=False, counts=False,
-                check_targets=False, flags=0):
+                check_targets=False, flags=0, row_stats=None):
     """Direct call of ce_forward on a 2-D (rows, V) tensor (overwritten by the
-    gradient when ``grad``). Returns (loss, z_loss, token_accuracy, argmax, counts)."""
+    gradient when ``grad``). Returns (loss, z_loss, token_accuracy, argmax, counts);
+    ``row_stats``, a (rows, 2) float32 tensor, receives the per-row (m, log2 s)."""
     if logits2d.dim() != 2 or logits2d.stride(-1) != 1:
         raise ValueError("logits2d must be 2-D with unit class stride")
     return _forward_raw(logits2d, target, weight, ignore_index, label_smoothing,
                         lse_square_scale, softcap, reduction, grad, z_loss, token_accuracy,
-                        argmax, counts, check_targets, flags)
+                        argmax, counts, check_targets, flags, row_stats)

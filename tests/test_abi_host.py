@@ -67,7 +67,7 @@ def _fwd(**kw):
     a = dict(logits=FAKE, dtype=_lib.CE_F32, rows=4, V=16, row_stride=16, target=FAKE, weight=0,
              ignore_index=-100, label_smoothing=0.0, lse_square_scale=0.0, softcap=0.0,
              reduction=_lib.CE_RED_MEAN, flags=0, loss=FAKE, z_loss=0, token_accuracy=0,
-             argmax=0, counts=0, workspace=0, workspace_bytes=0, stream=0)
+             argmax=0, counts=0, row_stats=0, workspace=0, workspace_bytes=0, stream=0)
     a.update(kw)
     return _lib.ce_forward(**a)
 
@@ -109,6 +109,33 @@ def test_backward_validation(kw, status):
              per_row=0, stream=0)
     a.update(kw)
     assert _lib.ce_backward(**a) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=3), _lib.CE_E_DTYPE),
+    (dict(rows=-1), _lib.CE_E_SHAPE),
+    (dict(row_stride=15), _lib.CE_E_SHAPE),
+    (dict(grad_stride=15), _lib.CE_E_SHAPE),
+    (dict(grad=FAKE, grad_stride=32), _lib.CE_E_SHAPE),   # in place needs the logits' stride
+    (dict(reduction=5), _lib.CE_E_PARAM),
+    (dict(label_smoothing=-0.5), _lib.CE_E_PARAM),
+    (dict(softcap=float("nan")), _lib.CE_E_PARAM),
+    (dict(grad_output=0), _lib.CE_E_NULL),
+    (dict(row_stats=0), _lib.CE_E_NULL),
+    (dict(grad=0), _lib.CE_E_NULL),
+    (dict(logits=0), _lib.CE_E_NULL),
+    (dict(workspace=0), _lib.CE_E_WORKSPACE),
+    (dict(workspace=FAKE + 16), _lib.CE_E_WORKSPACE),
+    (dict(workspace_bytes=128), _lib.CE_E_WORKSPACE),
+    (dict(rows=0, logits=0, grad=0, row_stats=0), _lib.CE_OK),
+])
+def test_backward_recompute_validation(kw, status):
+    a = dict(logits=FAKE, dtype=_lib.CE_F32, rows=4, V=16, row_stride=16, target=FAKE, weight=0,
+             ignore_index=-100, label_smoothing=0.0, lse_square_scale=0.0, softcap=0.0,
+             reduction=_lib.CE_RED_MEAN, row_stats=FAKE, grad_output=FAKE, per_row=0,
+             grad=FAKE + 4096, grad_stride=16, workspace=FAKE, workspace_bytes=256, stream=0)
+    a.update(kw)
+    assert _lib.ce_backward_recompute(**a) == status
 
 
 def test_workspace_bytes():

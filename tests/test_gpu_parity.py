@@ -16,7 +16,7 @@ import synth
 from oracle import rows_forward, summarize_targets
 from parity import (OracleRef, assert_acc_exact, assert_grad_close, assert_loss_close,
                     host_logits)
-from softmax_cross_entropy_amd import _lib, backward_, forward_raw
+from softmax_cross_entropy_amd import _lib, backward_, backward_recompute, forward_raw
 from softmax_cross_entropy_amd._lib import (CE_F_FORCE_FUSED, CE_F_FORCE_SCALAR,
                                             CE_F_FORCE_SPLITV)
 
@@ -267,6 +267,84 @@ def test_backward_scale(dtype, go, aligned):
     want = (g0.float().cpu() * gov.float().reshape(-1, 1 if go == "rows" else 1)).to(dtype)
     assert torch.equal(xd.cpu().view(torch.int16 if dtype == torch.bfloat16 else torch.int32),
                        want.view(torch.int16 if dtype == torch.bfloat16 else torch.int32))
+
+
+# ---------------------------------------------------------------------------
+# Gradient recomputed from kept logits (ce_backward_recompute)
+# ---------------------------------------------------------------------------
+
+RECOMPUTE_OPTS = {
+    "plain": dict(),
+    "all": dict(weight=True, eps=0.1, softcap=4.0, lam=1e-2),
+    "smooth_weight": dict(weight=True, eps=0.2),
+}
+
+
+@pytest.mark.parametrize("opt", list(RECOMPUTE_OPTS))
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("reduction,go", [("mean", 1.0), ("sum", 2.5), ("none", "rows")])
+@pytest.mark.parametrize("fwd_path,layout", [("fused", "aligned"), ("splitv", "aligned"),
+                                             ("scalar", "unaligned"), ("fused", "inplace")])
+def test_backward_recompute(opt, dtype, reduction, go, fwd_path, layout):
+    o = RECOMPUTE_OPTS[opt]
+    rows, V = 37, 3001
+    stride = V if layout == "unaligned" else 3008
+    x = synth.make_logits(rows, V, dtype, 3.0, 17)
+    t = synth.make_targets(rows, V, 17, 4)
+    t[3] = V + 5  # out of range: not counted, zero gradient
+    wt = None
+    if o.get("weight"):
+        wt = 0.5 + 1.5 * torch.rand(V, generator=torch.Generator().manual_seed(19))
+    _announce(name=f"recompute-{opt}", dtype=dtype, reduction=reduction, go=go, path=fwd_path,
+              layout=layout)
+    xd = _padded(x, stride)
+    x_before = xd.detach().clone()
+    td = t.to(DEV)
+    wd = None if wt is None else wt.to(DEV)
+    eps, lam, cap = o.get("eps", 0.0), o.get("lam", 0.0), o.get("softcap")
+    stats = torch.empty((rows, 2), device=DEV, dtype=torch.float32)
+    forward_raw(xd, td, wd, -100, eps, lam, cap, reduction, grad=False, row_stats=stats,
+                flags=PATH_FLAGS[fwd_path])
+    torch.cuda.synchronize()
+    assert torch.equal(xd, x_before)  # a forward without the gradient only reads
+    if go == "rows":
+        gov = torch.linspace(-2.0, 3.0, rows)
+    else:
+        gov = torch.tensor(go)
+    if layout == "inplace":
+        g = backward_recompute(xd, td, wd, -100, eps, lam, cap, reduction, stats, gov.to(DEV),
+                               grad=xd)
+    else:
+        g = backward_recompute(xd, td, wd, -100, eps, lam, cap, reduction, stats, gov.to(DEV))
+        assert torch.equal(xd.cpu().view(torch.int16 if dtype == torch.bfloat16 else torch.int32),
+                           x_before.cpu().view(torch.int16 if dtype == torch.bfloat16
+                                               else torch.int32))
+    torch.cuda.synchronize()
+    ref = OracleRef(host_logits(x), t.numpy(), weight=None if wt is None else wt.numpy(),
+                    label_smoothing=eps, lse_square_scale=lam, softcap=cap, reduction=reduction)
+    scale = gov.double().numpy().reshape(-1, 1) if go == "rows" else float(go)
+    assert_grad_close(g, ref.grad * scale, ref.mag * np.abs(scale), zero_rows=ref.not_counted)
+
+
+def test_keep_logits_autograd_matches_inplace():
+    import softmax_cross_entropy_amd as sce
+    rows, V = 300, 8200
+    x = synth.make_logits(rows, V, torch.bfloat16, 2.0, 23).to(DEV)
+    t = synth.make_targets(rows, V, 23, 30).to(DEV)
+    _announce(name="keep_logits", rows=rows, V=V)
+    a = x.clone().requires_grad_(True)
+    la = sce.cross_entropy(a, t, label_smoothing=0.1, lse_square_scale=1e-3, keep_logits=True)
+    (la * 3.0).backward()
+    b = x.clone().requires_grad_(True)
+    lb = sce.cross_entropy(b, t, label_smoothing=0.1, lse_square_scale=1e-3, inplace=False)
+    (lb * 3.0).backward()
+    torch.cuda.synchronize()
+    assert torch.equal(a.detach(), x)          # logits kept
+    assert la.item() == lb.item()
+    # same gradient formula; bf16 stored once (recompute) vs twice (forward, then x3)
+    ref = OracleRef(host_logits(x.cpu()), t.cpu().numpy(), label_smoothing=0.1,
+                    lse_square_scale=1e-3, reduction="mean")
+    assert_grad_close(a.grad, ref.grad * 3.0, ref.mag * 3.0, zero_rows=ref.not_counted)
 
 
 def test_determinism_bitwise():
