@@ -129,7 +129,7 @@ def write_traffic(workload: str, fetch_csv: str, write_csv: str) -> dict:
     return rec
 
 
-def sweep(steps: int, warmup: int) -> None:
+def sweep(steps: int, warmup: int, extra_flags: int = 0) -> None:
     """Context numbers: the Liger CE profile's benchmark sweep shape (B=8, T=512
     rows, bf16, V from 4096 to 131072, mean) for this library's fused forward +
     gradient + backward step, next to PyTorch eager F.cross_entropy forward +
@@ -151,13 +151,13 @@ def sweep(steps: int, warmup: int) -> None:
         loss = torch.empty((), device=dev, dtype=torch.float32)
         go = torch.ones((), device=dev, dtype=torch.float32)
         dt = _lib.CE_BF16
-        wsb = _lib.ce_workspace_bytes(rows, V, dt, _lib.CE_F_GRAD)
+        wsb = _lib.ce_workspace_bytes(rows, V, dt, _lib.CE_F_GRAD | extra_flags)
         ws = _workspace(dev, wsb)
         s = stream.cuda_stream
 
         def ours(b):
             _lib.check(_lib.ce_forward(b.data_ptr(), dt, rows, V, V, t.data_ptr(), 0, -100, 0.0,
-                                       0.0, 0.0, _lib.CE_RED_MEAN, _lib.CE_F_GRAD,
+                                       0.0, 0.0, _lib.CE_RED_MEAN, _lib.CE_F_GRAD | extra_flags,
                                        loss.data_ptr(), 0, 0, 0, 0, 0, ws.data_ptr(), wsb, s),
                        "ce_forward")
             _lib.check(_lib.ce_backward(b.data_ptr(), dt, rows, V, V, go.data_ptr(), 0, s),
@@ -239,6 +239,9 @@ def main(argv=None) -> int:
                          "the recomputing kernel)")
     ap.add_argument("--path", choices=("auto", "fused", "splitv", "scalar"), default="auto",
                     help="force a kernel path (default: the library's choice)")
+    ap.add_argument("--alt-shape", action="store_true",
+                    help="the other fused layout for rows of 8 K to 32 K 16-byte vectors "
+                         "(test hook, for comparing layouts)")
     ap.add_argument("--sweep", action="store_true",
                     help="context sweep over V at the Liger benchmark shape, this library "
                          "against PyTorch eager F.cross_entropy (JSON line per V), then exit")
@@ -251,7 +254,8 @@ def main(argv=None) -> int:
         return 0
 
     if a.sweep:
-        sweep(a.steps, a.warmup)
+        from softmax_cross_entropy_amd import _lib
+        sweep(a.steps, a.warmup, _lib.CE_F_SHAPE_ALT if a.alt_shape else 0)
         return 0
 
     if a.gpus != 1:
@@ -284,6 +288,8 @@ def main(argv=None) -> int:
     flags = _lib.CE_F_GRAD if a.mode == "fused" else 0
     flags |= {"auto": 0, "fused": _lib.CE_F_FORCE_FUSED, "splitv": _lib.CE_F_FORCE_SPLITV,
               "scalar": _lib.CE_F_FORCE_SCALAR}[a.path]
+    if a.alt_shape:
+        flags |= _lib.CE_F_SHAPE_ALT
     rows, V = w.rows, w.V
     f32 = dict(device=dev, dtype=torch.float32)
     loss = torch.empty((rows,) if red == "none" else (), **f32)
@@ -387,6 +393,7 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "mode": a.mode, "rows": rows, "V": V,
                    "reduction": red, "path": path,
+                   "layout": "alternative" if a.alt_shape else "default",
                    "label_smoothing": w.label_smoothing, "softcap": w.softcap,
                    "lse_square_scale": w.lse_square_scale, "class_weights": w.weights,
                    "parallelism": "single GPU"},

@@ -41,6 +41,7 @@ CE_F_CHECK_TARGETS = 1 << 4
 CE_F_FORCE_FUSED = 1 << 5
 CE_F_FORCE_SPLITV = 1 << 6
 CE_F_FORCE_SCALAR = 1 << 7
+CE_F_SHAPE_ALT = 1 << 8
 
 CE_PATH_FUSED = 1
 CE_PATH_SPLITV = 2

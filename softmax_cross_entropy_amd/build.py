@@ -25,7 +25,8 @@ LIB_NAME = "libce_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["ce_api.hip", "ce_inst_f32.hip", "ce_inst_bf16.hip"]
+SOURCES = ["ce_api.hip", "ce_inst_f32.hip", "ce_inst_bf16.hip", "ce_inst_f32_wide.hip",
+           "ce_inst_bf16_wide.hip"]
 
 # -ffp-contract=off: every fused multiply-add in the kernels is written out
 # explicitly, so a value computed in two places (e.g. the target logit and

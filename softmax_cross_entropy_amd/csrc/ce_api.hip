@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "ce.h"
 #include "ce_launch.hpp"
 
@@ -58,6 +60,26 @@ void split_plan(int64_t rows, int64_t nvec, bool forced, Plan* pl) {
   pl->S = static_cast<int>(S < 1 ? 1 : S);
 }
 
+// Fused shape for rows of nvec vectors: the smallest capacity that holds the
+// row, with the layout measured fastest on MI355X where two exist (rows of
+// 8 K to 16 K vectors: 1024 x 16 for bf16, 512 x 32 for fp32; rows of 16 K
+// to 32 K vectors: the row pair for fp32, whose gradient pass is one
+// multiply per element, and the whole row per CU in VGPRs + LDS for bf16,
+// whose gradient pass recomputes the exponential). CE_F_SHAPE_ALT takes the
+// other layout. -1: no fused shape.
+int fused_shape(int64_t nvec, int dtype, uint32_t flags) {
+  const bool alt = (flags & CE_F_SHAPE_ALT) != 0;
+  for (int s = 0; s <= 3; ++s)
+    if (nvec <= kShapes[s].cap()) return s;
+  if (nvec <= kShapes[4].cap()) return (dtype == CE_BF16) != alt ? cehost::kWideShape : 4;
+  if (nvec <= kShapes[cehost::kPairShape].cap()) {
+    const int lds = nvec <= kShapes[6].cap() ? 6 : 7;
+    const bool pair = (dtype == CE_F32) != alt;
+    return pair ? cehost::kPairShape : lds;
+  }
+  return -1;
+}
+
 // Path choice for an aligned problem (alignment is checked by the caller).
 void plan_aligned(int64_t rows, int64_t V, int dtype, uint32_t flags, Plan* pl) {
   const int64_t nvec = V / elems_per_vec(dtype);
@@ -65,13 +87,7 @@ void plan_aligned(int64_t rows, int64_t V, int dtype, uint32_t flags, Plan* pl) 
     split_plan(rows, nvec, true, pl);
     return;
   }
-  int fit = -1;
-  for (int s = 0; s < cehost::kNumShapes; ++s) {
-    if (nvec <= kShapes[s].cap()) {
-      fit = s;
-      break;
-    }
-  }
+  const int fit = fused_shape(nvec, dtype, flags);
   const bool few_rows = rows < 256 && nvec >= 4096;
   if (fit >= 0 && ((flags & CE_F_FORCE_FUSED) || !few_rows)) {
     pl->path = CE_PATH_FUSED;
@@ -109,7 +125,15 @@ struct Layout {
   size_t row_ce, row_z, row_ok, part, total;
 };
 
-Layout layout(int64_t rows, int S) {
+// Partials per row: S for split-V, 2 for a row pair, none otherwise.
+int plan_partials(const Plan& pl) {
+  if (pl.path == CE_PATH_SPLITV) return pl.S;
+  if (pl.path == CE_PATH_FUSED && kShapes[pl.shape].halves == 2) return 4;  // 64 B per half
+  return 0;
+}
+
+Layout layout(int64_t rows, const Plan& pl) {
+  const int S = plan_partials(pl);
   Layout L;
   size_t off = kAlign;  // header
   L.row_ce = off;
@@ -124,18 +148,16 @@ Layout layout(int64_t rows, int S) {
   return L;
 }
 
-int workspace_chunks(int64_t rows, int64_t V, int dtype, uint32_t flags) {
-  Plan pl;
-  plan_aligned(rows, V, dtype, flags, &pl);
-  return pl.path == CE_PATH_SPLITV ? pl.S : 0;
-}
-
 }  // namespace
 
 CE_API size_t ce_workspace_bytes(int64_t rows, int64_t V, int dtype, uint32_t flags) {
   if (dtype != CE_F32 && dtype != CE_BF16) return 0;
   if (!valid_shape(rows, V, V)) return 0;
-  return layout(rows, workspace_chunks(rows, V, dtype, flags)).total;
+  // The largest layout any path of this shape can take (the vector paths
+  // need 16-byte alignment, which is known only at the call).
+  Plan pl;
+  plan_aligned(rows, V, dtype, flags, &pl);
+  return layout(rows, pl).total;
 }
 
 CE_API int ce_plan_path(const void* logits, int dtype, int64_t rows, int64_t V,
@@ -203,8 +225,8 @@ CE_API ce_status ce_forward(void* logits, int dtype, int64_t rows, int64_t V, in
 
   Plan pl;
   make_plan(logits, dtype, rows, V, row_stride, weight, label_smoothing, flags, &pl);
-  if (pl.path == CE_PATH_SPLITV && rows * pl.S > kMaxInt) return CE_E_SHAPE;
-  const Layout L = layout(rows, pl.path == CE_PATH_SPLITV ? pl.S : 0);
+  if (rows * (plan_partials(pl) > 0 ? plan_partials(pl) : 1) > kMaxInt) return CE_E_SHAPE;
+  const Layout L = layout(rows, pl);
   if (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
     return CE_E_WORKSPACE;
   if (workspace_bytes < L.total) return CE_E_WORKSPACE;
@@ -233,6 +255,14 @@ CE_API ce_status ce_forward(void* logits, int dtype, int64_t rows, int64_t V, in
   p.row_z = reinterpret_cast<float*>(ws + L.row_z);
   p.row_ok = reinterpret_cast<int32_t*>(ws + L.row_ok);
   p.part = reinterpret_cast<cedev::Partial*>(ws + L.part);
+  // Row pairs stamp their partials with a number unique to this call, so no
+  // reset is needed between calls that share the workspace. Stamps are taken
+  // from [0xC0000001, 0xFFFFFFFF]: as fp32 bit patterns these are negative
+  // numbers, which no per-row loss array holds, and no other workspace word
+  // (counts, flags, split-V padding) takes such values either.
+  static std::atomic<uint32_t> calls{0};
+  const uint32_t ep = 0xC0000000u | (calls.fetch_add(1, std::memory_order_relaxed) % 0x3FFFFFFFu + 1u);
+  p.epoch = ep;
   p.S = pl.S;
   p.chunk_vec = pl.chunk_vec;
 

@@ -219,7 +219,8 @@ struct Params {
   float* row_z;                        // (rows) z-loss term per row
   int32_t* row_ok;                     // (rows) bit 0: argmax == target, bit 1: counted
   float* row_stats;                    // (rows, 2) shift m and log2 s per row, or null
-  Partial* part;                       // (rows, S) split-V partials
+  Partial* part;                       // (rows, S) split-V partials; 128 bytes per row for row pairs
+  uint32_t epoch;                      // unique per forward call: row-pair exchange stamp
   int S;                               // chunks per row (split-V)
   int chunk_vec;                       // vectors per chunk (split-V)
 };

@@ -3,6 +3,7 @@
 
 #include "ce_kernels.hpp"
 #include "ce_launch.hpp"
+#include "ce_wide.hpp"
 
 namespace cehost {
 
@@ -42,10 +43,32 @@ hipError_t launch_fused(int shape, const Params& p, hipStream_t st) {
     case 2: return launch_rows<E, SC, SM, 256, 16, 0>(p, st);
     case 3: return launch_rows<E, SC, SM, 512, 16, 0>(p, st);
     case 4: return launch_rows<E, SC, SM, 512, 32, 0>(p, st);
-    case 5: return launch_rows<E, SC, SM, 512, 44, 19>(p, st);
-    case 6: return launch_rows<E, SC, SM, 512, 45, 19>(p, st);
+    case 6: return launch_rows<E, SC, SM, 512, 44, 19>(p, st);
+    case 7: return launch_rows<E, SC, SM, 512, 45, 19>(p, st);
+    case kWideShape:
+    case kPairShape: {
+      const int halves = kShapes[shape].halves;
+      if constexpr (E::EPV == 4) return launch_wide_f32(halves, p, st);
+      return launch_wide_bf16(halves, p, st);
+    }
     default: return hipErrorInvalidValue;
   }
+}
+
+// wide_kernel launch (instantiated in the ce_inst_*_wide units).
+template <class E, int HALVES, int SC, int SM>
+hipError_t launch_wide_t(const Params& p, hipStream_t st) {
+  cedev::wide_kernel<E, HALVES, SC, SM>
+      <<<dim3(static_cast<unsigned>(p.rows * HALVES)), cedev::kWideBlock, 0, st>>>(p);
+  return hipGetLastError();
+}
+
+template <class E, int HALVES>
+hipError_t launch_wide_h(const Params& p, hipStream_t st) {
+  const bool sc = p.softcap > 0.0f;
+  const bool sm = p.eps > 0.0f;
+  if (sc) return sm ? launch_wide_t<E, HALVES, 1, 1>(p, st) : launch_wide_t<E, HALVES, 1, 0>(p, st);
+  return sm ? launch_wide_t<E, HALVES, 0, 1>(p, st) : launch_wide_t<E, HALVES, 0, 0>(p, st);
 }
 
 template <class E, int SC, int SM>

@@ -18,13 +18,13 @@ from parity import (OracleRef, assert_acc_exact, assert_grad_close, assert_loss_
                     host_logits)
 from softmax_cross_entropy_amd import _lib, backward_, backward_recompute, forward_raw
 from softmax_cross_entropy_amd._lib import (CE_F_FORCE_FUSED, CE_F_FORCE_SCALAR,
-                                            CE_F_FORCE_SPLITV)
+                                            CE_F_FORCE_SPLITV, CE_F_SHAPE_ALT)
 
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
 PATH_FLAGS = {"auto": 0, "fused": CE_F_FORCE_FUSED, "splitv": CE_F_FORCE_SPLITV,
-              "scalar": CE_F_FORCE_SCALAR}
+              "scalar": CE_F_FORCE_SCALAR, "fused_alt": CE_F_FORCE_FUSED | CE_F_SHAPE_ALT}
 
 
 def _announce(**kw):
@@ -376,40 +376,56 @@ def test_determinism_bitwise():
 # ---------------------------------------------------------------------------
 
 SHAPE_CASES = [
-    # (dtype, V, rows, options): V picks the shape, rows exceed its resident grid
+    # (dtype, V, rows, options): V picks the shape (default layout / the
+    # alternative one where a row size has two), rows exceed the resident grid
     (torch.float32, 4001, 2600, dict()),                              # 256 x 4
     (torch.float32, 16001, 1100, dict(eps=0.1, lam=1e-3)),            # 256 x 16
-    (torch.float32, 65001, 300, dict(weight=True, eps=0.05)),         # 512 x 32
-    (torch.float32, 129001, 300, dict(lam=1e-4)),                     # 512 x 44 + 19 LDS
+    (torch.float32, 65001, 300, dict(weight=True, eps=0.05)),         # 512 x 32 / 1024 x 16
+    (torch.float32, 129001, 300, dict(lam=1e-4)),                     # row pair / 512 x (44 + 19)
     (torch.bfloat16, 16001, 2600, dict(softcap=20.0)),                # 256 x 8
     (torch.bfloat16, 65001, 600, dict()),                             # 512 x 16
-    (torch.bfloat16, 131001, 300, dict(weight=True, eps=0.1, softcap=30.0, lam=1e-4)),  # 512 x 32
+    (torch.bfloat16, 131001, 300, dict(weight=True, eps=0.1, softcap=30.0, lam=1e-4)),
     # the two largest shapes with every per-element option (fewer rows: oracle time)
-    (torch.float32, 130001, 40, dict(weight=True, eps=0.1, softcap=15.0)),    # 512 x 45 + 19 LDS
-    (torch.bfloat16, 250001, 40, dict(eps=0.1, softcap=30.0, lam=1e-4)),      # 512 x 44 + 19 LDS
-    (torch.bfloat16, 262001, 24, dict(weight=True, eps=0.2)),                 # 512 x 45 + 19 LDS
+    (torch.float32, 130001, 40, dict(weight=True, eps=0.1, softcap=15.0)),    # row pair / 45 + 19
+    (torch.bfloat16, 250001, 40, dict(eps=0.1, softcap=30.0, lam=1e-4)),      # 44 + 19 / row pair
+    (torch.bfloat16, 262001, 24, dict(weight=True, eps=0.2)),                 # 45 + 19 / row pair
+    # row pairs: argmax and target in either half, a tie across the halves,
+    # small logits (|max| < 2: the argmax re-reads raw logits), no row tail
+    (torch.float32, 128256, 64, dict(sigma=0.3, tie=1.5)),
+    (torch.bfloat16, 262144, 48, dict(sigma=0.5, tie=4.0)),
 ]
 
 
 @pytest.mark.parametrize("case", range(len(SHAPE_CASES)))
 @pytest.mark.parametrize("reduction", ["mean", "none"])
-def test_fused_shapes_many_rows(case, reduction):
+@pytest.mark.parametrize("layout", ["fused", "fused_alt"])
+def test_fused_shapes_many_rows(case, reduction, layout):
     dtype, V, rows, o = SHAPE_CASES[case]
     seed = 100 + case
-    x = synth.make_logits(rows, V, dtype, 2.5, seed)
+    x = synth.make_logits(rows, V, dtype, o.get("sigma", 2.5), seed)
     t = synth.make_targets(rows, V, seed, rows * 3 // 10)
+    if o.get("tie"):
+        # equal maxima in both halves of every other row (first one in half 0),
+        # the single maximum in the second half of the rest
+        for r in range(rows):
+            x[r, V - 5] = o["tie"]
+            if r % 2 == 0:
+                x[r, 7 + r] = o["tie"]
+        t[1::4] = V - 3
     wt = None
     if o.get("weight"):
         wt = 0.5 + 1.5 * torch.rand(V, generator=torch.Generator().manual_seed(seed))
     stride = (V + 7) // 8 * 8  # 16-byte aligned rows: the vector path
     run_case(x, t, weight=wt, eps=o.get("eps", 0.0), lam=o.get("lam", 0.0),
-             softcap=o.get("softcap"), reduction=reduction, path="fused", stride=stride,
+             softcap=o.get("softcap"), reduction=reduction, path=layout, stride=stride,
              name=f"shape-{case}")
 
 
-def test_persistent_claims_reset_between_calls():
-    """Row claims start from zero on every call: the same batch gives the same
-    bits after calls of other sizes share the workspace."""
+@pytest.mark.parametrize("alt", [False, True])
+def test_persistent_claims_reset_between_calls(alt):
+    """Row claims (persistent kernel) start from zero on every call and row
+    pairs find only this call's partials: the same batch gives the same bits
+    after calls of other sizes share the workspace."""
     V = 129001
     xa = synth.make_logits(600, V, torch.float32, 2.0, 91)
     ta = synth.make_targets(600, V, 91, 40)
@@ -417,11 +433,12 @@ def test_persistent_claims_reset_between_calls():
     tb = synth.make_targets(290, V, 92, 200)
     outs = []
     for x, t in ((xa, ta), (xb, tb), (xa, ta), (xb, tb), (xa, ta)):
-        _announce(name="claims", rows=x.shape[0], V=V)
+        _announce(name="claims", rows=x.shape[0], V=V, alt=alt)
         xd = _padded(x, V + 7)
-        assert _plan(xd, None, 0.0, 0) == "fused"
+        flags = CE_F_SHAPE_ALT if alt else 0
+        assert _plan(xd, None, 0.0, flags) == "fused"
         r = forward_raw(xd, t.to(DEV), reduction="sum", z_loss=True, token_accuracy=True,
-                        argmax=True, counts=True)
+                        argmax=True, counts=True, flags=flags)
         torch.cuda.synchronize()
         outs.append((xd.cpu(), [o.cpu() for o in r if o is not None]))
     for a, b in ((0, 2), (0, 4), (1, 3)):
