@@ -61,21 +61,18 @@ void split_plan(int64_t rows, int64_t nvec, bool forced, Plan* pl) {
 }
 
 // Fused shape for rows of nvec vectors: the smallest capacity that holds the
-// row, with the layout measured fastest on MI355X where two exist (rows of
-// 8 K to 16 K vectors: 1024 x 16 for bf16, 512 x 32 for fp32; rows of 16 K
-// to 32 K vectors: the row pair for fp32, whose gradient pass is one
-// multiply per element, and the whole row per CU in VGPRs + LDS for bf16,
-// whose gradient pass recomputes the exponential). CE_F_SHAPE_ALT takes the
-// other layout. -1: no fused shape.
-int fused_shape(int64_t nvec, int dtype, uint32_t flags) {
+// row. Rows of 8 K to 32 K vectors take the 1024-thread layouts (one
+// workgroup, or a row pair), measured faster on MI355X than 512-thread
+// workgroups holding the whole row; CE_F_SHAPE_ALT takes the 512-thread
+// layouts instead (a test hook for comparing them). -1: no fused shape.
+int fused_shape(int64_t nvec, uint32_t flags) {
   const bool alt = (flags & CE_F_SHAPE_ALT) != 0;
   for (int s = 0; s <= 3; ++s)
     if (nvec <= kShapes[s].cap()) return s;
-  if (nvec <= kShapes[4].cap()) return (dtype == CE_BF16) != alt ? cehost::kWideShape : 4;
+  if (nvec <= kShapes[4].cap()) return alt ? 4 : cehost::kWideShape;
   if (nvec <= kShapes[cehost::kPairShape].cap()) {
-    const int lds = nvec <= kShapes[6].cap() ? 6 : 7;
-    const bool pair = (dtype == CE_F32) != alt;
-    return pair ? cehost::kPairShape : lds;
+    if (!alt) return cehost::kPairShape;
+    return nvec <= kShapes[6].cap() ? 6 : 7;
   }
   return -1;
 }
@@ -87,7 +84,7 @@ void plan_aligned(int64_t rows, int64_t V, int dtype, uint32_t flags, Plan* pl) 
     split_plan(rows, nvec, true, pl);
     return;
   }
-  const int fit = fused_shape(nvec, dtype, flags);
+  const int fit = fused_shape(nvec, flags);
   const bool few_rows = rows < 256 && nvec >= 4096;
   if (fit >= 0 && ((flags & CE_F_FORCE_FUSED) || !few_rows)) {
     pl->path = CE_PATH_FUSED;

@@ -26,6 +26,7 @@ constexpr int kNoIndex = 0x7fffffff;
 constexpr int kPrologueBlock = 1024;  // threads of the single-workgroup prologue
 constexpr int kBwdBlock = 256;        // backward: threads per block
 constexpr int kBwdUnroll = 4;         // backward: vectors per thread
+constexpr int kBwdMaxGrid = 4096;     // backward: blocks (grid-stride over the rest)
 
 // ---------------------------------------------------------------------------
 // Hardware transcendentals (v_exp_f32 = 2^x, v_log_f32 = log2 x, v_rcp_f32).

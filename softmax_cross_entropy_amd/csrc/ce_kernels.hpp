@@ -1202,48 +1202,57 @@ __global__ __launch_bounds__(kBwdBlock) void recompute_kernel(Params p, void* gr
 
 // ---------------------------------------------------------------------------
 // Backward: the stored gradient times grad_output, in place (Liger-Kernel CE
-// profile, Backward Pass). A block whose scale is exactly 1 exits at once.
+// profile, Backward Pass). Work units are (row, span of kBwdBlock x
+// kBwdUnroll vectors); a bounded grid strides over them. A scalar
+// grad_output of exactly 1 ends every block at once (the common
+// loss.backward() call costs one small launch); with per-row scales a unit
+// whose row scale is exactly 1 is skipped.
 // ---------------------------------------------------------------------------
 template <class E, bool VEC>
-__global__ __launch_bounds__(kBwdBlock) void backward_kernel(void* grad, int64_t V, int64_t stride,
-                                                             const float* go, int per_row,
-                                                             int blocks_per_row) {
+__global__ __launch_bounds__(kBwdBlock) void backward_kernel(void* grad, int64_t rows, int64_t V,
+                                                             int64_t stride, const float* go,
+                                                             int per_row, int blocks_per_row) {
   constexpr int EPV = E::EPV;
-  const int64_t row = blockIdx.x / blocks_per_row;
-  const int b = blockIdx.x - static_cast<int>(row) * blocks_per_row;
-  const float g = per_row ? go[row] : go[0];
-  if (g == 1.0f) return;
-  char* rp = static_cast<char*>(grad) + row * stride * E::BYTES;
+  if (!per_row && go[0] == 1.0f) return;
+  const int64_t units = rows * blocks_per_row;
   const int tid = threadIdx.x;
-  if constexpr (VEC) {
-    const int nvec = static_cast<int>(V / EPV);
-    u4* vp = reinterpret_cast<u4*>(rp);
-    const int j0 = b * kBwdBlock * kBwdUnroll;
-    u4 v[kBwdUnroll];
+  for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+    const int64_t row = unit / blocks_per_row;
+    const int b = static_cast<int>(unit - row * blocks_per_row);
+    const float g = per_row ? go[row] : go[0];
+    if (g == 1.0f) continue;
+    char* rp = static_cast<char*>(grad) + row * stride * E::BYTES;
+    if constexpr (VEC) {
+      const int nvec = static_cast<int>(V / EPV);
+      u4* vp = reinterpret_cast<u4*>(rp);
+      const int j0 = b * kBwdBlock * kBwdUnroll;
+      u4 v[kBwdUnroll];
 #pragma unroll
-    for (int u = 0; u < kBwdUnroll; ++u) {
-      const int j = j0 + u * kBwdBlock + tid;
-      v[u] = (j < nvec) ? vp[j] : u4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int u = 0; u < kBwdUnroll; ++u) {
-      const int j = j0 + u * kBwdBlock + tid;
-      if (j < nvec) {
-        float f[EPV];
-        E::unpack(v[u], f);
-#pragma unroll
-        for (int i = 0; i < EPV; ++i) f[i] *= g;
-        __builtin_nontemporal_store(E::pack(f), vp + j);
+      for (int u = 0; u < kBwdUnroll; ++u) {
+        const int j = j0 + u * kBwdBlock + tid;
+        v[u] = (j < nvec) ? vp[j] : u4{0u, 0u, 0u, 0u};
       }
+#pragma unroll
+      for (int u = 0; u < kBwdUnroll; ++u) {
+        const int j = j0 + u * kBwdBlock + tid;
+        if (j < nvec) {
+          float f[EPV];
+          E::unpack(v[u], f);
+#pragma unroll
+          for (int i = 0; i < EPV; ++i) f[i] *= g;
+          __builtin_nontemporal_store(E::pack(f), vp + j);
+        }
+      }
+      if (b == blocks_per_row - 1) {
+        const int64_t tail0 = static_cast<int64_t>(nvec) * EPV;
+        if (tail0 + tid < V) E::st(rp, tail0 + tid, E::ld(rp, tail0 + tid) * g);
+      }
+    } else {
+      const int64_t span = static_cast<int64_t>(kBwdBlock) * kBwdUnroll;
+      const int64_t k0 = static_cast<int64_t>(b) * span;
+      for (int64_t k = k0 + tid; k < V && k < k0 + span; k += kBwdBlock)
+        E::st(rp, k, E::ld(rp, k) * g);
     }
-    if (b == blocks_per_row - 1) {
-      const int64_t tail0 = static_cast<int64_t>(nvec) * EPV;
-      if (tail0 + tid < V) E::st(rp, tail0 + tid, E::ld(rp, tail0 + tid) * g);
-    }
-  } else {
-    const int64_t span = static_cast<int64_t>(kBwdBlock) * kBwdUnroll;
-    const int64_t k0 = static_cast<int64_t>(b) * span;
-    for (int64_t k = k0 + tid; k < V && k < k0 + span; k += kBwdBlock) E::st(rp, k, E::ld(rp, k) * g);
   }
 }
 

@@ -9,26 +9,37 @@ namespace cehost {
 
 using cedev::Params;
 
-// Persistent row kernel: as many workgroups as fit on the device at once
-// (occupancy x compute units, cached per device), at most one per row.
-template <class E, int SC, int SM, int BLOCK, int NREG, int NLDS>
-hipError_t launch_rows(const Params& p, hipStream_t st) {
+// Workgroups of `kernel` (BLOCK threads) resident on the current device at
+// once: occupancy x compute units, cached per device and kernel.
+template <class K>
+hipError_t resident_blocks(K kernel, int block, int* cache, int* out) {
   constexpr int kMaxDevices = 64;
-  static int resident[kMaxDevices] = {};
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  int r = (dev >= 0 && dev < kMaxDevices) ? resident[dev] : 0;
+  int r = (dev >= 0 && dev < kMaxDevices) ? cache[dev] : 0;
   if (r == 0) {
     int per_cu = 0, ncu = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &per_cu, cedev::rows_kernel<E, BLOCK, NREG, NLDS, SC, SM>, BLOCK, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0);
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
     r = (per_cu > 0 ? per_cu : 1) * (ncu > 0 ? ncu : 1);
-    if (dev >= 0 && dev < kMaxDevices) resident[dev] = r;
+    if (dev >= 0 && dev < kMaxDevices) cache[dev] = r;
   }
+  *out = r;
+  return hipSuccess;
+}
+
+// Persistent row kernel: as many workgroups as fit on the device at once
+// (occupancy x compute units, cached per device), at most one per row.
+template <class E, int SC, int SM, int BLOCK, int NREG, int NLDS>
+hipError_t launch_rows(const Params& p, hipStream_t st) {
+  static int cache[64] = {};
+  int r = 0;
+  const hipError_t e =
+      resident_blocks(cedev::rows_kernel<E, BLOCK, NREG, NLDS, SC, SM>, BLOCK, cache, &r);
+  if (e != hipSuccess) return e;
   const int64_t grid = p.rows < r ? p.rows : r;
   cedev::rows_kernel<E, BLOCK, NREG, NLDS, SC, SM>
       <<<dim3(static_cast<unsigned>(grid)), BLOCK, 0, st>>>(p);
@@ -55,11 +66,19 @@ hipError_t launch_fused(int shape, const Params& p, hipStream_t st) {
   }
 }
 
-// wide_kernel launch (instantiated in the ce_inst_*_wide units).
+// wide_kernel launch (instantiated in the ce_inst_*_wide units): persistent,
+// at most one workgroup per part.
 template <class E, int HALVES, int SC, int SM>
 hipError_t launch_wide_t(const Params& p, hipStream_t st) {
+  static int cache[64] = {};
+  int r = 0;
+  const hipError_t e =
+      resident_blocks(cedev::wide_kernel<E, HALVES, SC, SM>, cedev::kWideBlock, cache, &r);
+  if (e != hipSuccess) return e;
+  const int64_t parts = p.rows * HALVES;
+  const int64_t grid = parts < r ? parts : r;
   cedev::wide_kernel<E, HALVES, SC, SM>
-      <<<dim3(static_cast<unsigned>(p.rows * HALVES)), cedev::kWideBlock, 0, st>>>(p);
+      <<<dim3(static_cast<unsigned>(grid)), cedev::kWideBlock, 0, st>>>(p);
   return hipGetLastError();
 }
 
@@ -148,13 +167,14 @@ hipError_t launch_backward(void* grad, int64_t rows, int64_t V, int64_t stride, 
   int64_t units = vec ? (V / E::EPV) : V;
   int64_t bpr = (units + span - 1) / span;
   if (bpr < 1) bpr = 1;
-  const dim3 grid(static_cast<unsigned>(rows * bpr));
+  const int64_t total = rows * bpr;
+  const dim3 grid(static_cast<unsigned>(total < cedev::kBwdMaxGrid ? total : cedev::kBwdMaxGrid));
   if (vec) {
-    cedev::backward_kernel<E, true>
-        <<<grid, cedev::kBwdBlock, 0, st>>>(grad, V, stride, go, per_row, static_cast<int>(bpr));
+    cedev::backward_kernel<E, true><<<grid, cedev::kBwdBlock, 0, st>>>(
+        grad, rows, V, stride, go, per_row, static_cast<int>(bpr));
   } else {
-    cedev::backward_kernel<E, false>
-        <<<grid, cedev::kBwdBlock, 0, st>>>(grad, V, stride, go, per_row, static_cast<int>(bpr));
+    cedev::backward_kernel<E, false><<<grid, cedev::kBwdBlock, 0, st>>>(
+        grad, rows, V, stride, go, per_row, static_cast<int>(bpr));
   }
   return hipGetLastError();
 }

@@ -69,8 +69,38 @@ __device__ __forceinline__ bool pair_exchange(const Params& p, int64_t row, int 
   }
 }
 
+// Block-shared state of the part in flight.
+struct WideShared {
+  Acc acc[kWideBlock / 64];
+  int cand[kWideBlock / 64];
+  RowScalars rs;
+  float xy;
+  int64_t next_t, next_y;  // the part claimed next and its row's target
+};
+
+// Part claims: workgroup b starts with part b; thread 0 claims the next one
+// (gridDim.x + the claim counter) once the current part's pass 1 is done, so
+// parts go to workgroups in the order they finish. Every part processed
+// takes exactly one claim, so the claim that returns parts - 1 is the
+// launch's last and resets the counter for the next launch. The two halves
+// of a row are consecutive parts: their claims are made one after the other.
+__device__ __forceinline__ uint32_t claim_issue(const Params& p) {
+  return __hip_atomic_fetch_add(&p.hdr->next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <int HALVES>
+__device__ __forceinline__ void claim_finish(const Params& p, uint32_t c, WideShared& sh) {
+  const int64_t parts = p.rows * HALVES;
+  if (c == static_cast<uint32_t>(parts - 1))
+    __hip_atomic_store(&p.hdr->next, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int64_t nt = static_cast<int64_t>(gridDim.x) + c;
+  sh.next_t = nt;
+  sh.next_y = nt < parts ? p.target[nt / HALVES] : 0;
+}
+
+// One part (a whole row, or half of one) of the persistent wide kernel.
 template <class E, int HALVES, int SC, int SM>
-__global__ __launch_bounds__(kWideBlock) void wide_kernel(Params p) {
+__device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
+                                          WideShared& sh) {
   constexpr int BLOCK = kWideBlock;
   constexpr int NREG = kWideSlots;
   constexpr int NW = BLOCK / 64;
@@ -78,18 +108,17 @@ __global__ __launch_bounds__(kWideBlock) void wide_kernel(Params p) {
   constexpr int GS = (EPV == 4) ? 4 : 2;  // slots per pass-1 group
   constexpr int NG = NREG / GS;
   constexpr bool KEEP_E = (EPV == 4) && !SC;
-  __shared__ Acc s_acc[NW];
-  __shared__ int s_cand[NW];
-  __shared__ RowScalars s_rs;
-  __shared__ float s_xy;
-  __shared__ int s_last;
+  Acc* s_acc = sh.acc;
+  int* s_cand = sh.cand;
 
-  const int64_t row = blockIdx.x / HALVES;
-  const int h = HALVES == 1 ? 0 : static_cast<int>(blockIdx.x % HALVES);
-  const int tid = threadIdx.x;
+  const int64_t row = t / HALVES;
+  const int h = HALVES == 1 ? 0 : static_cast<int>(t % HALVES);
+  // Opaque per part: values derived from the thread index are recomputed per
+  // part instead of being kept live across the loop.
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t y = p.target[row];
   const bool ignored = (y == p.ignore_index);
   const bool bad = !ignored && (y < 0 || y >= p.V);
   char* rp = row_ptr(p, row, E::BYTES);
@@ -106,6 +135,9 @@ __global__ __launch_bounds__(kWideBlock) void wide_kernel(Params p) {
   if (ignored || bad) {
     // Ignored rows are never read; their gradient is exactly +0.0
     // (tt-mlir PR #9324 page: ignored rows, also with non-finite logits).
+    __syncthreads();  // every thread has read the previous part's next_t
+    if (tid == 0) claim_finish<HALVES>(p, claim_issue(p), sh);
+    __syncthreads();
     if (p.grad) {
       u4* vp = reinterpret_cast<u4*>(hp);
       for (int j = tid; j < nv; j += BLOCK) __builtin_nontemporal_store(u4{0u, 0u, 0u, 0u}, vp + j);
@@ -307,6 +339,7 @@ __global__ __launch_bounds__(kWideBlock) void wide_kernel(Params p) {
       t.bv = bmax;
       t.bi = arg;
       if (lane == 0) {
+        const uint32_t claim = claim_issue(p);
         if constexpr (HALVES == 2) {
           // Exchange partials with the other half; both combine half 0 first.
           uint32_t mine_w[kPairWords] = {
@@ -336,8 +369,9 @@ __global__ __launch_bounds__(kWideBlock) void wide_kernel(Params p) {
         row_scalars(rs, t.m, t.s, t.sz, zval<SC>(p, xy), wy, W, p, alpha, beta);
         rs.arg = t.bi;
         rs.ok = (t.bi == y);
-        s_rs = rs;
-        s_xy = xy;
+        sh.rs = rs;
+        sh.xy = xy;
+        claim_finish<HALVES>(p, claim, sh);
         if (h == 0) {
           write_row_outputs(p, row, rs.ce, rs.zl, rs.ok, t.bi);
           write_row_stats(p, row, rs.m, rs.l2s);
@@ -349,7 +383,7 @@ __global__ __launch_bounds__(kWideBlock) void wide_kernel(Params p) {
 
     // ---- pass 2: the gradient from on-chip data, written over the logits ----
     if (p.grad) {
-      const RowScalars rs = s_rs;
+      const RowScalars rs = sh.rs;
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
         if (g * GS * BLOCK < nv) {
@@ -384,14 +418,33 @@ __global__ __launch_bounds__(kWideBlock) void wide_kernel(Params p) {
           tid == static_cast<int>((yl / EPV) % BLOCK)) {
         const float wy = (SM && p.weight) ? p.weight[y] : 1.0f;
         E::template st_buf<kStoreNT>(rsrc, static_cast<int>(yl),
-                                     grad_one<SC, SM>(p, rs, s_xy, wy, true));
+                                     grad_one<SC, SM>(p, rs, sh.xy, wy, true));
       }
     }
   }
+}
+
+// Persistent: as many workgroups as fit on the device at once (at most one
+// per part); each processes parts until the claims run out, then arrives
+// once at the epilogue. The next part's loads are issued as soon as the
+// current part's gradient stores are (they drain while the next part
+// arrives).
+template <class E, int HALVES, int SC, int SM>
+__global__ __launch_bounds__(kWideBlock) void wide_kernel(Params p) {
+  __shared__ WideShared sh;
+  __shared__ int s_last;
+  const int64_t parts = p.rows * HALVES;
+  int64_t t = blockIdx.x;
+  int64_t y = p.target[t / HALVES];
+  while (t < parts) {
+    wide_part<E, HALVES, SC, SM>(p, t, y, sh);
+    t = uniform_i64(sh.next_t);
+    y = uniform_i64(sh.next_y);
+  }
   if (p.epilogue) {
-    if (tid == 0) s_last = arrive(p, gridDim.x);
+    if (threadIdx.x == 0) s_last = arrive(p, gridDim.x);
     __syncthreads();
-    if (s_last) epilogue_reduce<BLOCK>(p);
+    if (s_last) epilogue_reduce<kWideBlock>(p);
   }
 }
 

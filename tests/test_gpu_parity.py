@@ -376,19 +376,20 @@ def test_determinism_bitwise():
 # ---------------------------------------------------------------------------
 
 SHAPE_CASES = [
-    # (dtype, V, rows, options): V picks the shape (default layout / the
-    # alternative one where a row size has two), rows exceed the resident grid
+    # (dtype, V, rows, options): V picks the shape (the default layout / the
+    # CE_F_SHAPE_ALT one where a row size has two); rows exceed the resident
+    # grid, so persistent workgroups claim rows (or half rows) as they finish
     (torch.float32, 4001, 2600, dict()),                              # 256 x 4
     (torch.float32, 16001, 1100, dict(eps=0.1, lam=1e-3)),            # 256 x 16
-    (torch.float32, 65001, 300, dict(weight=True, eps=0.05)),         # 512 x 32 / 1024 x 16
-    (torch.float32, 129001, 300, dict(lam=1e-4)),                     # row pair / 512 x (44 + 19)
+    (torch.float32, 65001, 300, dict(weight=True, eps=0.05)),         # 1024 x 16 / 512 x 32
+    (torch.float32, 129001, 300, dict(lam=1e-4)),                     # row pair / 512 x (45 + 19)
     (torch.bfloat16, 16001, 2600, dict(softcap=20.0)),                # 256 x 8
     (torch.bfloat16, 65001, 600, dict()),                             # 512 x 16
     (torch.bfloat16, 131001, 300, dict(weight=True, eps=0.1, softcap=30.0, lam=1e-4)),
-    # the two largest shapes with every per-element option (fewer rows: oracle time)
-    (torch.float32, 130001, 40, dict(weight=True, eps=0.1, softcap=15.0)),    # row pair / 45 + 19
-    (torch.bfloat16, 250001, 40, dict(eps=0.1, softcap=30.0, lam=1e-4)),      # 44 + 19 / row pair
-    (torch.bfloat16, 262001, 24, dict(weight=True, eps=0.2)),                 # 45 + 19 / row pair
+    # the largest shapes with every per-element option (fewer rows: oracle time)
+    (torch.float32, 130001, 40, dict(weight=True, eps=0.1, softcap=15.0)),    # pair / 45 + 19
+    (torch.bfloat16, 250001, 40, dict(eps=0.1, softcap=30.0, lam=1e-4)),      # pair / 44 + 19
+    (torch.bfloat16, 262001, 24, dict(weight=True, eps=0.2)),                 # pair / 45 + 19
     # row pairs: argmax and target in either half, a tie across the halves,
     # small logits (|max| < 2: the argmax re-reads raw logits), no row tail
     (torch.float32, 128256, 64, dict(sigma=0.3, tie=1.5)),
