@@ -111,7 +111,7 @@ def write_traffic(workload: str, fetch_csv: str, write_csv: str) -> dict:
         copies = [v for k, vs in per.items() if "copyBuffer" in k for v in vs]
         big = [v for v in copies if v >= 0.9 * max(copies)]
         factor = nbytes / (sum(big) / len(big) * 1024.0)
-        kern = {k: vs for k, vs in per.items() if "rows_kernel" in k}
+        kern = {k: vs for k, vs in per.items() if "rows_kernel" in k or "wide_kernel" in k}
         if len(kern) != 1:
             raise SystemExit(f"expected one fused kernel in {path}, found {list(kern)}")
         name, vs = next(iter(kern.items()))
