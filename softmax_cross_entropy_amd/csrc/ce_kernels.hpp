@@ -1023,19 +1023,56 @@ __global__ __launch_bounds__(kPrologueBlock) void prologue_kernel(Params p) {
   double D = 0.0, W = 0.0;
   int64_t n = 0;
   uint32_t err = 0;
-  for (int64_t r = tid; r < p.rows; r += kPrologueBlock) {
-    const int64_t y = p.target[r];
-    if (y != p.ignore_index) {
-      if (y >= 0 && y < p.V) {
-        n += 1;
-        D += p.weight ? static_cast<double>(p.weight[y]) : 1.0;
-      } else {
-        err = 1u;
+  // kU independent loads in flight per thread (one workgroup has to cover
+  // every target and, with weighted smoothing, every class weight); the
+  // sums still run in a fixed order.
+  constexpr int kU = 8;
+  for (int64_t r0 = tid; r0 < p.rows; r0 += static_cast<int64_t>(kPrologueBlock) * kU) {
+    int64_t yv[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t r = r0 + static_cast<int64_t>(u) * kPrologueBlock;
+      yv[u] = r < p.rows ? p.target[r] : p.ignore_index;
+    }
+    float wv[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const bool ok = yv[u] != p.ignore_index && yv[u] >= 0 && yv[u] < p.V;
+      wv[u] = (ok && p.weight) ? p.weight[yv[u]] : 1.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if (yv[u] != p.ignore_index) {
+        if (yv[u] >= 0 && yv[u] < p.V) {
+          n += 1;
+          D += static_cast<double>(wv[u]);
+        } else {
+          err = 1u;
+        }
       }
     }
   }
-  if (p.weight)
-    for (int64_t k = tid; k < p.V; k += kPrologueBlock) W += static_cast<double>(p.weight[k]);
+  if (p.weight) {
+    const bool vec = (reinterpret_cast<uintptr_t>(p.weight) & 15) == 0;
+    const int64_t nv4 = vec ? p.V / 4 : 0;
+    const f4* w4 = reinterpret_cast<const f4*>(p.weight);
+    for (int64_t j0 = tid; j0 < nv4; j0 += static_cast<int64_t>(kPrologueBlock) * kU) {
+      f4 v[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int64_t j = j0 + static_cast<int64_t>(u) * kPrologueBlock;
+        v[u] = j < nv4 ? w4[j] : f4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        W += static_cast<double>(v[u][0]);
+        W += static_cast<double>(v[u][1]);
+        W += static_cast<double>(v[u][2]);
+        W += static_cast<double>(v[u][3]);
+      }
+    }
+    for (int64_t k = nv4 * 4 + tid; k < p.V; k += kPrologueBlock) W += static_cast<double>(p.weight[k]);
+  }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     D += __shfl_xor(D, off, 64);
