@@ -192,6 +192,60 @@ def sweep(steps: int, warmup: int, extra_flags: int = 0) -> None:
         del bufs, x0
 
 
+def linear_bench(steps: int, warmup: int, rows: int = 4096, H: int = 4096, V: int = 128256,
+                 chunk_rows: int = 0) -> None:
+    """The linear layer fused with the cross-entropy at a language-model head
+    shape (B=8, T=512 rows, hidden 4096, V = 128256, bf16), mean reduction:
+    one step = ce_linear_forward with both gradients (grad_output = 1, so the
+    backward's scaling exits at once), against PyTorch eager (bf16 matmul,
+    fp32 cross-entropy, autograd) on the same GPU. Matrix-core roofline:
+    6 rows V H flops per step (three products) against the bf16 dense peak."""
+    import torch
+    import torch.nn.functional as F
+    import synth
+    from softmax_cross_entropy_amd import linear_forward_raw
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    x = (torch.randn(rows, H, device=dev, generator=g) * 0.5).to(torch.bfloat16)
+    w = (torch.randn(V, H, device=dev, generator=g) * (2.0 / H ** 0.5)).to(torch.bfloat16)
+    t = synth.make_targets(rows, V, 7, rows // 20).to(dev)
+
+    def ours():
+        linear_forward_raw(x, w, t, reduction="mean", grad=True, chunk_rows=chunk_rows)
+
+    def eager():
+        xe = x.detach().requires_grad_(True)
+        we = w.detach().requires_grad_(True)
+        loss = F.cross_entropy((xe @ we.t()).float(), t, ignore_index=-100)
+        loss.backward()
+
+    res = {}
+    for name, fn in (("this_library", ours), ("torch_eager", eager)):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / steps
+    flops = 6.0 * rows * V * H
+    tf = flops / (res["this_library"] * 1e-3) / 1e12
+    print(json.dumps({
+        "linear": "linear layer fused with the cross-entropy (hidden @ weight^T, CE, both "
+                  "gradients), mean, bf16 inputs",
+        "config": {"rows": rows, "H": H, "V": V, "chunk_rows": chunk_rows or "default"},
+        "ms_per_step": res,
+        "speedup_vs_torch_eager": res["torch_eager"] / res["this_library"],
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": tf / 2500.0, "flops_per_step": flops}}), flush=True)
+
+
 def cpu_baseline(x_host, t_host, weight_host, w, reduction, budget_s=12.0):
     """Time the float64 oracle, as it is, on a bounded sample of the rows."""
     import numpy as np
@@ -242,6 +296,11 @@ def main(argv=None) -> int:
     ap.add_argument("--alt-shape", action="store_true",
                     help="the other fused layout for rows of 8 K to 32 K 16-byte vectors "
                          "(test hook, for comparing layouts)")
+    ap.add_argument("--linear", action="store_true",
+                    help="the linear layer fused with the cross-entropy at 4096 x 4096 hidden, "
+                         "V = 128256 (JSON line with its matrix-core roofline), then exit")
+    ap.add_argument("--chunk-rows", type=int, default=0,
+                    help="--linear: rows per chunk (0: the library's default)")
     ap.add_argument("--sweep", action="store_true",
                     help="context sweep over V at the Liger benchmark shape, this library "
                          "against PyTorch eager F.cross_entropy (JSON line per V), then exit")
@@ -251,6 +310,10 @@ def main(argv=None) -> int:
     a = ap.parse_args(argv)
     if a.traffic:
         write_traffic(a.workload, *a.traffic)
+        return 0
+
+    if a.linear:
+        linear_bench(a.steps, a.warmup, chunk_rows=a.chunk_rows)
         return 0
 
     if a.sweep:

@@ -163,6 +163,69 @@ ce_status ce_backward_recompute(const void* logits, int dtype, int64_t rows, int
                                 void* grad, int64_t grad_stride, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Linear layer fused with the cross-entropy. The Liger-Kernel page above,
+ * Classification, names the fused linear cross-entropy as the kernel this
+ * operation extends with a linear layer; read plainly, the logits are the
+ * output of a bias-free linear layer (a language model head),
+ *   logits = hidden @ weight^T,   hidden (rows, H), weight (V, H),
+ * followed by exactly the cross-entropy of ce_forward (same options, same
+ * outputs, same conventions), and the gradients follow by the chain rule
+ * from G = d loss / d logits:
+ *   d loss / d hidden = G @ weight,   d loss / d weight = G^T @ hidden.
+ * The full (rows, V) logits are never held at once: rows are processed in
+ * chunks of chunk_rows; each chunk's logits (fp32) live in the workspace,
+ * are turned into G in place by the fused cross-entropy kernels, and feed
+ * the two gradient products.
+ *
+ * Precision: hidden and weight are bf16; the products accumulate in fp32
+ * (matrix cores, through rocBLAS); the logits and the cross-entropy are
+ * fp32; G is scaled by grad_output and rounded to bf16 (nearest even)
+ * before the two gradient products, whose fp32 results are returned.
+ *
+ * The GEMMs run through rocBLAS: the first call on a device creates that
+ * device's rocBLAS handle (which allocates rocBLAS's own workspace); calls
+ * after that allocate nothing.
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of device workspace ce_linear_forward needs (>= 256), or 0 for
+ * invalid sizes. chunk_rows = 0 picks the default chunk (rows whose fp32
+ * logits and bf16 gradient take at most 6 GiB). */
+size_t ce_linear_workspace_bytes(int64_t rows, int64_t H, int64_t V, int64_t chunk_rows,
+                                 uint32_t flags);
+
+/* Forward of cross_entropy(hidden @ weight^T) and, when grad_hidden or
+ * grad_weight is given, its gradients.
+ *  hidden     [device] bf16 (rows, ld_hidden) row-major, first H used.
+ *  weight     [device] bf16 (V, ld_weight) row-major (out x in), first H used.
+ *  target, class_weight, ignore_index, label_smoothing, lse_square_scale,
+ *  softcap, reduction, loss, z_loss, token_accuracy, argmax, counts
+ *             as for ce_forward (class_weight: per-class weights, (V,)).
+ *  flags      CE_F_CHECK_TARGETS and the kernel-path test hooks of
+ *             ce_forward; CE_F_GRAD is implied by a gradient output.
+ *  grad_output [device] fp32: one value, or rows values when per_row != 0;
+ *             NULL = 1. The gradients are those of grad_output * loss (per
+ *             row for reduction none).
+ *  grad_hidden [device] fp32 (rows, ld_grad_hidden), or NULL; overwritten.
+ *  grad_weight [device] fp32 (V, ld_grad_weight), or NULL; overwritten.
+ *  chunk_rows rows per chunk (> 0), or 0 for the default; the workspace
+ *             must have been sized with the same value.
+ *  workspace  [device] >= ce_linear_workspace_bytes(...) bytes, 256-byte
+ *             aligned, zero-filled before its first use; reusable as for
+ *             ce_forward.
+ * Errors as ce_forward; CE_E_DTYPE if dtype is not CE_BF16; CE_E_SHAPE also
+ * for H < 1 or a leading dimension below H. */
+ce_status ce_linear_forward(const void* hidden, int64_t ld_hidden, const void* weight,
+                            int64_t ld_weight, int dtype, int64_t rows, int64_t H, int64_t V,
+                            const int64_t* target, const float* class_weight,
+                            int64_t ignore_index, float label_smoothing, float lse_square_scale,
+                            float softcap, int reduction, uint32_t flags,
+                            const float* grad_output, int per_row, int64_t chunk_rows,
+                            float* loss, float* z_loss, float* token_accuracy, int64_t* argmax,
+                            int64_t* counts, float* grad_hidden, int64_t ld_grad_hidden,
+                            float* grad_weight, int64_t ld_grad_weight, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
 /* Static, human-readable text of a ce_status value. */
 const char* ce_status_string(int status);
 

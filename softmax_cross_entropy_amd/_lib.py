@@ -64,6 +64,12 @@ _SIGNATURES = {
                                              ctypes.c_float, ctypes.c_float, ctypes.c_float,
                                              ctypes.c_int, _P, _P, ctypes.c_int, _P, _I64, _P,
                                              ctypes.c_size_t, _P]),
+    "ce_linear_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64, _I64, ctypes.c_uint32]),
+    "ce_linear_forward": (ctypes.c_int, [_P, _I64, _P, _I64, ctypes.c_int, _I64, _I64, _I64,
+                                         _P, _P, _I64, ctypes.c_float, ctypes.c_float,
+                                         ctypes.c_float, ctypes.c_int, ctypes.c_uint32, _P,
+                                         ctypes.c_int, _I64, _P, _P, _P, _P, _P, _P, _I64, _P,
+                                         _I64, _P, ctypes.c_size_t, _P]),
     "ce_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 SYMBOLS = tuple(_SIGNATURES)
@@ -144,6 +150,27 @@ def ce_backward(grad: int, dtype: int, rows: int, V: int, row_stride: int, grad_
                 per_row: int, stream: int) -> int:
     """Raw call; returns the ce_status (0 = CE_OK)."""
     return int(lib().ce_backward(grad, dtype, rows, V, row_stride, grad_output, per_row, stream))
+
+
+def ce_linear_workspace_bytes(rows: int, H: int, V: int, chunk_rows: int, flags: int) -> int:
+    return int(lib().ce_linear_workspace_bytes(rows, H, V, chunk_rows, flags))
+
+
+def ce_linear_forward(hidden: int, ld_hidden: int, weight: int, ld_weight: int, dtype: int,
+                      rows: int, H: int, V: int, target: int, class_weight: int,
+                      ignore_index: int, label_smoothing: float, lse_square_scale: float,
+                      softcap: float, reduction: int, flags: int, grad_output: int,
+                      per_row: int, chunk_rows: int, loss: int, z_loss: int,
+                      token_accuracy: int, argmax: int, counts: int, grad_hidden: int,
+                      ld_grad_hidden: int, grad_weight: int, ld_grad_weight: int,
+                      workspace: int, workspace_bytes: int, stream: int) -> int:
+    """Raw call; returns the ce_status (0 = CE_OK)."""
+    return int(lib().ce_linear_forward(hidden, ld_hidden, weight, ld_weight, dtype, rows, H, V,
+                                       target, class_weight, ignore_index, label_smoothing,
+                                       lse_square_scale, softcap, reduction, flags, grad_output,
+                                       per_row, chunk_rows, loss, z_loss, token_accuracy, argmax,
+                                       counts, grad_hidden, ld_grad_hidden, grad_weight,
+                                       ld_grad_weight, workspace, workspace_bytes, stream))
 
 
 def check(status: int, where: str) -> None:

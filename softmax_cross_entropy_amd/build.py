@@ -25,8 +25,10 @@ LIB_NAME = "libce_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
-SOURCES = ["ce_api.hip", "ce_inst_f32.hip", "ce_inst_bf16.hip", "ce_inst_f32_wide.hip",
-           "ce_inst_bf16_wide.hip"]
+SOURCES = ["ce_api.hip", "ce_linear.hip", "ce_inst_f32.hip", "ce_inst_bf16.hip",
+           "ce_inst_f32_wide.hip", "ce_inst_bf16_wide.hip"]
+# rocBLAS runs the products of the linear layer fused with the cross-entropy.
+LINK_FLAGS = ["-lrocblas", "-Wl,-rpath,/opt/rocm/lib"]
 
 # -ffp-contract=off: every fused multiply-add in the kernels is written out
 # explicitly, so a value computed in two places (e.g. the target logit and
@@ -73,7 +75,7 @@ def build(jobs: int = 0, verbose: bool = False) -> str:
         for f in [ex.submit(_run, c, verbose) for c in cmds]:
             f.result()
     tmp = LIB_PATH + ".tmp"
-    _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
+    _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, *LINK_FLAGS, "-o", tmp], verbose)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

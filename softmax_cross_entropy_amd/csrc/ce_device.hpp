@@ -208,7 +208,9 @@ struct Params {
   double one_minus_eps, eps_over_v, lam_d;  // host-computed row-invariant terms
   int reduction;                       // 0 none, 1 mean, 2 sum
   int grad;                            // write d loss / d logits in place
-  int epilogue;                        // run the last-block reduction
+  int epilogue;                        // publish per-row values, run the last-block reduction
+  int no_reduce;                       // epilogue: publish and arrive only (a later launch
+                                       // reduces, e.g. over several row chunks)
   int has_hdr;                         // the prologue ran: scales, W and D are in hdr
   float* loss;
   float* z_loss;
@@ -448,6 +450,17 @@ __device__ __forceinline__ void epilogue_reduce(const Params& p) {
       p.counts[1] = nc;
     }
     p.hdr->done = 0u;
+  }
+}
+
+// The last block's work: the reduction, or with no_reduce only the reset of
+// the arrival counter (the per-row values stay for a later reduction).
+template <int BLOCK>
+__device__ __forceinline__ void epilogue_finish(const Params& p) {
+  if (p.no_reduce) {
+    if (threadIdx.x == 0) p.hdr->done = 0u;
+  } else {
+    epilogue_reduce<BLOCK>(p);
   }
 }
 

@@ -717,7 +717,7 @@ __global__ __launch_bounds__(BLOCK) void rows_kernel(Params p) {
   if (p.epilogue) {
     if (threadIdx.x == 0) s_last = arrive(p, static_cast<uint32_t>(G));
     __syncthreads();
-    if (s_last) epilogue_reduce<BLOCK>(p);
+    if (s_last) epilogue_finish<BLOCK>(p);
   }
 }
 
@@ -861,7 +861,7 @@ __global__ __launch_bounds__(BLOCK) void splitv_finish_kernel(Params p) {
     }
     if (p.epilogue) {
       __syncthreads();
-      if (s_last0) epilogue_reduce<BLOCK>(p);
+      if (s_last0) epilogue_finish<BLOCK>(p);
     }
     return;
   }
@@ -931,7 +931,7 @@ __global__ __launch_bounds__(BLOCK) void splitv_finish_kernel(Params p) {
   }
   if (p.epilogue) {
     __syncthreads();
-    if (s_last) epilogue_reduce<BLOCK>(p);
+    if (s_last) epilogue_finish<BLOCK>(p);
   }
 }
 
@@ -964,7 +964,7 @@ __global__ __launch_bounds__(BLOCK) void row_scalar_kernel(Params p) {
     }
     if (p.epilogue) {
       __syncthreads();
-      if (s_last0) epilogue_reduce<BLOCK>(p);
+      if (s_last0) epilogue_finish<BLOCK>(p);
     }
     return;
   }
@@ -1002,7 +1002,7 @@ __global__ __launch_bounds__(BLOCK) void row_scalar_kernel(Params p) {
   }
   if (p.epilogue) {
     __syncthreads();
-    if (s_last) epilogue_reduce<BLOCK>(p);
+    if (s_last) epilogue_finish<BLOCK>(p);
   }
 }
 

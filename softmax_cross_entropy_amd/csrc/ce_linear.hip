@@ -1,0 +1,292 @@
+// C ABI of the linear layer fused with the cross-entropy (declared in
+// include/ce.h): logits = hidden @ weight^T in row chunks (rocBLAS, bf16 in,
+// fp32 out on the matrix cores), the fused cross-entropy kernels on each
+// chunk's fp32 logits (gradient in place), the gradient narrowed to bf16,
+// and the two gradient products d hidden = G @ weight, d weight = G^T @
+// hidden. The Liger-Kernel page "Kernel Profile: CrossEntropy (Tier 3 -
+// Fused/Complex)", Classification, names this fusion as the one the
+// cross-entropy kernel extends with a linear layer.
+#include <rocblas/rocblas.h>
+
+#include <mutex>
+
+#include "ce_plan.hpp"
+
+#define CE_API extern "C" __attribute__((visibility("default")))
+
+using namespace ceplan;
+
+namespace {
+
+// Default chunk: the fp32 logits and the bf16 gradient of a chunk take at
+// most this many bytes (MI355X has 288 GB of HBM; bigger chunks keep the
+// gradient products wide, which they need to run near the matrix peak).
+constexpr size_t kDefaultChunkBytes = size_t{6} << 30;
+constexpr int kNarrowBlock = 256;
+constexpr int kNarrowUnroll = 4;
+constexpr int kEpilogueBlock = 1024;
+
+// G (fp32 rows of ldl) times grad_output, rounded to bf16 (nearest even)
+// into rows of ldg. One 16-byte vector of G -> one 8-byte vector of bf16;
+// the padding columns past V are converted too and never read.
+__global__ __launch_bounds__(kNarrowBlock) void grad_narrow_kernel(
+    const float* __restrict__ g, int64_t ldl, uint32_t* __restrict__ out, int64_t ldg,
+    int64_t nv4, const float* go, int per_row) {
+  const int64_t r = blockIdx.y;
+  const float s = go ? (per_row ? go[r] : go[0]) : 1.0f;
+  const cedev::f4* src = reinterpret_cast<const cedev::f4*>(g + r * ldl);
+  uint32_t* dst = out + r * (ldg / 2);
+  const int64_t j0 = (static_cast<int64_t>(blockIdx.x) * kNarrowUnroll) * kNarrowBlock + threadIdx.x;
+  cedev::f4 v[kNarrowUnroll];
+#pragma unroll
+  for (int u = 0; u < kNarrowUnroll; ++u) {
+    const int64_t j = j0 + u * kNarrowBlock;
+    v[u] = j < nv4 ? __builtin_nontemporal_load(src + j) : cedev::f4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+#pragma unroll
+  for (int u = 0; u < kNarrowUnroll; ++u) {
+    const int64_t j = j0 + u * kNarrowBlock;
+    if (j < nv4) {
+      dst[2 * j] = cedev::pack_bf16x2(v[u][0] * s, v[u][1] * s);
+      dst[2 * j + 1] = cedev::pack_bf16x2(v[u][2] * s, v[u][3] * s);
+    }
+  }
+}
+
+// grad_weight = 0 for an empty batch (no chunk runs the weight product).
+__global__ __launch_bounds__(256) void zero_rows_kernel(float* a, int64_t rows, int64_t cols,
+                                                        int64_t ld) {
+  for (int64_t r = blockIdx.y; r < rows; r += gridDim.y)
+    for (int64_t k = blockIdx.x * 256ll + threadIdx.x; k < cols; k += gridDim.x * 256ll)
+      a[r * ld + k] = 0.0f;
+}
+
+// The reductions over every row of every chunk, after the last chunk.
+__global__ __launch_bounds__(kEpilogueBlock) void linear_epilogue_kernel(cedev::Params p) {
+  cedev::epilogue_reduce<kEpilogueBlock>(p);
+}
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+struct LinLayout {
+  int64_t C;        // rows per chunk
+  int64_t ldl;      // fp32 logits row stride (16-byte rows)
+  int64_t ldg;      // bf16 gradient row stride (16-byte rows)
+  size_t row_ce, row_z, row_ok, part, logits, gbuf, total;
+};
+
+// Workspace: the cross-entropy header and per-row arrays for every row,
+// partials for one chunk (the larger of a full and the last chunk's plan),
+// then one chunk of fp32 logits and one of bf16 gradient.
+LinLayout lin_layout(int64_t rows, int64_t V, int64_t chunk_rows, uint32_t flags) {
+  LinLayout L;
+  L.ldl = round_up(V, 4);
+  L.ldg = round_up(V, 8);
+  const int64_t per_row = L.ldl * 4 + L.ldg * 2;
+  int64_t C = chunk_rows > 0 ? chunk_rows
+                             : static_cast<int64_t>(kDefaultChunkBytes / static_cast<size_t>(per_row));
+  if (C < 1) C = 1;
+  if (C > rows) C = rows;
+  L.C = C;
+  int64_t parts = 0;
+  if (rows > 0) {
+    const int64_t sizes[2] = {C, rows % C};
+    for (int64_t c : sizes) {
+      if (c <= 0) continue;
+      Plan pl;
+      plan_aligned(c, V, CE_F32, flags, &pl);
+      const int64_t q = c * plan_partials(pl);
+      parts = q > parts ? q : parts;
+    }
+  }
+  size_t off = kAlign;  // header
+  L.row_ce = off;
+  off += align_up(static_cast<size_t>(rows) * 4);
+  L.row_z = off;
+  off += align_up(static_cast<size_t>(rows) * 4);
+  L.row_ok = off;
+  off += align_up(static_cast<size_t>(rows) * 4);
+  L.part = off;
+  off += align_up(static_cast<size_t>(parts) * sizeof(cedev::Partial));
+  L.logits = off;
+  off += align_up(static_cast<size_t>(C) * static_cast<size_t>(L.ldl) * 4);
+  L.gbuf = off;
+  off += align_up(static_cast<size_t>(C) * static_cast<size_t>(L.ldg) * 2);
+  L.total = off;
+  return L;
+}
+
+// One rocBLAS handle per device, created on first use; calls that share it
+// set its stream and enqueue their products under the lock.
+constexpr int kMaxDevices = 64;
+std::mutex g_blas_mu;
+rocblas_handle g_blas[kMaxDevices] = {};
+
+rocblas_handle blas_handle(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  if (g_blas[dev] == nullptr) {
+    rocblas_handle h = nullptr;
+    if (rocblas_create_handle(&h) != rocblas_status_success) return nullptr;
+    g_blas[dev] = h;
+  }
+  return g_blas[dev];
+}
+
+// Column-major GEMM D = op(A) op(B) + beta D, bf16 inputs, fp32 output and
+// accumulation (the row-major products are written as their transposes).
+bool gemm_bf16_f32(rocblas_handle h, rocblas_operation ta, rocblas_operation tb, int64_t m,
+                   int64_t n, int64_t k, const void* A, int64_t lda, const void* B, int64_t ldb,
+                   float beta, float* D, int64_t ldd) {
+  const float alpha = 1.0f;
+  const rocblas_status st = rocblas_gemm_ex(
+      h, ta, tb, static_cast<rocblas_int>(m), static_cast<rocblas_int>(n),
+      static_cast<rocblas_int>(k), &alpha, A, rocblas_datatype_bf16_r,
+      static_cast<rocblas_int>(lda), B, rocblas_datatype_bf16_r, static_cast<rocblas_int>(ldb),
+      &beta, D, rocblas_datatype_f32_r, static_cast<rocblas_int>(ldd), D,
+      rocblas_datatype_f32_r, static_cast<rocblas_int>(ldd), rocblas_datatype_f32_r,
+      rocblas_gemm_algo_standard, 0, 0);
+  return st == rocblas_status_success;
+}
+
+}  // namespace
+
+CE_API size_t ce_linear_workspace_bytes(int64_t rows, int64_t H, int64_t V, int64_t chunk_rows,
+                                        uint32_t flags) {
+  if (!valid_shape(rows, V, V) || H < 1 || H > kMaxInt || chunk_rows < 0) return 0;
+  return lin_layout(rows, V, chunk_rows, flags).total;
+}
+
+CE_API ce_status ce_linear_forward(const void* hidden, int64_t ld_hidden, const void* weight,
+                                   int64_t ld_weight, int dtype, int64_t rows, int64_t H,
+                                   int64_t V, const int64_t* target, const float* class_weight,
+                                   int64_t ignore_index, float label_smoothing,
+                                   float lse_square_scale, float softcap, int reduction,
+                                   uint32_t flags, const float* grad_output, int per_row,
+                                   int64_t chunk_rows, float* loss, float* z_loss,
+                                   float* token_accuracy, int64_t* argmax, int64_t* counts,
+                                   float* grad_hidden, int64_t ld_grad_hidden,
+                                   float* grad_weight, int64_t ld_grad_weight, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  if (dtype != CE_BF16) return CE_E_DTYPE;
+  const ce_status bad = check_options(CE_F32, rows, V, V, label_smoothing, lse_square_scale,
+                                      softcap, reduction);
+  if (bad != CE_OK) return bad;
+  if (H < 1 || H > kMaxInt || chunk_rows < 0) return CE_E_SHAPE;
+  if (ld_hidden < H || ld_weight < H || ld_hidden > kMaxInt || ld_weight > kMaxInt)
+    return CE_E_SHAPE;
+  if (grad_hidden && (ld_grad_hidden < H || ld_grad_hidden > kMaxInt)) return CE_E_SHAPE;
+  if (grad_weight && (ld_grad_weight < H || ld_grad_weight > kMaxInt)) return CE_E_SHAPE;
+  if (round_up(V, 8) > kMaxInt) return CE_E_SHAPE;
+  if (loss == nullptr) return CE_E_NULL;
+  if (rows > 0 && (hidden == nullptr || target == nullptr || weight == nullptr)) return CE_E_NULL;
+  if (per_row && reduction != CE_RED_NONE) return CE_E_PARAM;
+  const bool want_grad = grad_hidden != nullptr || grad_weight != nullptr;
+  const LinLayout L = lin_layout(rows, V, chunk_rows, flags);
+  if (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
+    return CE_E_WORKSPACE;
+  if (workspace_bytes < L.total) return CE_E_WORKSPACE;
+
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return CE_E_HIP;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  std::lock_guard<std::mutex> lock(g_blas_mu);
+  rocblas_handle blas = blas_handle(dev);
+  if (blas == nullptr || rocblas_set_stream(blas, st) != rocblas_status_success) return CE_E_HIP;
+
+  char* ws = static_cast<char*>(workspace);
+  float* logits = reinterpret_cast<float*>(ws + L.logits);
+  uint32_t* gbuf = reinterpret_cast<uint32_t*>(ws + L.gbuf);
+  cedev::Params base;
+  fill_options(base, logits, rows, V, L.ldl, target, class_weight, ignore_index,
+               label_smoothing, lse_square_scale, softcap, reduction);
+  base.grad = want_grad ? 1 : 0;
+  base.epilogue = (reduction != CE_RED_NONE || counts != nullptr) ? 1 : 0;
+  base.has_hdr = (reduction == CE_RED_MEAN || (class_weight != nullptr && label_smoothing > 0.0f) ||
+                  (flags & CE_F_CHECK_TARGETS) || rows == 0)
+                     ? 1
+                     : 0;
+  base.loss = loss;
+  base.z_loss = z_loss;
+  base.acc = token_accuracy;
+  base.argmax = argmax;
+  base.counts = counts;
+  base.hdr = reinterpret_cast<cedev::Header*>(ws);
+  base.row_ce = reinterpret_cast<float*>(ws + L.row_ce);
+  base.row_z = reinterpret_cast<float*>(ws + L.row_z);
+  base.row_ok = reinterpret_cast<int32_t*>(ws + L.row_ok);
+  base.part = reinterpret_cast<cedev::Partial*>(ws + L.part);
+
+  // n, D and the mean scales over the whole batch, before any gradient.
+  if (base.has_hdr && cehost::launch_prologue(base, st) != hipSuccess) return CE_E_HIP;
+
+  const uint32_t path_flags =
+      flags & (CE_F_FORCE_FUSED | CE_F_FORCE_SPLITV | CE_F_FORCE_SCALAR | CE_F_SHAPE_ALT);
+  const char* hid = static_cast<const char*>(hidden);
+  for (int64_t c0 = 0; c0 < rows; c0 += L.C) {
+    const int64_t cr = rows - c0 < L.C ? rows - c0 : L.C;
+    const void* xc = hid + c0 * ld_hidden * 2;
+    // logits (cr x V, row-major) = hidden_chunk @ weight^T
+    if (!gemm_bf16_f32(blas, rocblas_operation_transpose, rocblas_operation_none, V, cr, H, weight,
+                       ld_weight, xc, ld_hidden, 0.0f, logits, L.ldl))
+      return CE_E_HIP;
+    cedev::Params pc = base;
+    pc.rows = cr;
+    pc.target = target + c0;
+    pc.row_ce = base.row_ce + c0;
+    pc.row_z = base.row_z + c0;
+    pc.row_ok = base.row_ok + c0;
+    if (reduction == CE_RED_NONE) {
+      pc.loss = loss + c0;
+      if (z_loss) pc.z_loss = z_loss + c0;
+      if (token_accuracy) pc.acc = token_accuracy + c0;
+    }
+    if (argmax) pc.argmax = argmax + c0;
+    pc.counts = nullptr;
+    pc.no_reduce = 1;  // per-row values only; one reduction after the last chunk
+    Plan pl;
+    make_plan(logits, CE_F32, cr, V, L.ldl, class_weight, label_smoothing, path_flags, &pl);
+    pc.S = pl.S;
+    pc.chunk_vec = pl.chunk_vec;
+    pc.epoch = next_epoch();
+    if (cehost::launch_forward_f32(pl, pc, st) != hipSuccess) return CE_E_HIP;
+    if (!want_grad) continue;
+    const int64_t nv4 = L.ldl / 4;
+    const dim3 ngrid(static_cast<unsigned>((nv4 + kNarrowBlock * kNarrowUnroll - 1) /
+                                           (kNarrowBlock * kNarrowUnroll)),
+                     static_cast<unsigned>(cr));
+    grad_narrow_kernel<<<ngrid, kNarrowBlock, 0, st>>>(
+        logits, L.ldl, gbuf, L.ldg, nv4, grad_output ? grad_output + (per_row ? c0 : 0) : nullptr,
+        per_row);
+    if (hipGetLastError() != hipSuccess) return CE_E_HIP;
+    // d hidden_chunk (cr x H) = G_chunk @ weight
+    if (grad_hidden &&
+        !gemm_bf16_f32(blas, rocblas_operation_none, rocblas_operation_none, H, cr, V, weight,
+                       ld_weight, gbuf, L.ldg, 0.0f, grad_hidden + c0 * ld_grad_hidden,
+                       ld_grad_hidden))
+      return CE_E_HIP;
+    // d weight (V x H) (+)= G_chunk^T @ hidden_chunk
+    if (grad_weight &&
+        !gemm_bf16_f32(blas, rocblas_operation_none, rocblas_operation_transpose, H, V, cr, xc,
+                       ld_hidden, gbuf, L.ldg, c0 == 0 ? 0.0f : 1.0f, grad_weight, ld_grad_weight))
+      return CE_E_HIP;
+  }
+  if (rows == 0 && grad_weight) {
+    const dim3 zg(static_cast<unsigned>((H + 255) / 256),
+                  static_cast<unsigned>(V < 65535 ? V : 65535));
+    zero_rows_kernel<<<zg, 256, 0, st>>>(grad_weight, V, H, ld_grad_weight);
+    if (hipGetLastError() != hipSuccess) return CE_E_HIP;
+  }
+  if (base.epilogue && rows > 0) {
+    linear_epilogue_kernel<<<1, kEpilogueBlock, 0, st>>>(base);
+    if (hipGetLastError() != hipSuccess) return CE_E_HIP;
+  }
+  if (flags & CE_F_CHECK_TARGETS) {
+    uint32_t err = 0;
+    if (hipMemcpyAsync(&err, &base.hdr->err, sizeof(err), hipMemcpyDeviceToHost, st) != hipSuccess)
+      return CE_E_HIP;
+    if (hipStreamSynchronize(st) != hipSuccess) return CE_E_HIP;
+    if (err & 1u) return CE_E_TARGET_RANGE;
+    if (err & 2u) return CE_E_HIP;  // a row pair whose partner never published
+  }
+  return CE_OK;
+}

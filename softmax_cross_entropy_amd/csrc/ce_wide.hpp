@@ -444,7 +444,7 @@ __global__ __launch_bounds__(kWideBlock) void wide_kernel(Params p) {
   if (p.epilogue) {
     if (threadIdx.x == 0) s_last = arrive(p, gridDim.x);
     __syncthreads();
-    if (s_last) epilogue_reduce<kWideBlock>(p);
+    if (s_last) epilogue_finish<kWideBlock>(p);
   }
 }
 

@@ -1,0 +1,199 @@
+"""GPU parity of the linear layer fused with the cross-entropy
+(ce_linear_forward through the C ABI) against the float64 oracle
+(oracle/linear_oracle.py).
+
+Tolerances, derived from the arithmetic of the HIP path (bf16 inputs, fp32
+products and cross-entropy, G rounded to bf16 before the gradient products):
+  * logits: |dz_ik| <= H 2^-24 (|hidden| @ |weight|^T)_ik (fp32 accumulation
+    of exact bf16 products), so a row's loss moves by at most 2 max_k dz_ik
+    (its log-sum-exp and its target logit), plus the cross-entropy's own
+    1e-5 relative bar;
+  * gradients: G rounded to bf16 moves each term of d hidden = G @ weight
+    and d weight = G^T @ hidden by at most 2^-9 of its magnitude, and the
+    fp32 sums add at most K 2^-24 of it, so |error| <= (2^-8 + K 2^-24) M
+    with M = |G| @ |weight| (resp. |G|^T @ |hidden|), plus 1e-7.
+Where the two largest logits of a row are closer than their error bound
+the argmax may pick either; it must then be one of the candidates.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import grad_magnitudes, linear_forward
+from softmax_cross_entropy_amd import linear_cross_entropy, linear_forward_raw
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _announce(**kw):
+    print("CASE " + " ".join(f"{k}={v}" for k, v in kw.items()), flush=True)
+
+
+def _bits(a: torch.Tensor) -> np.ndarray:
+    return a.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def _make(rows, H, V, seed, n_ignored):
+    g = torch.Generator().manual_seed(seed)
+    x = (torch.randn(rows, H, generator=g) * 0.5).to(torch.bfloat16)
+    w = (torch.randn(V, H, generator=g) * (2.0 / H ** 0.5)).to(torch.bfloat16)
+    t = synth.make_targets(rows, V, seed, n_ignored)
+    return x, w, t
+
+
+def _check(x, w, t, res, *, cw=None, eps=0.0, lam=0.0, softcap=None, reduction="mean",
+           grad_scale=None, what=""):
+    loss, zl, acc, am, cnt, gh, gw = res
+    rows, H = x.shape
+    V = w.shape[0]
+    ref = linear_forward(_bits(x), _bits(w), t.numpy(),
+                         class_weight=None if cw is None else cw.numpy(), label_smoothing=eps,
+                         lse_square_scale=lam, softcap=softcap, reduction=reduction)
+    r = ref.ce
+    counted = (t.numpy() != -100)
+    # logits error bound per row, and the loss bound it implies: the row's
+    # log-sum-exp and target logit each move by at most dz; the z-loss
+    # lam lse^2 by at most 2 lam |lse| dz with |lse| <= max |z| + ln V
+    dz = H * 2.0 ** -24 * ref.logits_abs.max(axis=1)
+    row_bound = 2.0 * dz
+    if lam > 0.0:
+        lse_max = np.abs(ref.logits).max(axis=1) + np.log(V)
+        row_bound = row_bound + 2.0 * lam * lse_max * dz
+    row_bound = np.where(counted, row_bound, 0.0)
+    if reduction == "none":
+        got = loss.cpu().double().numpy()
+        want = np.asarray(r.loss, dtype=np.float64)
+        tol = 1e-5 * np.abs(want) + row_bound + 1e-7
+        assert np.all(np.abs(got - want) <= tol), (what, np.max(np.abs(got - want) - tol))
+    else:
+        scale = 1.0 / r.D if reduction == "mean" else 1.0
+        want = float(r.loss)
+        tol = 1e-5 * abs(want) + scale * row_bound.sum() + 1e-7
+        assert abs(loss.item() - want) <= tol, (what, loss.item(), want, tol)
+    # argmax: exact where the top two logits are farther apart than the bound
+    srt = np.sort(ref.logits, axis=1)
+    gap = srt[:, -1] - srt[:, -2] if V > 1 else np.full(rows, np.inf)
+    am_g = am.cpu().numpy()
+    for i in range(rows):
+        if not counted[i]:
+            assert am_g[i] == -1
+        elif gap[i] > 2.0 * dz[i]:
+            assert am_g[i] == r.argmax[i], (what, i)
+        else:
+            assert ref.logits[i, am_g[i]] >= srt[i, -1] - 2.0 * dz[i], (what, i)
+    c = cnt.cpu().numpy()
+    assert int(c[0]) == r.n_valid
+    assert int(c[1]) == int(np.sum((am_g == t.numpy()) & counted))
+    if gh is None:
+        return
+    G = r.grad if grad_scale is None else r.grad * np.asarray(grad_scale).reshape(-1, 1)
+    m_h, m_w = grad_magnitudes(_bits(x), _bits(w), G)
+    xf = (_bits(x).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    wf = (_bits(w).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    want_h = G @ wf
+    want_w = G.T @ xf
+    got_h = gh.cpu().double().numpy()
+    got_w = gw.cpu().double().numpy()
+    tol_h = (2.0 ** -8 + V * 2.0 ** -24) * m_h + 1e-7
+    tol_w = (2.0 ** -8 + rows * 2.0 ** -24) * m_w + 1e-7
+    eh = np.abs(got_h - want_h) - tol_h
+    ew = np.abs(got_w - want_w) - tol_w
+    assert np.all(eh <= 0), (what, "grad_hidden", float(eh.max()))
+    assert np.all(ew <= 0), (what, "grad_weight", float(ew.max()))
+    assert np.all(got_h[~counted] == 0.0), (what, "ignored rows")
+
+
+OPTS = {
+    "plain": dict(),
+    "smooth_weight": dict(eps=0.1, cw=True),
+    "softcap_zloss": dict(softcap=5.0, lam=1e-3),
+    "all": dict(eps=0.2, cw=True, softcap=3.0, lam=1e-2),
+}
+
+
+@pytest.mark.parametrize("opt", list(OPTS))
+@pytest.mark.parametrize("reduction", ["mean", "sum", "none"])
+@pytest.mark.parametrize("shape,chunk", [((37, 64, 3001), 0), ((300, 96, 4096), 64),
+                                         ((130, 128, 8000), 29)])
+def test_linear_parity(opt, reduction, shape, chunk):
+    rows, H, V = shape
+    o = OPTS[opt]
+    x, w, t = _make(rows, H, V, rows + V, rows // 6)
+    cw = (0.5 + 1.5 * torch.rand(V, generator=torch.Generator().manual_seed(V))
+          if o.get("cw") else None)
+    _announce(name="linear", rows=rows, H=H, V=V, chunk=chunk, opt=opt, reduction=reduction)
+    res = linear_forward_raw(x.to(DEV), w.to(DEV), t.to(DEV),
+                             None if cw is None else cw.to(DEV), -100, o.get("eps", 0.0),
+                             o.get("lam", 0.0), o.get("softcap"), reduction, grad=True,
+                             z_loss=True, token_accuracy=True, argmax=True, counts=True,
+                             chunk_rows=chunk)
+    torch.cuda.synchronize()
+    _check(x, w, t, res, cw=cw, eps=o.get("eps", 0.0), lam=o.get("lam", 0.0),
+           softcap=o.get("softcap"), reduction=reduction, what=f"{opt}/{reduction}/{shape}")
+
+
+@pytest.mark.parametrize("reduction", ["mean", "none"])
+def test_linear_autograd_grad_output(reduction):
+    """loss.backward(grad_output): mean scales the forward's gradients; none
+    recomputes them with the per-row grad_output."""
+    rows, H, V = 64, 64, 5000
+    x, w, t = _make(rows, H, V, 77, 8)
+    _announce(name="linear-autograd", rows=rows, H=H, V=V, reduction=reduction)
+    xd = x.to(DEV).requires_grad_(True)
+    wd = w.to(DEV).requires_grad_(True)
+    out = linear_cross_entropy(xd, wd, t.to(DEV), label_smoothing=0.1, reduction=reduction,
+                               chunk_rows=24)
+    if reduction == "none":
+        go = torch.linspace(0.5, 2.0, rows)
+        out.loss.backward(go.to(DEV))
+        scale = go.double().numpy()
+    else:
+        out.loss.backward(torch.tensor(2.5, device=DEV))
+        scale = np.full(rows, 2.5)
+    torch.cuda.synchronize()
+    ref = linear_forward(_bits(x), _bits(w), t.numpy(), label_smoothing=0.1, reduction=reduction)
+    G = ref.ce.grad * scale.reshape(-1, 1)
+    m_h, m_w = grad_magnitudes(_bits(x), _bits(w), G)
+    xf = (_bits(x).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    wf = (_bits(w).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    # the returned gradients are rounded to the parameters' dtype (bf16)
+    gh = xd.grad.double().cpu().numpy()
+    gw = wd.grad.double().cpu().numpy()
+    want_h, want_w = G @ wf, G.T @ xf
+    tol_h = (2.0 ** -7 + V * 2.0 ** -24) * m_h + np.abs(want_h) * 2.0 ** -8 + 1e-7
+    tol_w = (2.0 ** -7 + rows * 2.0 ** -24) * m_w + np.abs(want_w) * 2.0 ** -8 + 1e-7
+    assert np.all(np.abs(gh - want_h) <= tol_h)
+    assert np.all(np.abs(gw - want_w) <= tol_w)
+
+
+def test_linear_all_ignored_and_empty():
+    rows, H, V = 16, 32, 1000
+    x, w, _ = _make(rows, H, V, 5, 0)
+    t = torch.full((rows,), -100, dtype=torch.int64)
+    _announce(name="linear-all-ignored", rows=rows)
+    loss, _, _, _, cnt, gh, gw = linear_forward_raw(x.to(DEV), w.to(DEV), t.to(DEV), counts=True)
+    torch.cuda.synchronize()
+    assert torch.isnan(loss).item()
+    assert int(cnt[0]) == 0
+    assert torch.count_nonzero(gh).item() == 0 and torch.count_nonzero(gw).item() == 0
+    _announce(name="linear-empty", rows=0)
+    loss, _, _, _, cnt, gh, gw = linear_forward_raw(
+        x[:0].to(DEV), w.to(DEV), t[:0].to(DEV), counts=True)
+    torch.cuda.synchronize()
+    assert torch.isnan(loss).item() and int(cnt[0]) == 0
+    assert gh.numel() == 0 and torch.count_nonzero(gw).item() == 0
+
+
+def test_linear_medium_default_chunk():
+    """512 x 1024 hidden, V = 32000 (one default chunk), mean, every output."""
+    rows, H, V = 512, 1024, 32000
+    x, w, t = _make(rows, H, V, 123, 25)
+    _announce(name="linear-medium", rows=rows, H=H, V=V)
+    res = linear_forward_raw(x.to(DEV), w.to(DEV), t.to(DEV), label_smoothing=0.1,
+                             lse_square_scale=1e-4, z_loss=True, token_accuracy=True,
+                             argmax=True, counts=True)
+    torch.cuda.synchronize()
+    _check(x, w, t, res, eps=0.1, lam=1e-4, what="medium")
