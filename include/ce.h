@@ -79,9 +79,10 @@ enum {
   CE_F_FORCE_FUSED = 1u << 5,   /* test hooks: pick the kernel path            */
   CE_F_FORCE_SPLITV = 1u << 6,
   CE_F_FORCE_SCALAR = 1u << 7,
-  CE_F_SHAPE_ALT = 1u << 8      /* test hook: rows of 8 K to 32 K 16-byte      */
-                                /* vectors take the 512-thread fused layouts   */
-                                /* instead of the 1024-thread ones             */
+  CE_F_SHAPE_ALT = 1u << 8      /* test hook: the other fused layout where a   */
+                                /* row size has two (rows of 2 K to 32 K       */
+                                /* 16-byte vectors: 1024-thread workgroups vs  */
+                                /* 256/512-thread ones)                        */
 };
 
 /* Kernel paths (ce_plan_path). */

@@ -3,7 +3,12 @@
 #include "ce_launch_impl.hpp"
 
 namespace cehost {
-hipError_t launch_wide_f32(int halves, const cedev::Params& p, hipStream_t st) {
-  return halves == 2 ? launch_wide_h<cedev::F32, 2>(p, st) : launch_wide_h<cedev::F32, 1>(p, st);
+hipError_t launch_wide_f32(int nreg, int halves, const cedev::Params& p, hipStream_t st) {
+  if (halves == 2) return launch_wide_h<cedev::F32, 16, 2>(p, st);
+  switch (nreg) {
+    case 4: return launch_wide_h<cedev::F32, 4, 1>(p, st);
+    case 8: return launch_wide_h<cedev::F32, 8, 1>(p, st);
+    default: return launch_wide_h<cedev::F32, 16, 1>(p, st);
+  }
 }
 }  // namespace cehost

@@ -15,7 +15,7 @@ struct Shape {
   int block, nreg, nlds, halves;
   int cap() const { return block * (nreg + nlds) * halves; }
 };
-constexpr int kNumShapes = 9;
+constexpr int kNumShapes = 11;
 constexpr Shape kShapes[kNumShapes] = {
     {256, 4, 0, 1},    // 1024 vectors:  16 KiB rows
     {256, 8, 0, 1},    // 2048 vectors:  32 KiB
@@ -26,9 +26,13 @@ constexpr Shape kShapes[kNumShapes] = {
     {512, 44, 19, 1},  // 32256 vectors: 504 KiB (176 VGPRs + 152 KiB LDS)
     {512, 45, 19, 1},  // 32768 vectors: 512 KiB (180 VGPRs + 152 KiB LDS)
     {1024, 16, 0, 2},  // 32768 vectors: 512 KiB (row pair of 1024-thread workgroups)
+    {1024, 4, 0, 1},   // 4096 vectors:  64 KiB (wide_kernel, 16 waves)
+    {1024, 8, 0, 1},   // 8192 vectors: 128 KiB (wide_kernel, 16 waves)
 };
 constexpr int kWideShape = 5;
 constexpr int kPairShape = 8;
+constexpr int kWide4Shape = 9;
+constexpr int kWide8Shape = 10;
 constexpr int kSplitShapeSmall = 0;  // split-V chunk shapes
 constexpr int kSplitShapeLarge = 3;
 constexpr int kSplitBlock = 256;     // block of the split-V second stage
@@ -42,9 +46,10 @@ struct Plan {
 };
 
 hipError_t launch_prologue(const cedev::Params& p, hipStream_t st);
-// wide_kernel with HALVES = halves (1 or 2) workgroups per row.
-hipError_t launch_wide_f32(int halves, const cedev::Params& p, hipStream_t st);
-hipError_t launch_wide_bf16(int halves, const cedev::Params& p, hipStream_t st);
+// wide_kernel with nreg VGPR slots per thread and halves (1 or 2)
+// workgroups per row.
+hipError_t launch_wide_f32(int nreg, int halves, const cedev::Params& p, hipStream_t st);
+hipError_t launch_wide_bf16(int nreg, int halves, const cedev::Params& p, hipStream_t st);
 hipError_t launch_forward_f32(const Plan& plan, const cedev::Params& p, hipStream_t st);
 hipError_t launch_forward_bf16(const Plan& plan, const cedev::Params& p, hipStream_t st);
 hipError_t launch_recompute_f32(const cedev::Params& p, void* grad, int64_t grad_stride,

@@ -57,10 +57,12 @@ hipError_t launch_fused(int shape, const Params& p, hipStream_t st) {
     case 6: return launch_rows<E, SC, SM, 512, 44, 19>(p, st);
     case 7: return launch_rows<E, SC, SM, 512, 45, 19>(p, st);
     case kWideShape:
-    case kPairShape: {
-      const int halves = kShapes[shape].halves;
-      if constexpr (E::EPV == 4) return launch_wide_f32(halves, p, st);
-      return launch_wide_bf16(halves, p, st);
+    case kPairShape:
+    case kWide4Shape:
+    case kWide8Shape: {
+      const int halves = kShapes[shape].halves, nreg = kShapes[shape].nreg;
+      if constexpr (E::EPV == 4) return launch_wide_f32(nreg, halves, p, st);
+      return launch_wide_bf16(nreg, halves, p, st);
     }
     default: return hipErrorInvalidValue;
   }
@@ -68,26 +70,30 @@ hipError_t launch_fused(int shape, const Params& p, hipStream_t st) {
 
 // wide_kernel launch (instantiated in the ce_inst_*_wide units): persistent,
 // at most one workgroup per part.
-template <class E, int HALVES, int SC, int SM>
+template <class E, int NREG, int HALVES, int SC, int SM>
 hipError_t launch_wide_t(const Params& p, hipStream_t st) {
   static int cache[64] = {};
   int r = 0;
   const hipError_t e =
-      resident_blocks(cedev::wide_kernel<E, HALVES, SC, SM>, cedev::kWideBlock, cache, &r);
+      resident_blocks(cedev::wide_kernel<E, NREG, HALVES, SC, SM>, cedev::kWideBlock, cache, &r);
   if (e != hipSuccess) return e;
   const int64_t parts = p.rows * HALVES;
   const int64_t grid = parts < r ? parts : r;
-  cedev::wide_kernel<E, HALVES, SC, SM>
+  cedev::wide_kernel<E, NREG, HALVES, SC, SM>
       <<<dim3(static_cast<unsigned>(grid)), cedev::kWideBlock, 0, st>>>(p);
   return hipGetLastError();
 }
 
-template <class E, int HALVES>
+template <class E, int NREG, int HALVES>
 hipError_t launch_wide_h(const Params& p, hipStream_t st) {
   const bool sc = p.softcap > 0.0f;
   const bool sm = p.eps > 0.0f;
-  if (sc) return sm ? launch_wide_t<E, HALVES, 1, 1>(p, st) : launch_wide_t<E, HALVES, 1, 0>(p, st);
-  return sm ? launch_wide_t<E, HALVES, 0, 1>(p, st) : launch_wide_t<E, HALVES, 0, 0>(p, st);
+  if (sc) {
+    return sm ? launch_wide_t<E, NREG, HALVES, 1, 1>(p, st)
+              : launch_wide_t<E, NREG, HALVES, 1, 0>(p, st);
+  }
+  return sm ? launch_wide_t<E, NREG, HALVES, 0, 1>(p, st)
+            : launch_wide_t<E, NREG, HALVES, 0, 0>(p, st);
 }
 
 template <class E, int SC, int SM>

@@ -61,14 +61,18 @@ inline void split_plan(int64_t rows, int64_t nvec, bool forced, Plan* pl) {
 }
 
 // Fused shape for rows of nvec vectors: the smallest capacity that holds the
-// row. Rows of 8 K to 32 K vectors take the 1024-thread layouts (one
+// row. Rows of 4 K to 32 K vectors take the 1024-thread layouts (one
 // workgroup, or a row pair), measured faster on MI355X than 512-thread
-// workgroups holding the whole row; CE_F_SHAPE_ALT takes the 512-thread
-// layouts instead (a test hook for comparing them). -1: no fused shape.
+// workgroups holding the whole row; rows of up to 4 K vectors stay with
+// 256/512-thread workgroups (a 1024-thread workgroup per 64 KiB row was
+// slower). CE_F_SHAPE_ALT takes the other layout where a row size has two
+// (a test hook for comparing them). -1: no fused shape.
 inline int fused_shape(int64_t nvec, uint32_t flags) {
   const bool alt = (flags & CE_F_SHAPE_ALT) != 0;
-  for (int s = 0; s <= 3; ++s)
+  for (int s = 0; s <= 1; ++s)
     if (nvec <= kShapes[s].cap()) return s;
+  if (nvec <= kShapes[2].cap()) return alt ? cehost::kWide4Shape : 2;
+  if (nvec <= kShapes[3].cap()) return alt ? 3 : cehost::kWide8Shape;
   if (nvec <= kShapes[4].cap()) return alt ? 4 : cehost::kWideShape;
   if (nvec <= kShapes[cehost::kPairShape].cap()) {
     if (!alt) return cehost::kPairShape;

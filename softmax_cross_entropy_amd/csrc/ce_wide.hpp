@@ -27,7 +27,7 @@
 namespace cedev {
 
 constexpr int kWideBlock = 1024;
-constexpr int kWideSlots = 16;
+constexpr int kWideSlots = 16;  // VGPR slots per thread of the largest wide shapes
 // Polls of the partner's partial before a pair gives up and flags the row
 // (each poll is one device-coherent load, about a microsecond); a partner
 // that never arrives would otherwise hold the workgroup forever.
@@ -98,11 +98,10 @@ __device__ __forceinline__ void claim_finish(const Params& p, uint32_t c, WideSh
 }
 
 // One part (a whole row, or half of one) of the persistent wide kernel.
-template <class E, int HALVES, int SC, int SM>
+template <class E, int NREG, int HALVES, int SC, int SM>
 __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
                                           WideShared& sh) {
   constexpr int BLOCK = kWideBlock;
-  constexpr int NREG = kWideSlots;
   constexpr int NW = BLOCK / 64;
   constexpr int EPV = E::EPV;
   constexpr int GS = (EPV == 4) ? 4 : 2;  // slots per pass-1 group
@@ -429,7 +428,7 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
 // once at the epilogue. The next part's loads are issued as soon as the
 // current part's gradient stores are (they drain while the next part
 // arrives).
-template <class E, int HALVES, int SC, int SM>
+template <class E, int NREG, int HALVES, int SC, int SM>
 __global__ __launch_bounds__(kWideBlock) void wide_kernel(Params p) {
   __shared__ WideShared sh;
   __shared__ int s_last;
@@ -437,7 +436,7 @@ __global__ __launch_bounds__(kWideBlock) void wide_kernel(Params p) {
   int64_t t = blockIdx.x;
   int64_t y = p.target[t / HALVES];
   while (t < parts) {
-    wide_part<E, HALVES, SC, SM>(p, t, y, sh);
+    wide_part<E, NREG, HALVES, SC, SM>(p, t, y, sh);
     t = uniform_i64(sh.next_t);
     y = uniform_i64(sh.next_y);
   }
