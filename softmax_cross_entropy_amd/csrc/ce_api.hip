@@ -65,6 +65,16 @@ CE_API ce_status ce_forward(void* logits, int dtype, int64_t rows, int64_t V, in
                (flags & CE_F_CHECK_TARGETS) || rows == 0)
                   ? 1
                   : 0;
+  // A mean whose only batch-wide inputs are n and D (no weighted smoothing,
+  // no target check) on the fused path: every persistent workgroup counts
+  // them itself (a read of the targets from L2) instead of waiting for a
+  // prologue launch. Up to kSelfScaleRows rows, so that read stays small.
+  if (reduction == CE_RED_MEAN && !(weight != nullptr && label_smoothing > 0.0f) &&
+      !(flags & CE_F_CHECK_TARGETS) && rows > 0 && rows <= kSelfScaleRows &&
+      pl.path == CE_PATH_FUSED) {
+    p.has_hdr = 0;
+    p.self_scales = 1;
+  }
   p.loss = loss;
   p.z_loss = z_loss;
   p.acc = token_accuracy;

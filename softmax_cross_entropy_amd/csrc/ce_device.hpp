@@ -211,6 +211,8 @@ struct Params {
   int epilogue;                        // publish per-row values, run the last-block reduction
   int no_reduce;                       // epilogue: publish and arrive only (a later launch
                                        // reduces, e.g. over several row chunks)
+  int self_scales;                     // mean without the prologue: every workgroup counts n
+                                       // and D itself (workgroup 0 also fills the header)
   int has_hdr;                         // the prologue ran: scales, W and D are in hdr
   float* loss;
   float* z_loss;
@@ -436,7 +438,9 @@ __device__ __forceinline__ void epilogue_reduce(const Params& p) {
       ncount += s_cnt[1][w];
     }
     const double n = static_cast<double>(ncount);
-    const double D = p.has_hdr ? p.hdr->D : n;
+    const double D = (p.has_hdr || p.self_scales)
+                         ? __hip_atomic_load(&p.hdr->D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                         : n;
     if (p.reduction == 1) {
       if (p.loss) p.loss[0] = static_cast<float>(tce / D + tz / n);
       if (p.z_loss) p.z_loss[0] = static_cast<float>(tz / n);

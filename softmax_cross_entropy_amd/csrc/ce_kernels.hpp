@@ -233,11 +233,82 @@ __device__ __forceinline__ Acc block_combine(const Acc (&s)[NW]) {
   return t;
 }
 
+// The mean's scales computed by the workgroup itself (self_scales):
+// {D, alpha = 1/D, beta = 1/n}.
+__shared__ double s_self_scales[3];
+
+// Every workgroup of a fused launch with self_scales counts the counted rows
+// n and D = sum of w[target] over them (the prologue's sums, in the same
+// fixed order in every workgroup, so all get the same bits) and keeps the
+// mean scales in LDS; workgroup 0 also stores D, n and the scales in the
+// header for the epilogue (device-scope stores, complete before its arrival).
+template <int BLOCK>
+__device__ __forceinline__ void compute_self_scales(const Params& p) {
+  constexpr int NW = BLOCK / 64;
+  constexpr int kU = 8;
+  __shared__ double s_D[NW];
+  __shared__ int64_t s_n[NW];
+  const int tid = threadIdx.x;
+  double D = 0.0;
+  int64_t n = 0;
+  for (int64_t r0 = tid; r0 < p.rows; r0 += static_cast<int64_t>(BLOCK) * kU) {
+    int64_t yv[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t r = r0 + static_cast<int64_t>(u) * BLOCK;
+      yv[u] = r < p.rows ? p.target[r] : p.ignore_index;
+    }
+    float wv[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const bool ok = yv[u] != p.ignore_index && yv[u] >= 0 && yv[u] < p.V;
+      wv[u] = ok ? (p.weight ? p.weight[yv[u]] : 1.0f) : 0.0f;
+      n += ok ? 1 : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) D += static_cast<double>(wv[u]);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    D += __shfl_xor(D, off, 64);
+    n += __shfl_xor(n, off, 64);
+  }
+  if ((tid & 63) == 0) {
+    s_D[tid >> 6] = D;
+    s_n[tid >> 6] = n;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double tD = 0.0;
+    int64_t tn = 0;
+    for (int w = 0; w < NW; ++w) {
+      tD += s_D[w];
+      tn += s_n[w];
+    }
+    const double alpha = (tD != 0.0) ? static_cast<double>(static_cast<float>(1.0 / tD)) : 0.0;
+    const double beta =
+        (tn != 0) ? static_cast<double>(static_cast<float>(1.0 / static_cast<double>(tn))) : 0.0;
+    s_self_scales[0] = tD;
+    s_self_scales[1] = alpha;
+    s_self_scales[2] = beta;
+    if (blockIdx.x == 0) {
+      __hip_atomic_store(&p.hdr->D, tD, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&p.hdr->n, tn, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __syncthreads();
+}
+
 // Scales of the row formulas: from the prologue when it ran (mean, weighted
-// smoothing), else the sum/none values alpha = beta = 1 and W = V.
+// smoothing), from the workgroup's own count (self_scales), else the
+// sum/none values alpha = beta = 1 and W = V.
 __device__ __forceinline__ void load_scales(const Params& p, double& W, double& alpha,
                                             double& beta) {
-  if (p.has_hdr) {
+  if (p.self_scales) {
+    W = static_cast<double>(p.V);
+    alpha = s_self_scales[1];
+    beta = s_self_scales[2];
+  } else if (p.has_hdr) {
     W = p.hdr->W;
     alpha = p.hdr->alpha;
     beta = p.hdr->beta;
@@ -371,7 +442,7 @@ struct RowClaim {
 
 template <class E, int BLOCK, int NREG, int NLDS, int SC, int SM, bool DYN>
 __device__ __forceinline__ void fused_row(const Params& p, int64_t row, int64_t y,
-                                          RowShared<BLOCK, NLDS>& sh) {
+                                          RowShared<BLOCK, NLDS>& sh, bool& scaled) {
   constexpr int EPV = E::EPV;
   constexpr int NS = NREG + NLDS;
   constexpr int NW = BLOCK / 64;
@@ -444,6 +515,12 @@ __device__ __forceinline__ void fused_row(const Params& p, int64_t row, int64_t 
   for (int k = 0; k < NLDS; ++k)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_ptr)(lds_rows + k * BLOCK + wave * 64),
                                              16, voff, (NREG + k) * BLOCK * 16, 0, 0);
+  // self_scales: the workgroup counts n and D once, while its first row's
+  // loads are in flight (uniform: every thread takes the same branch).
+  if (!scaled) {
+    compute_self_scales<BLOCK>(p);
+    scaled = true;
+  }
 
   // ---- pass 1 ----
   // Thread state: (tm, ts) = max of z and sum of exp(z - tm), tsz = smoothing
@@ -690,11 +767,12 @@ __global__ __launch_bounds__(BLOCK) void rows_kernel(Params p) {
   __shared__ int64_t s_y[DYN ? 1 : kRowsStaged];
   __shared__ int s_last;
   const int64_t G = gridDim.x;
+  bool scaled = !p.self_scales;
   if constexpr (DYN) {
     int64_t row = blockIdx.x;
     int64_t y = p.target[row];
     while (true) {
-      fused_row<E, BLOCK, NREG, NLDS, SC, SM, true>(p, row, y, sh);
+      fused_row<E, BLOCK, NREG, NLDS, SC, SM, true>(p, row, y, sh, scaled);
       row = uniform_i64(sh.next_row);
       y = uniform_i64(sh.next_y);
       if (row >= p.rows) break;
@@ -711,9 +789,11 @@ __global__ __launch_bounds__(BLOCK) void rows_kernel(Params p) {
         }
         __syncthreads();
       }
-      fused_row<E, BLOCK, NREG, NLDS, SC, SM, false>(p, row, uniform_i64(s_y[q]), sh);
+      fused_row<E, BLOCK, NREG, NLDS, SC, SM, false>(p, row, uniform_i64(s_y[q]), sh, scaled);
     }
   }
+  // workgroup 0 stores D for the epilogue even if all its rows were skipped
+  if (!scaled && blockIdx.x == 0) compute_self_scales<BLOCK>(p);
   if (p.epilogue) {
     if (threadIdx.x == 0) s_last = arrive(p, static_cast<uint32_t>(G));
     __syncthreads();

@@ -18,6 +18,7 @@ using cehost::kShapes;
 using cehost::Plan;
 
 constexpr int64_t kMaxInt = 0x7fffffffLL;
+constexpr int64_t kSelfScaleRows = 65536;  // rows a workgroup counts itself (self_scales)
 constexpr size_t kAlign = 256;
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }

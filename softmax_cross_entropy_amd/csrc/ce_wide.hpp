@@ -100,7 +100,7 @@ __device__ __forceinline__ void claim_finish(const Params& p, uint32_t c, WideSh
 // One part (a whole row, or half of one) of the persistent wide kernel.
 template <class E, int NREG, int HALVES, int SC, int SM>
 __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
-                                          WideShared& sh) {
+                                          WideShared& sh, bool& scaled) {
   constexpr int BLOCK = kWideBlock;
   constexpr int NW = BLOCK / 64;
   constexpr int EPV = E::EPV;
@@ -164,6 +164,12 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
 #pragma unroll
     for (int k = 0; k < NREG; ++k)
       r[k] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, k * BLOCK * 16, kLoadNT);
+    // self_scales: the workgroup counts n and D once, while its first part's
+    // loads are in flight (uniform: every thread takes the same branch).
+    if (!scaled) {
+      compute_self_scales<BLOCK>(p);
+      scaled = true;
+    }
 
     // ---- pass 1, group by group in load order ----
     // (tm, ts): max of z and sum of exp(z - tm); tsz: smoothing sum;
@@ -433,13 +439,16 @@ __global__ __launch_bounds__(kWideBlock) void wide_kernel(Params p) {
   __shared__ WideShared sh;
   __shared__ int s_last;
   const int64_t parts = p.rows * HALVES;
+  bool scaled = !p.self_scales;
   int64_t t = blockIdx.x;
   int64_t y = p.target[t / HALVES];
   while (t < parts) {
-    wide_part<E, NREG, HALVES, SC, SM>(p, t, y, sh);
+    wide_part<E, NREG, HALVES, SC, SM>(p, t, y, sh, scaled);
     t = uniform_i64(sh.next_t);
     y = uniform_i64(sh.next_y);
   }
+  // workgroup 0 stores D for the epilogue even if all its parts were skipped
+  if (!scaled && blockIdx.x == 0) compute_self_scales<kWideBlock>(p);
   if (p.epilogue) {
     if (threadIdx.x == 0) s_last = arrive(p, gridDim.x);
     __syncthreads();
