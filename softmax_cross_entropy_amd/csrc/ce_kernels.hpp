@@ -442,7 +442,7 @@ struct RowClaim {
 
 template <class E, int BLOCK, int NREG, int NLDS, int SC, int SM, bool DYN>
 __device__ __forceinline__ void fused_row(const Params& p, int64_t row, int64_t y,
-                                          RowShared<BLOCK, NLDS>& sh, bool& scaled) {
+                                          RowShared<BLOCK, NLDS>& sh) {
   constexpr int EPV = E::EPV;
   constexpr int NS = NREG + NLDS;
   constexpr int NW = BLOCK / 64;
@@ -515,13 +515,6 @@ __device__ __forceinline__ void fused_row(const Params& p, int64_t row, int64_t 
   for (int k = 0; k < NLDS; ++k)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_ptr)(lds_rows + k * BLOCK + wave * 64),
                                              16, voff, (NREG + k) * BLOCK * 16, 0, 0);
-  // self_scales: the workgroup counts n and D once, while its first row's
-  // loads are in flight (uniform: every thread takes the same branch).
-  if (!scaled) {
-    compute_self_scales<BLOCK>(p);
-    scaled = true;
-  }
-
   // ---- pass 1 ----
   // Thread state: (tm, ts) = max of z and sum of exp(z - tm), tsz = smoothing
   // sum, tb = raw maximum and tg = first group holding it (NG: the tail).
@@ -767,12 +760,14 @@ __global__ __launch_bounds__(BLOCK) void rows_kernel(Params p) {
   __shared__ int64_t s_y[DYN ? 1 : kRowsStaged];
   __shared__ int s_last;
   const int64_t G = gridDim.x;
-  bool scaled = !p.self_scales;
+  // self_scales: every workgroup counts n and D once, before its rows (kept
+  // out of the row loop, whose registers it would otherwise crowd)
+  if (p.self_scales) compute_self_scales<BLOCK>(p);
   if constexpr (DYN) {
     int64_t row = blockIdx.x;
     int64_t y = p.target[row];
     while (true) {
-      fused_row<E, BLOCK, NREG, NLDS, SC, SM, true>(p, row, y, sh, scaled);
+      fused_row<E, BLOCK, NREG, NLDS, SC, SM, true>(p, row, y, sh);
       row = uniform_i64(sh.next_row);
       y = uniform_i64(sh.next_y);
       if (row >= p.rows) break;
@@ -789,11 +784,9 @@ __global__ __launch_bounds__(BLOCK) void rows_kernel(Params p) {
         }
         __syncthreads();
       }
-      fused_row<E, BLOCK, NREG, NLDS, SC, SM, false>(p, row, uniform_i64(s_y[q]), sh, scaled);
+      fused_row<E, BLOCK, NREG, NLDS, SC, SM, false>(p, row, uniform_i64(s_y[q]), sh);
     }
   }
-  // workgroup 0 stores D for the epilogue even if all its rows were skipped
-  if (!scaled && blockIdx.x == 0) compute_self_scales<BLOCK>(p);
   if (p.epilogue) {
     if (threadIdx.x == 0) s_last = arrive(p, static_cast<uint32_t>(G));
     __syncthreads();

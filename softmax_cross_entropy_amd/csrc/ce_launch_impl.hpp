@@ -69,7 +69,8 @@ hipError_t launch_fused(int shape, const Params& p, hipStream_t st) {
 }
 
 // wide_kernel launch (instantiated in the ce_inst_*_wide units): persistent,
-// at most one workgroup per part.
+// at most one workgroup per part; half rows take an even number of
+// workgroups (fixed pairs 2j, 2j + 1), at least one pair.
 template <class E, int NREG, int HALVES, int SC, int SM>
 hipError_t launch_wide_t(const Params& p, hipStream_t st) {
   static int cache[64] = {};
@@ -78,7 +79,8 @@ hipError_t launch_wide_t(const Params& p, hipStream_t st) {
       resident_blocks(cedev::wide_kernel<E, NREG, HALVES, SC, SM>, cedev::kWideBlock, cache, &r);
   if (e != hipSuccess) return e;
   const int64_t parts = p.rows * HALVES;
-  const int64_t grid = parts < r ? parts : r;
+  int64_t grid = parts < r ? parts : r;
+  if (HALVES == 2) grid = grid >= 2 ? (grid & ~static_cast<int64_t>(1)) : 2;
   cedev::wide_kernel<E, NREG, HALVES, SC, SM>
       <<<dim3(static_cast<unsigned>(grid)), cedev::kWideBlock, 0, st>>>(p);
   return hipGetLastError();

@@ -14,8 +14,12 @@
 //  * A row of two halves: each workgroup reduces its half to a partial
 //    (max, sum, smoothing sum, argmax), publishes it, and takes the other
 //    half's partial; both combine the two in the same order (half 0 first),
-//    so both get bitwise identical row scalars. The halves of row r are
-//    workgroups 2r and 2r + 1, started by the hardware in that order.
+//    so both get bitwise identical row scalars. Pairs are fixed: workgroups
+//    2j and 2j + 1 take the two halves of one row after another, so a
+//    workgroup only ever waits for its neighbour, which the hardware starts
+//    right after it. Pair j starts with row j; the even workgroup claims the
+//    pair's next row when it starts a row and hands it over with its
+//    partial.
 //  * Pass 1 works in groups of 4 slots (fp32; 2 for bf16) with one shift per
 //    group; rows of fp32 logits without softcap keep exp(z - group shift)
 //    in place of the logits, so the gradient pass is one multiply per
@@ -28,44 +32,52 @@ namespace cedev {
 
 constexpr int kWideBlock = 1024;
 constexpr int kWideSlots = 16;  // VGPR slots per thread of the largest wide shapes
-// Polls of the partner's partial before a pair gives up and flags the row
+// Polls of the partner's words before a pair gives up and flags the row
 // (each poll is one device-coherent load, about a microsecond); a partner
-// that never arrives would otherwise hold the workgroup forever.
+// that never arrives would otherwise hold the workgroup forever. After one
+// such failure the workgroup polls once per row: the error bit is set and
+// the launch ends in bounded time.
 constexpr int kPairSpinLimit = 1 << 22;
 
 // Row-pair exchange through the row's two 64-byte slots (one per half).
-// Each of the five words of a partial (max, sum, smoothing sum, largest raw
-// logit, its index) travels as a 64-bit atomic store of (word, epoch), where
-// the epoch is a number the host makes unique per call: a reader that sees
-// this call's epoch in a pair has that pair's word, with no wait between
-// data and flag on the writer's side. The partner polls its five pairs
-// until all carry this call's epoch. Nothing has to be reset between calls:
-// a slot left by an earlier call carries an older epoch.
-// Thread 0 of the workgroup; returns false if the partner never published.
+// Words 0-4 are a half's partial (max, sum, smoothing sum, largest raw
+// logit, its index); words 5-7, written by half 0 only, are the pair's next
+// row and that row's target (low, high). Each word travels as a 64-bit
+// atomic store of (word, epoch), where the epoch is a number the host makes
+// unique per call: a reader that sees this call's epoch in a pair has that
+// pair's word, with no wait between data and flag on the writer's side.
+// Nothing has to be reset between calls: a slot left by an earlier call
+// carries an older epoch.
 constexpr int kPairWords = 5;
+constexpr int kSlotWords = 8;
 
+// Thread 0: publishes words [A, B) of `mine`, then polls words [C, D) of
+// the partner's slot until all carry this call's epoch; returns false if
+// the partner did not publish within `limit` polls.
+template <int A, int B, int C, int D>
 __device__ __forceinline__ bool pair_exchange(const Params& p, int64_t row, int h,
-                                              const uint32_t (&mine)[kPairWords],
-                                              uint32_t (&other)[kPairWords]) {
+                                              const uint32_t (&mine)[kSlotWords],
+                                              uint32_t (&other)[kSlotWords], int limit) {
   uint64_t* slot = reinterpret_cast<uint64_t*>(p.part + row * 4);  // 2 x 64 bytes
   const uint64_t ep = static_cast<uint64_t>(p.epoch) << 32;
 #pragma unroll
-  for (int i = 0; i < kPairWords; ++i)
-    __hip_atomic_store(slot + 8 * h + i, ep | mine[i], __ATOMIC_RELAXED,
+  for (int i = A; i < B; ++i)
+    __hip_atomic_store(slot + kSlotWords * h + i, ep | mine[i], __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
-  const uint64_t* osrc = slot + 8 * (1 - h);
+  if constexpr (C == D) return true;
+  const uint64_t* osrc = slot + kSlotWords * (1 - h);
   int it = 0;
   while (true) {
     bool all = true;
 #pragma unroll
-    for (int i = 0; i < kPairWords; ++i) {
+    for (int i = C; i < D; ++i) {
       const uint64_t v = __hip_atomic_load(osrc + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       other[i] = static_cast<uint32_t>(v);
       all = all && (static_cast<uint32_t>(v >> 32) == p.epoch);
     }
     if (all) return true;
+    if (++it >= limit) return false;
     __builtin_amdgcn_s_sleep(1);
-    if (++it >= kPairSpinLimit) return false;
   }
 }
 
@@ -75,15 +87,21 @@ struct WideShared {
   int cand[kWideBlock / 64];
   RowScalars rs;
   float xy;
-  int64_t next_t, next_y;  // the part claimed next and its row's target
+  int64_t next_t, next_y;  // the part (whole rows) or row (pairs) next, and its target
+  int limit;               // poll limit of the pair exchange (thread 0 only)
 };
 
-// Part claims: workgroup b starts with part b; thread 0 claims the next one
-// (gridDim.x + the claim counter) once the current part's pass 1 is done, so
-// parts go to workgroups in the order they finish. Every part processed
-// takes exactly one claim, so the claim that returns parts - 1 is the
-// launch's last and resets the counter for the next launch. The two halves
-// of a row are consecutive parts: their claims are made one after the other.
+// Whole-row parts are claimed: workgroup b starts with part b; thread 0
+// claims the next one (gridDim.x + the claim counter) once the current
+// part's pass 1 is done, so parts go to workgroups in the order they finish.
+// Every part processed takes exactly one claim, so the claim that returns
+// parts - 1 is the launch's last and resets the counter for the next launch.
+// Half rows are not claimed one by one (a workgroup that claimed before
+// waiting for its partner could be handed that partner's half and wait on
+// itself): half 0 of a fixed pair claims whole rows (pairs + the counter)
+// when it starts a row, so it holds its next row before it can wait; the
+// launch makes one claim per row, and the claim that returns rows - 1
+// resets the counter.
 __device__ __forceinline__ uint32_t claim_issue(const Params& p) {
   return __hip_atomic_fetch_add(&p.hdr->next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -97,10 +115,52 @@ __device__ __forceinline__ void claim_finish(const Params& p, uint32_t c, WideSh
   sh.next_y = nt < parts ? p.target[nt / HALVES] : 0;
 }
 
+// Half 0 of a pair (thread 0): the row a claim `c` stands for (issued when
+// the current row started, so its target is read while the row is in
+// flight); the launch's last claim resets the counter.
+__device__ __forceinline__ int64_t pair_row(const Params& p, uint32_t c) {
+  return static_cast<int64_t>(gridDim.x >> 1) + c;
+}
+__device__ __forceinline__ int64_t pair_target(const Params& p, uint32_t c) {
+  const int64_t nr = pair_row(p, c);
+  return nr < p.rows ? p.target[nr] : 0;
+}
+__device__ __forceinline__ void pair_reset(const Params& p, uint32_t c) {
+  if (c == static_cast<uint32_t>(p.rows - 1))
+    __hip_atomic_store(&p.hdr->next, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Thread 0: the pair's next row and its target into the block-shared state
+// (half 1 takes them from half 0's words 5-7; if they never came, the
+// workgroup stops).
+__device__ __forceinline__ void pair_next(const Params& p, int h, bool ok, uint32_t c,
+                                          int64_t ny, const uint32_t (&other)[kSlotWords],
+                                          WideShared& sh) {
+  if (h == 0) {
+    sh.next_t = pair_row(p, c);
+    sh.next_y = ny;
+  } else {
+    sh.next_t = ok ? static_cast<int64_t>(other[5]) : p.rows;
+    sh.next_y = static_cast<int64_t>((static_cast<uint64_t>(other[7]) << 32) | other[6]);
+  }
+  if (!ok) {
+    atomicOr(&p.hdr->err, 2u);
+    sh.limit = 1;
+  }
+}
+
+// Half 0's words 5-7: the pair's next row and its target.
+__device__ __forceinline__ void next_words(const Params& p, uint32_t c, int64_t ny,
+                                           uint32_t (&w)[kSlotWords]) {
+  w[5] = static_cast<uint32_t>(pair_row(p, c));
+  w[6] = static_cast<uint32_t>(ny);
+  w[7] = static_cast<uint32_t>(static_cast<uint64_t>(ny) >> 32);
+}
+
 // One part (a whole row, or half of one) of the persistent wide kernel.
 template <class E, int NREG, int HALVES, int SC, int SM>
 __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
-                                          WideShared& sh, bool& scaled) {
+                                          WideShared& sh) {
   constexpr int BLOCK = kWideBlock;
   constexpr int NW = BLOCK / 64;
   constexpr int EPV = E::EPV;
@@ -134,13 +194,38 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
   if (ignored || bad) {
     // Ignored rows are never read; their gradient is exactly +0.0
     // (tt-mlir PR #9324 page: ignored rows, also with non-finite logits).
-    __syncthreads();  // every thread has read the previous part's next_t
-    if (tid == 0) claim_finish<HALVES>(p, claim_issue(p), sh);
-    __syncthreads();
+    if constexpr (HALVES == 1) {
+      __syncthreads();  // every thread has read the previous part's next_t
+      if (tid == 0) claim_finish<HALVES>(p, claim_issue(p), sh);
+      __syncthreads();
+    }
+    uint32_t claim = 0;
+    if constexpr (HALVES == 2) {
+      if (tid == 0 && h == 0) claim = claim_issue(p);
+    }
     if (p.grad) {
       u4* vp = reinterpret_cast<u4*>(hp);
       for (int j = tid; j < nv; j += BLOCK) __builtin_nontemporal_store(u4{0u, 0u, 0u, 0u}, vp + j);
       if (tid < tail) E::st(rp, tail0 + tid, 0.0f);
+    }
+    if constexpr (HALVES == 2) {
+      // no partials to combine: half 0 only hands over the pair's next row
+      __syncthreads();  // every thread has read the previous part's next_t
+      if (tid == 0) {
+        uint32_t mine_w[kSlotWords] = {}, other_w[kSlotWords] = {};
+        bool ok = true;
+        int64_t ny = 0;
+        if (h == 0) {
+          pair_reset(p, claim);
+          ny = pair_target(p, claim);
+          next_words(p, claim, ny, mine_w);
+          pair_exchange<5, kSlotWords, 0, 0>(p, row, h, mine_w, other_w, sh.limit);
+        } else {
+          ok = pair_exchange<0, 0, 5, kSlotWords>(p, row, h, mine_w, other_w, sh.limit);
+        }
+        pair_next(p, h, ok, claim, ny, other_w, sh);
+      }
+      __syncthreads();
     }
     if (tid == 0 && h == 0) {
       const float q = bad ? __builtin_nanf("") : 0.0f;
@@ -154,6 +239,11 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
     // spanning exactly the part's vectors: lanes past it read 0 and their
     // stores are dropped. Both halves read the target logit before either
     // can write a gradient (each writes only after both have published).
+    // Half 0 of a pair claims the pair's next row before its loads go out.
+    uint32_t claim = 0;
+    if constexpr (HALVES == 2) {
+      if (tid == 0 && h == 0) claim = claim_issue(p);
+    }
     float xy = 0.0f;
     if (tid == 0) xy = E::ld(rp, y);
     float xt = 0.0f;
@@ -164,11 +254,9 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
 #pragma unroll
     for (int k = 0; k < NREG; ++k)
       r[k] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, k * BLOCK * 16, kLoadNT);
-    // self_scales: the workgroup counts n and D once, while its first part's
-    // loads are in flight (uniform: every thread takes the same branch).
-    if (!scaled) {
-      compute_self_scales<BLOCK>(p);
-      scaled = true;
+    int64_t ny = 0;  // target of the pair's next row (half 0, thread 0)
+    if constexpr (HALVES == 2) {
+      if (tid == 0 && h == 0) ny = pair_target(p, claim);
     }
 
     // ---- pass 1, group by group in load order ----
@@ -344,15 +432,26 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
       t.bv = bmax;
       t.bi = arg;
       if (lane == 0) {
-        const uint32_t claim = claim_issue(p);
+        if constexpr (HALVES == 1) claim = claim_issue(p);
         if constexpr (HALVES == 2) {
-          // Exchange partials with the other half; both combine half 0 first.
-          uint32_t mine_w[kPairWords] = {
+          // Exchange partials with the other half (half 0 adds the pair's
+          // next row); both combine half 0 first.
+          uint32_t mine_w[kSlotWords] = {
               __builtin_bit_cast(uint32_t, t.m), __builtin_bit_cast(uint32_t, t.s),
               __builtin_bit_cast(uint32_t, t.sz), __builtin_bit_cast(uint32_t, t.bv),
-              static_cast<uint32_t>(t.bi)};
-          uint32_t other_w[kPairWords];
-          if (!pair_exchange(p, row, h, mine_w, other_w)) atomicOr(&p.hdr->err, 2u);
+              static_cast<uint32_t>(t.bi), 0u, 0u, 0u};
+          uint32_t other_w[kSlotWords] = {};
+          bool ok;
+          if (h == 0) {
+            pair_reset(p, claim);
+            next_words(p, claim, ny, mine_w);
+            ok = pair_exchange<0, kSlotWords, 0, kPairWords>(p, row, h, mine_w, other_w,
+                                                             sh.limit);
+          } else {
+            ok = pair_exchange<0, kPairWords, 0, kSlotWords>(p, row, h, mine_w, other_w,
+                                                             sh.limit);
+          }
+          pair_next(p, h, ok, claim, ny, other_w, sh);
           const uint32_t* q0 = h == 0 ? mine_w : other_w;
           const uint32_t* q1 = h == 0 ? other_w : mine_w;
           float m = __builtin_bit_cast(float, q0[0]), sum = __builtin_bit_cast(float, q0[1]);
@@ -376,7 +475,7 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
         rs.ok = (t.bi == y);
         sh.rs = rs;
         sh.xy = xy;
-        claim_finish<HALVES>(p, claim, sh);
+        if constexpr (HALVES == 1) claim_finish<HALVES>(p, claim, sh);
         if (h == 0) {
           write_row_outputs(p, row, rs.ce, rs.zl, rs.ok, t.bi);
           write_row_stats(p, row, rs.m, rs.l2s);
@@ -430,25 +529,40 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
 }
 
 // Persistent: as many workgroups as fit on the device at once (at most one
-// per part); each processes parts until the claims run out, then arrives
-// once at the epilogue. The next part's loads are issued as soon as the
-// current part's gradient stores are (they drain while the next part
-// arrives).
+// per part; an even number for half rows); each processes parts until the
+// claims run out, then arrives once at the epilogue. The next part's loads
+// are issued as soon as the current part's gradient stores are (they drain
+// while the next part arrives).
 template <class E, int NREG, int HALVES, int SC, int SM>
 __global__ __launch_bounds__(kWideBlock) void wide_kernel(Params p) {
+  static_assert(HALVES == 1 || HALVES == 2, "whole rows or half rows");
   __shared__ WideShared sh;
   __shared__ int s_last;
-  const int64_t parts = p.rows * HALVES;
-  bool scaled = !p.self_scales;
-  int64_t t = blockIdx.x;
-  int64_t y = p.target[t / HALVES];
-  while (t < parts) {
-    wide_part<E, NREG, HALVES, SC, SM>(p, t, y, sh, scaled);
-    t = uniform_i64(sh.next_t);
-    y = uniform_i64(sh.next_y);
+  // self_scales: every workgroup counts n and D once, before its parts
+  // (kept out of the part loop, whose registers it would otherwise crowd)
+  if (p.self_scales) compute_self_scales<kWideBlock>(p);
+  if (threadIdx.x == 0) sh.limit = kPairSpinLimit;
+  if constexpr (HALVES == 2) {
+    // pair j = workgroups 2j, 2j + 1 starts with row j (the grid holds at
+    // most one pair per row)
+    const int h = blockIdx.x & 1;
+    int64_t row = blockIdx.x >> 1;
+    int64_t y = p.target[row];
+    while (row < p.rows) {
+      wide_part<E, NREG, HALVES, SC, SM>(p, 2 * row + h, y, sh);
+      row = uniform_i64(sh.next_t);
+      y = uniform_i64(sh.next_y);
+    }
+  } else {
+    const int64_t parts = p.rows;
+    int64_t t = blockIdx.x;
+    int64_t y = p.target[t];
+    while (t < parts) {
+      wide_part<E, NREG, HALVES, SC, SM>(p, t, y, sh);
+      t = uniform_i64(sh.next_t);
+      y = uniform_i64(sh.next_y);
+    }
   }
-  // workgroup 0 stores D for the epilogue even if all its parts were skipped
-  if (!scaled && blockIdx.x == 0) compute_self_scales<kWideBlock>(p);
   if (p.epilogue) {
     if (threadIdx.x == 0) s_last = arrive(p, gridDim.x);
     __syncthreads();
