@@ -31,6 +31,8 @@
 namespace cedev {
 
 constexpr int kWideBlock = 1024;
+// s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt left at their maxima
+constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr int kWideSlots = 16;  // VGPR slots per thread of the largest wide shapes
 // Polls of the partner's words before a pair gives up and flags the row
 // (each poll is one device-coherent load, about a microsecond); a partner
@@ -160,7 +162,7 @@ __device__ __forceinline__ void next_words(const Params& p, uint32_t c, int64_t 
 // One part (a whole row, or half of one) of the persistent wide kernel.
 template <class E, int NREG, int HALVES, int SC, int SM>
 __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
-                                          WideShared& sh) {
+                                          WideShared& sh, int64_t& next_t, int64_t& next_y) {
   constexpr int BLOCK = kWideBlock;
   constexpr int NW = BLOCK / 64;
   constexpr int EPV = E::EPV;
@@ -198,6 +200,8 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
       __syncthreads();  // every thread has read the previous part's next_t
       if (tid == 0) claim_finish<HALVES>(p, claim_issue(p), sh);
       __syncthreads();
+      next_t = uniform_i64(sh.next_t);
+      next_y = uniform_i64(sh.next_y);
     }
     uint32_t claim = 0;
     if constexpr (HALVES == 2) {
@@ -226,6 +230,8 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
         pair_next(p, h, ok, claim, ny, other_w, sh);
       }
       __syncthreads();
+      next_t = uniform_i64(sh.next_t);
+      next_y = uniform_i64(sh.next_y);
     }
     if (tid == 0 && h == 0) {
       const float q = bad ? __builtin_nanf("") : 0.0f;
@@ -350,6 +356,12 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
       if constexpr (SM) tsz = p.weight ? __builtin_fmaf(p.weight[tail0 + tid], z, tsz) : tsz + z;
     }
 
+    // Every load of the part has been consumed by pass 1 (a part holds data
+    // in each group it reads); saying so with an explicit wait keeps the
+    // compiler from guarding later writes of those registers with a wait
+    // for every store in flight (it cannot see that a skipped group's load
+    // is skipped too).
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     Acc a;
     a.m = tm;
     a.s = ts;
@@ -484,6 +496,11 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
       }
     }
     __syncthreads();
+    // The next part, read here rather than after the gradient stores: an LDS
+    // read behind them made the compiler wait for every store to complete
+    // before the next part's loads could go out.
+    next_t = uniform_i64(sh.next_t);
+    next_y = uniform_i64(sh.next_y);
 
     // ---- pass 2: the gradient from on-chip data, written over the logits ----
     if (p.grad) {
@@ -549,18 +566,20 @@ __global__ __launch_bounds__(kWideBlock) void wide_kernel(Params p) {
     int64_t row = blockIdx.x >> 1;
     int64_t y = p.target[row];
     while (row < p.rows) {
-      wide_part<E, NREG, HALVES, SC, SM>(p, 2 * row + h, y, sh);
-      row = uniform_i64(sh.next_t);
-      y = uniform_i64(sh.next_y);
+      int64_t nr, ny;
+      wide_part<E, NREG, HALVES, SC, SM>(p, 2 * row + h, y, sh, nr, ny);
+      row = nr;
+      y = ny;
     }
   } else {
     const int64_t parts = p.rows;
     int64_t t = blockIdx.x;
     int64_t y = p.target[t];
     while (t < parts) {
-      wide_part<E, NREG, HALVES, SC, SM>(p, t, y, sh);
-      t = uniform_i64(sh.next_t);
-      y = uniform_i64(sh.next_y);
+      int64_t nt, ny;
+      wide_part<E, NREG, HALVES, SC, SM>(p, t, y, sh, nt, ny);
+      t = nt;
+      y = ny;
     }
   }
   if (p.epilogue) {
