@@ -113,6 +113,12 @@ struct F32 {
   __device__ static __forceinline__ float ld(const void* row, int64_t i) {
     return static_cast<const float*>(row)[i];
   }
+  // The fp32 value of an element's bits (loaded early, widened where used).
+  __device__ static __forceinline__ float widen(uint32_t r) { return __builtin_bit_cast(float, r); }
+  // Element i (bits) through a buffer descriptor: 0 outside it.
+  __device__ static __forceinline__ uint32_t ld_buf(__amdgpu_buffer_rsrc_t r, int i) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, i * 4, 0, 0);
+  }
   __device__ static __forceinline__ void st(void* row, int64_t i, float v) {
     static_cast<float*>(row)[i] = v;
   }
@@ -150,6 +156,12 @@ struct BF16 {
   __device__ static __forceinline__ float ld(const void* row, int64_t i) {
     const uint32_t h = static_cast<const uint16_t*>(row)[i];
     return __builtin_bit_cast(float, h << 16);
+  }
+  __device__ static __forceinline__ float widen(uint32_t r) {
+    return __builtin_bit_cast(float, r << 16);
+  }
+  __device__ static __forceinline__ uint32_t ld_buf(__amdgpu_buffer_rsrc_t r, int i) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, i * 2, 0, 0);
   }
   __device__ static __forceinline__ void st(void* row, int64_t i, float v) {
     static_cast<uint16_t*>(row)[i] = static_cast<uint16_t>(pack_bf16x2(v, 0.0f) & 0xffffu);

@@ -38,10 +38,23 @@ typedef __attribute__((address_space(3))) void* lds_void_ptr;
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kStoreNT = 2;  // non-temporal store (streaming gradient)
 constexpr int kLoadNT = 2;   // non-temporal load (each logit is read once)
+// s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt left at their maxima
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int nvec) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
                                            nvec * 16, kRsrcWord3);
+}
+// The same over `bytes` bytes (a row's V elements).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_bytes(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes,
+                                           kRsrcWord3);
+}
+// Zero in a VGPR that the compiler cannot see through.
+__device__ __forceinline__ uint32_t opaque_zero() {
+  uint32_t z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return z;
 }
 
 // Softcapped value z = c tanh(x / c) (Liger-Kernel CE profile, Forward Pass:

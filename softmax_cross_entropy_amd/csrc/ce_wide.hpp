@@ -31,8 +31,6 @@
 namespace cedev {
 
 constexpr int kWideBlock = 1024;
-// s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt left at their maxima
-constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr int kWideSlots = 16;  // VGPR slots per thread of the largest wide shapes
 // Polls of the partner's words before a pair gives up and flags the row
 // (each poll is one device-coherent load, about a microsecond); a partner
@@ -106,6 +104,16 @@ struct WideShared {
 // resets the counter.
 __device__ __forceinline__ uint32_t claim_issue(const Params& p) {
   return __hip_atomic_fetch_add(&p.hdr->next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// The same for a claim issued before the part's loads: the address carries
+// an opaque per-lane zero, so the compiler keeps it a one-lane atomic instead
+// of a wave-wide one whose result it would wait for (and with it for every
+// store still in flight) right after issuing it.
+__device__ __forceinline__ uint32_t claim_issue_early(const Params& p) {
+  int zero = 0;
+  asm volatile("" : "+v"(zero));
+  return __hip_atomic_fetch_add(&p.hdr->next + zero, 1u, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
 }
 template <int HALVES>
 __device__ __forceinline__ void claim_finish(const Params& p, uint32_t c, WideShared& sh) {
@@ -248,12 +256,21 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
     // Half 0 of a pair claims the pair's next row before its loads go out.
     uint32_t claim = 0;
     if constexpr (HALVES == 2) {
-      if (tid == 0 && h == 0) claim = claim_issue(p);
+      if (tid == 0 && h == 0) claim = claim_issue_early(p);
     }
-    float xy = 0.0f;
-    if (tid == 0) xy = E::ld(rp, y);
-    float xt = 0.0f;
-    if (tid < tail) xt = E::ld(rp, tail0 + tid);
+    // The target logit and the row tail as stored, read by every lane of wave
+    // 0 (the waves that use them) through a descriptor over the row's V
+    // elements (lanes past the tail read 0), and widened where used: a load
+    // in a per-lane branch, or a bf16 widening right here, would make the
+    // wave wait for the previous row's stores before its own loads go out.
+    // The other waves' value is an opaque zero, so the compiler cannot fold
+    // the widening into the branch.
+    uint32_t xy_raw = opaque_zero(), xt_raw = xy_raw;
+    if (wave == 0) {
+      const __amdgpu_buffer_rsrc_t rrow = make_rsrc_bytes(rp, static_cast<int>(p.V) * E::BYTES);
+      xy_raw = E::ld_buf(rrow, static_cast<int>(y));
+      xt_raw = E::ld_buf(rrow, static_cast<int>(tail0) + tid);
+    }
     const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(hp, nv);
     const int voff = tid * 16;
     u4 r[NREG];
@@ -346,6 +363,7 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
         if constexpr (KEEP_E) gm[g] = zg;
       }
     }
+    const float xt = E::widen(xt_raw);
     if (tid < tail) {
       // the row tail (last part): one element per thread, after every vector
       const bool take = xt > tb;
@@ -482,11 +500,11 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
         load_scales(p, W, alpha, beta);
         const float wy = p.weight ? p.weight[y] : 1.0f;
         RowScalars rs;
-        row_scalars(rs, t.m, t.s, t.sz, zval<SC>(p, xy), wy, W, p, alpha, beta);
+        row_scalars(rs, t.m, t.s, t.sz, zval<SC>(p, E::widen(xy_raw)), wy, W, p, alpha, beta);
         rs.arg = t.bi;
         rs.ok = (t.bi == y);
         sh.rs = rs;
-        sh.xy = xy;
+        sh.xy = E::widen(xy_raw);
         if constexpr (HALVES == 1) claim_finish<HALVES>(p, claim, sh);
         if (h == 0) {
           write_row_outputs(p, row, rs.ce, rs.zl, rs.ok, t.bi);
