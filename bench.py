@@ -294,7 +294,7 @@ def main(argv=None) -> int:
     ap.add_argument("--path", choices=("auto", "fused", "splitv", "scalar"), default="auto",
                     help="force a kernel path (default: the library's choice)")
     ap.add_argument("--alt-shape", action="store_true",
-                    help="the other fused layout for rows of 8 K to 32 K 16-byte vectors "
+                    help="the other fused layout for rows of 2 K to 32 K 16-byte vectors "
                          "(test hook, for comparing layouts)")
     ap.add_argument("--linear", action="store_true",
                     help="the linear layer fused with the cross-entropy at 4096 x 4096 hidden, "

@@ -80,9 +80,11 @@ enum {
   CE_F_FORCE_SPLITV = 1u << 6,
   CE_F_FORCE_SCALAR = 1u << 7,
   CE_F_SHAPE_ALT = 1u << 8      /* test hook: the other fused layout where a   */
-                                /* row size has two (rows of 2 K to 32 K       */
+                                /* row size has two (rows of 2 K to 16 K       */
                                 /* 16-byte vectors: 1024-thread workgroups vs  */
-                                /* 256/512-thread ones)                        */
+                                /* 256/512-thread ones; 16 K to 32 K: a pair   */
+                                /* of 1024-thread workgroups per row vs four   */
+                                /* 512-thread ones)                            */
 };
 
 /* Kernel paths (ce_plan_path). */

@@ -30,7 +30,6 @@
 
 namespace cedev {
 
-typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
 // Raw buffer descriptor over nvec 16-byte vectors at base (stride 0: byte
 // offsets; the fourth word selects 32-bit data on gfx9-family GPUs). Loads
@@ -332,22 +331,12 @@ __device__ __forceinline__ void load_scales(const Params& p, double& W, double& 
   }
 }
 
-// Register / LDS slot k of thread tid (k is a compile-time constant once the
-// slot loops are unrolled).
-template <int NREG, int BLOCK>
-__device__ __forceinline__ u4 slot_get(const u4 (&r)[NREG > 0 ? NREG : 1], const u4* lds, int k,
-                                       int tid) {
-  return (k < NREG) ? r[k < NREG ? k : 0] : lds[(k - NREG) * BLOCK + tid];
-}
-
-template <int NREG, int BLOCK>
-__device__ __forceinline__ void slot_put(u4 (&r)[NREG > 0 ? NREG : 1], u4* lds, int k, int tid,
-                                         u4 v) {
-  if (k < NREG) {
-    r[k < NREG ? k : 0] = v;
-  } else {
-    lds[(k - NREG) * BLOCK + tid] = v;
-  }
+// Register slot k of a thread (k is a compile-time constant once the slot
+// loops are unrolled; slots past NREG only appear in branches that are not
+// taken).
+template <int NREG>
+__device__ __forceinline__ u4& slot(u4 (&r)[NREG], int k) {
+  return r[k < NREG ? k : 0];
 }
 
 template <int EPV>
@@ -408,9 +397,8 @@ __device__ __forceinline__ void skipped_row(const Params& p, int64_t row, bool b
 }
 
 // Block-shared state of one row in flight.
-template <int BLOCK, int NLDS>
+template <int BLOCK>
 struct RowShared {
-  u4 rows[NLDS > 0 ? NLDS * BLOCK : 1];  // LDS slots
   Acc acc[BLOCK / 64];
   int cand[BLOCK / 64];
   RowScalars rs;
@@ -420,9 +408,8 @@ struct RowShared {
 
 // ---------------------------------------------------------------------------
 // fused_row: one row in one workgroup; the row is read from HBM once and kept
-// on chip. Slots: thread tid owns vectors j = k * BLOCK + tid, for k < NREG
-// in VGPRs and for NREG <= k < NREG + NLDS in LDS; the row tail (V % EPV
-// elements) is held by threads tid < tail.
+// on chip. Slots: thread tid owns vectors j = k * BLOCK + tid, k < NREG, in
+// VGPRs; the row tail (V % EPV elements) is held by threads tid < tail.
 //
 // Pass 1 takes the slots in groups of GS: first the group's raw maximum,
 // then the exponentials relative to the group's softcapped maximum and their
@@ -453,17 +440,15 @@ struct RowClaim {
   }
 };
 
-template <class E, int BLOCK, int NREG, int NLDS, int SC, int SM, bool DYN>
+template <class E, int BLOCK, int NREG, int SC, int SM, bool DYN>
 __device__ __forceinline__ void fused_row(const Params& p, int64_t row, int64_t y,
-                                          RowShared<BLOCK, NLDS>& sh) {
+                                          RowShared<BLOCK>& sh) {
   constexpr int EPV = E::EPV;
-  constexpr int NS = NREG + NLDS;
+  constexpr int NS = NREG;
   constexpr int NW = BLOCK / 64;
   constexpr bool KEEP_E = (EPV == 4) && !SC;
   constexpr int GS = (EPV == 4) ? 8 : 2;
   constexpr int NG = (NS + GS - 1) / GS;
-  constexpr int kRegPolicy = (NLDS == 0 || EPV == 8) ? kLoadNT : 0;
-  u4* lds_rows = sh.rows;
   Acc* s_acc = sh.acc;
   int* s_cand = sh.cand;
 
@@ -508,26 +493,19 @@ __device__ __forceinline__ void fused_row(const Params& p, int64_t row, int64_t 
   // one VGPR offset for every slot (the slot offset is scalar) and hardware
   // bounds checking (lanes past the row read 0 and their stores are
   // dropped), so the loads are unconditional and the compiler waits, for
-  // each register slot, only for that slot's data. Order: the two scalar
-  // loads, the register slots, then the LDS slots (consumed last).
-  // Cache policy, as measured on MI355X: non-temporal register-slot loads
-  // (each logit is read once, and the class weights of weighted rows stay
-  // in L2), except for fp32 rows that also use LDS slots, which ran faster
-  // with the default policy; LDS slots always use the default policy.
+  // each slot, only for that slot's data. Order: the target logit and the
+  // row tail, then the slots. The slot loads are non-temporal (each logit
+  // is read once, and the class weights of weighted rows stay in L2).
   float xy = 0.0f;
   if (tid == 0) xy = E::ld(rp, y);
   float xt = 0.0f;
   if (tid < tail) xt = E::ld(rp, tail0 + tid);
   const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(rp, nv);
   const int voff = tid * 16;
-  u4 r[NREG > 0 ? NREG : 1];
+  u4 r[NREG];
 #pragma unroll
   for (int k = 0; k < NREG; ++k)
-    r[k] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, k * BLOCK * 16, kRegPolicy);
-#pragma unroll
-  for (int k = 0; k < NLDS; ++k)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_ptr)(lds_rows + k * BLOCK + wave * 64),
-                                             16, voff, (NREG + k) * BLOCK * 16, 0, 0);
+    r[k] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, k * BLOCK * 16, kLoadNT);
   // ---- pass 1 ----
   // Thread state: (tm, ts) = max of z and sum of exp(z - tm), tsz = smoothing
   // sum, tb = raw maximum and tg = first group holding it (NG: the tail).
@@ -543,7 +521,7 @@ __device__ __forceinline__ void fused_row(const Params& p, int64_t row, int64_t 
         const int k = g * GS + q;
         if (k < NS && k * BLOCK < nv) {
           float f[EPV];
-          E::unpack(slot_get<NREG, BLOCK>(r, lds_rows, k, tid), f);
+          E::unpack(slot(r, k), f);
           if ((k + 1) * BLOCK > nv) {  // the row's last, partial slot (a scalar branch)
             asm volatile("");
             const bool ok = k * BLOCK + tid < nv;
@@ -564,7 +542,7 @@ __device__ __forceinline__ void fused_row(const Params& p, int64_t row, int64_t 
         const int k = g * GS + q;
         if (k < NS && k * BLOCK < nv) {
           float f[EPV];
-          E::unpack(slot_get<NREG, BLOCK>(r, lds_rows, k, tid), f);
+          E::unpack(slot(r, k), f);
           float z[EPV];
           if constexpr (SC) {
             float u[EPV], t[EPV];
@@ -580,7 +558,7 @@ __device__ __forceinline__ void fused_row(const Params& p, int64_t row, int64_t 
           float e[EPV];
 #pragma unroll
           for (int i = 0; i < EPV; ++i) e[i] = ex2((z[i] - zg) * kLog2e);
-          if constexpr (KEEP_E) slot_put<NREG, BLOCK>(r, lds_rows, k, tid, F32::pack(e));
+          if constexpr (KEEP_E) slot(r, k) = F32::pack(e);
           float es = e[0];
 #pragma unroll
           for (int i = 1; i < EPV; ++i) es += e[i];
@@ -661,7 +639,7 @@ __device__ __forceinline__ void fused_row(const Params& p, int64_t row, int64_t 
               if (KEEP_E && !by_e) {
                 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, k * BLOCK * 16, 0);
               } else {
-                v = slot_get<NREG, BLOCK>(r, lds_rows, k, tid);
+                v = slot(r, k);
               }
               float f[EPV];
               E::unpack(v, f);
@@ -722,7 +700,7 @@ __device__ __forceinline__ void fused_row(const Params& p, int64_t row, int64_t 
         for (int q = 0; q < GS; ++q) {
           const int k = g * GS + q;
           if (k < NS && k * BLOCK < nv) {
-            const u4 v = slot_get<NREG, BLOCK>(r, lds_rows, k, tid);
+            const u4 v = slot(r, k);
             u4 gv;
             if constexpr (KEEP_E) {
               gv = grad_vec_e<SM>(p, rs, v, sc, k * BLOCK + tid, -1);
@@ -766,10 +744,10 @@ __device__ __forceinline__ int64_t uniform_i64(int64_t v) {
 // Each row's values for the epilogue are stored as the row completes; the
 // workgroup arrives once, at its end.
 constexpr int kRowsStaged = 256;
-template <class E, int BLOCK, int NREG, int NLDS, int SC, int SM>
+template <class E, int BLOCK, int NREG, int SC, int SM>
 __global__ __launch_bounds__(BLOCK) void rows_kernel(Params p) {
-  constexpr bool DYN = NLDS > 0 || NREG >= 32;
-  __shared__ RowShared<BLOCK, NLDS> sh;
+  constexpr bool DYN = NREG >= 32;
+  __shared__ RowShared<BLOCK> sh;
   __shared__ int64_t s_y[DYN ? 1 : kRowsStaged];
   __shared__ int s_last;
   const int64_t G = gridDim.x;
@@ -780,7 +758,7 @@ __global__ __launch_bounds__(BLOCK) void rows_kernel(Params p) {
     int64_t row = blockIdx.x;
     int64_t y = p.target[row];
     while (true) {
-      fused_row<E, BLOCK, NREG, NLDS, SC, SM, true>(p, row, y, sh);
+      fused_row<E, BLOCK, NREG, SC, SM, true>(p, row, y, sh);
       row = uniform_i64(sh.next_row);
       y = uniform_i64(sh.next_y);
       if (row >= p.rows) break;
@@ -797,7 +775,7 @@ __global__ __launch_bounds__(BLOCK) void rows_kernel(Params p) {
         }
         __syncthreads();
       }
-      fused_row<E, BLOCK, NREG, NLDS, SC, SM, false>(p, row, uniform_i64(s_y[q]), sh);
+      fused_row<E, BLOCK, NREG, SC, SM, false>(p, row, uniform_i64(s_y[q]), sh);
     }
   }
   if (p.epilogue) {

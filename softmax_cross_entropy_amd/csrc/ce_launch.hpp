@@ -8,31 +8,31 @@
 
 namespace cehost {
 
-// Fused row shapes: BLOCK threads, each holding NREG vectors in VGPRs and
-// NLDS in LDS, HALVES workgroups per row (2: a row pair of wide_kernel);
-// capacity = BLOCK * (NREG + NLDS) * HALVES 16-byte vectors per row.
+// Fused row shapes: BLOCK threads, each holding NREG vectors in VGPRs,
+// HALVES workgroups per row (2: a row pair of wide_kernel, 4: four quarter
+// rows); capacity = BLOCK * NREG * HALVES 16-byte vectors per row.
 struct Shape {
-  int block, nreg, nlds, halves;
-  int cap() const { return block * (nreg + nlds) * halves; }
+  int block, nreg, halves;
+  int cap() const { return block * nreg * halves; }
 };
-constexpr int kNumShapes = 11;
+constexpr int kNumShapes = 10;
 constexpr Shape kShapes[kNumShapes] = {
-    {256, 4, 0, 1},    // 1024 vectors:  16 KiB rows
-    {256, 8, 0, 1},    // 2048 vectors:  32 KiB
-    {256, 16, 0, 1},   // 4096 vectors:  64 KiB
-    {512, 16, 0, 1},   // 8192 vectors: 128 KiB
-    {512, 32, 0, 1},   // 16384 vectors: 256 KiB
-    {1024, 16, 0, 1},  // 16384 vectors: 256 KiB (wide_kernel, 16 waves)
-    {512, 44, 19, 1},  // 32256 vectors: 504 KiB (176 VGPRs + 152 KiB LDS)
-    {512, 45, 19, 1},  // 32768 vectors: 512 KiB (180 VGPRs + 152 KiB LDS)
-    {1024, 16, 0, 2},  // 32768 vectors: 512 KiB (row pair of 1024-thread workgroups)
-    {1024, 4, 0, 1},   // 4096 vectors:  64 KiB (wide_kernel, 16 waves)
-    {1024, 8, 0, 1},   // 8192 vectors: 128 KiB (wide_kernel, 16 waves)
+    {256, 4, 1},    // 1024 vectors:  16 KiB rows
+    {256, 8, 1},    // 2048 vectors:  32 KiB
+    {256, 16, 1},   // 4096 vectors:  64 KiB
+    {512, 16, 1},   // 8192 vectors: 128 KiB
+    {512, 32, 1},   // 16384 vectors: 256 KiB
+    {1024, 16, 1},  // 16384 vectors: 256 KiB (wide_kernel, 16 waves)
+    {1024, 16, 2},  // 32768 vectors: 512 KiB (row pair of 1024-thread workgroups)
+    {1024, 4, 1},   // 4096 vectors:  64 KiB (wide_kernel, 16 waves)
+    {1024, 8, 1},   // 8192 vectors: 128 KiB (wide_kernel, 16 waves)
+    {512, 16, 4},   // 32768 vectors: 512 KiB (four 512-thread workgroups, two per CU)
 };
 constexpr int kWideShape = 5;
-constexpr int kPairShape = 8;
-constexpr int kWide4Shape = 9;
-constexpr int kWide8Shape = 10;
+constexpr int kPairShape = 6;
+constexpr int kWide4Shape = 7;
+constexpr int kWide8Shape = 8;
+constexpr int kQuadShape = 9;
 constexpr int kSplitShapeSmall = 0;  // split-V chunk shapes
 constexpr int kSplitShapeLarge = 3;
 constexpr int kSplitBlock = 256;     // block of the split-V second stage
@@ -46,8 +46,8 @@ struct Plan {
 };
 
 hipError_t launch_prologue(const cedev::Params& p, hipStream_t st);
-// wide_kernel with nreg VGPR slots per thread and halves (1 or 2)
-// workgroups per row.
+// wide_kernel with nreg VGPR slots per thread and halves (1, 2 or 4)
+// workgroups per row (1024 threads each; 512 for quarter rows).
 hipError_t launch_wide_f32(int nreg, int halves, const cedev::Params& p, hipStream_t st);
 hipError_t launch_wide_bf16(int nreg, int halves, const cedev::Params& p, hipStream_t st);
 hipError_t launch_forward_f32(const Plan& plan, const cedev::Params& p, hipStream_t st);

@@ -33,15 +33,15 @@ hipError_t resident_blocks(K kernel, int block, int* cache, int* out) {
 
 // Persistent row kernel: as many workgroups as fit on the device at once
 // (occupancy x compute units, cached per device), at most one per row.
-template <class E, int SC, int SM, int BLOCK, int NREG, int NLDS>
+template <class E, int SC, int SM, int BLOCK, int NREG>
 hipError_t launch_rows(const Params& p, hipStream_t st) {
   static int cache[64] = {};
   int r = 0;
   const hipError_t e =
-      resident_blocks(cedev::rows_kernel<E, BLOCK, NREG, NLDS, SC, SM>, BLOCK, cache, &r);
+      resident_blocks(cedev::rows_kernel<E, BLOCK, NREG, SC, SM>, BLOCK, cache, &r);
   if (e != hipSuccess) return e;
   const int64_t grid = p.rows < r ? p.rows : r;
-  cedev::rows_kernel<E, BLOCK, NREG, NLDS, SC, SM>
+  cedev::rows_kernel<E, BLOCK, NREG, SC, SM>
       <<<dim3(static_cast<unsigned>(grid)), BLOCK, 0, st>>>(p);
   return hipGetLastError();
 }
@@ -49,17 +49,16 @@ hipError_t launch_rows(const Params& p, hipStream_t st) {
 template <class E, int SC, int SM>
 hipError_t launch_fused(int shape, const Params& p, hipStream_t st) {
   switch (shape) {
-    case 0: return launch_rows<E, SC, SM, 256, 4, 0>(p, st);
-    case 1: return launch_rows<E, SC, SM, 256, 8, 0>(p, st);
-    case 2: return launch_rows<E, SC, SM, 256, 16, 0>(p, st);
-    case 3: return launch_rows<E, SC, SM, 512, 16, 0>(p, st);
-    case 4: return launch_rows<E, SC, SM, 512, 32, 0>(p, st);
-    case 6: return launch_rows<E, SC, SM, 512, 44, 19>(p, st);
-    case 7: return launch_rows<E, SC, SM, 512, 45, 19>(p, st);
+    case 0: return launch_rows<E, SC, SM, 256, 4>(p, st);
+    case 1: return launch_rows<E, SC, SM, 256, 8>(p, st);
+    case 2: return launch_rows<E, SC, SM, 256, 16>(p, st);
+    case 3: return launch_rows<E, SC, SM, 512, 16>(p, st);
+    case 4: return launch_rows<E, SC, SM, 512, 32>(p, st);
     case kWideShape:
     case kPairShape:
     case kWide4Shape:
-    case kWide8Shape: {
+    case kWide8Shape:
+    case kQuadShape: {
       const int halves = kShapes[shape].halves, nreg = kShapes[shape].nreg;
       if constexpr (E::EPV == 4) return launch_wide_f32(nreg, halves, p, st);
       return launch_wide_bf16(nreg, halves, p, st);
@@ -69,33 +68,33 @@ hipError_t launch_fused(int shape, const Params& p, hipStream_t st) {
 }
 
 // wide_kernel launch (instantiated in the ce_inst_*_wide units): persistent,
-// at most one workgroup per part; half rows take an even number of
-// workgroups (fixed pairs 2j, 2j + 1), at least one pair.
-template <class E, int NREG, int HALVES, int SC, int SM>
+// at most one workgroup per part; rows split over G parts take a multiple
+// of G workgroups (fixed groups G j ... G j + G - 1), at least one group.
+template <class E, int BLOCK, int NREG, int HALVES, int SC, int SM>
 hipError_t launch_wide_t(const Params& p, hipStream_t st) {
   static int cache[64] = {};
   int r = 0;
   const hipError_t e =
-      resident_blocks(cedev::wide_kernel<E, NREG, HALVES, SC, SM>, cedev::kWideBlock, cache, &r);
+      resident_blocks(cedev::wide_kernel<E, BLOCK, NREG, HALVES, SC, SM>, BLOCK, cache, &r);
   if (e != hipSuccess) return e;
   const int64_t parts = p.rows * HALVES;
   int64_t grid = parts < r ? parts : r;
-  if (HALVES == 2) grid = grid >= 2 ? (grid & ~static_cast<int64_t>(1)) : 2;
-  cedev::wide_kernel<E, NREG, HALVES, SC, SM>
-      <<<dim3(static_cast<unsigned>(grid)), cedev::kWideBlock, 0, st>>>(p);
+  if (HALVES > 1) grid = grid >= HALVES ? grid - grid % HALVES : HALVES;
+  cedev::wide_kernel<E, BLOCK, NREG, HALVES, SC, SM>
+      <<<dim3(static_cast<unsigned>(grid)), BLOCK, 0, st>>>(p);
   return hipGetLastError();
 }
 
-template <class E, int NREG, int HALVES>
+template <class E, int BLOCK, int NREG, int HALVES>
 hipError_t launch_wide_h(const Params& p, hipStream_t st) {
   const bool sc = p.softcap > 0.0f;
   const bool sm = p.eps > 0.0f;
   if (sc) {
-    return sm ? launch_wide_t<E, NREG, HALVES, 1, 1>(p, st)
-              : launch_wide_t<E, NREG, HALVES, 1, 0>(p, st);
+    return sm ? launch_wide_t<E, BLOCK, NREG, HALVES, 1, 1>(p, st)
+              : launch_wide_t<E, BLOCK, NREG, HALVES, 1, 0>(p, st);
   }
-  return sm ? launch_wide_t<E, NREG, HALVES, 0, 1>(p, st)
-            : launch_wide_t<E, NREG, HALVES, 0, 0>(p, st);
+  return sm ? launch_wide_t<E, BLOCK, NREG, HALVES, 0, 1>(p, st)
+            : launch_wide_t<E, BLOCK, NREG, HALVES, 0, 0>(p, st);
 }
 
 template <class E, int SC, int SM>

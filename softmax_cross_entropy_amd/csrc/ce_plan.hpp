@@ -75,10 +75,8 @@ inline int fused_shape(int64_t nvec, uint32_t flags) {
   if (nvec <= kShapes[2].cap()) return alt ? cehost::kWide4Shape : 2;
   if (nvec <= kShapes[3].cap()) return alt ? 3 : cehost::kWide8Shape;
   if (nvec <= kShapes[4].cap()) return alt ? 4 : cehost::kWideShape;
-  if (nvec <= kShapes[cehost::kPairShape].cap()) {
-    if (!alt) return cehost::kPairShape;
-    return nvec <= kShapes[6].cap() ? 6 : 7;
-  }
+  if (nvec <= kShapes[cehost::kQuadShape].cap())
+    return alt ? cehost::kPairShape : cehost::kQuadShape;
   return -1;
 }
 
@@ -130,7 +128,8 @@ struct Layout {
 // Partials per row: S for split-V, 2 for a row pair, none otherwise.
 inline int plan_partials(const Plan& pl) {
   if (pl.path == CE_PATH_SPLITV) return pl.S;
-  if (pl.path == CE_PATH_FUSED && kShapes[pl.shape].halves == 2) return 4;  // 64 B per half
+  if (pl.path == CE_PATH_FUSED && kShapes[pl.shape].halves > 1)
+    return 2 * kShapes[pl.shape].halves;  // 64 B per part
   return 0;
 }
 

@@ -1,25 +1,26 @@
 // Wide row kernel: rows of up to 16 K 16-byte vectors (256 KiB) per
 // workgroup of 1024 threads, or rows of up to 32 K vectors (512 KiB) split
-// into two halves held by a pair of workgroups. Each workgroup reads its
-// part of the row from HBM once, keeps it in VGPRs (NREG vectors per thread)
-// and writes the gradient over it.
+// into G parts held by a group of workgroups: four quarters on 512-thread
+// workgroups (two per CU), or two halves on 1024-thread ones. Each
+// workgroup reads its part of the row from HBM once, keeps it in VGPRs
+// (NREG vectors per thread) and writes the gradient over it.
 //
 // Same method as fused_row (Liger-Kernel page "Kernel Profile: CrossEntropy
 // (Tier 3 - Fused/Complex)", Key Patterns: online softmax pass, then the
 // gradient written in place of the logits), laid out for the largest rows:
 //  * 16 waves per CU with 16 dwordx4 loads in flight per wave. On MI355X the
 //    in-place read-then-write of a 1023 x 128256 fp32 batch runs at about
-//    5.9 TB/s in this layout (a half row per CU) against 5.2 TB/s with
-//    8 waves of 63 loads holding a whole row per CU (VGPRs + LDS).
-//  * A row of two halves: each workgroup reduces its half to a partial
-//    (max, sum, smoothing sum, argmax), publishes it, and takes the other
-//    half's partial; both combine the two in the same order (half 0 first),
-//    so both get bitwise identical row scalars. Pairs are fixed: workgroups
-//    2j and 2j + 1 take the two halves of one row after another, so a
-//    workgroup only ever waits for its neighbour, which the hardware starts
-//    right after it. Pair j starts with row j; the even workgroup claims the
-//    pair's next row when it starts a row and hands it over with its
-//    partial.
+//    5.9 TB/s with a half row per CU against 5.2 TB/s with 8 waves holding a
+//    whole row per CU (VGPRs + LDS); with quarter rows, two workgroups per
+//    CU, one streams while the other waits for its group.
+//  * A split row: each workgroup reduces its part to a partial (max, sum,
+//    smoothing sum, argmax), publishes it, and folds the G partials in part
+//    order (part 0 first), so all get bitwise identical row scalars. Groups
+//    are fixed: workgroups G j ... G j + G - 1 take the parts of one row
+//    after another, so a workgroup only ever waits for its neighbours, which
+//    the hardware starts right after it. Group j starts with row j; part 0
+//    claims the group's next row when it starts a row and hands it over with
+//    its partial.
 //  * Pass 1 works in groups of 4 slots (fp32; 2 for bf16) with one shift per
 //    group; rows of fp32 logits without softcap keep exp(z - group shift)
 //    in place of the logits, so the gradient pass is one multiply per
@@ -39,41 +40,48 @@ constexpr int kWideSlots = 16;  // VGPR slots per thread of the largest wide sha
 // the launch ends in bounded time.
 constexpr int kPairSpinLimit = 1 << 22;
 
-// Row-pair exchange through the row's two 64-byte slots (one per half).
-// Words 0-4 are a half's partial (max, sum, smoothing sum, largest raw
-// logit, its index); words 5-7, written by half 0 only, are the pair's next
-// row and that row's target (low, high). Each word travels as a 64-bit
-// atomic store of (word, epoch), where the epoch is a number the host makes
-// unique per call: a reader that sees this call's epoch in a pair has that
-// pair's word, with no wait between data and flag on the writer's side.
-// Nothing has to be reset between calls: a slot left by an earlier call
-// carries an older epoch.
+// Exchange within a row's group of G parts (a pair, or four quarters)
+// through the row's G 64-byte slots, one per part. Words 0-4 are a part's
+// partial (max, sum, smoothing sum, largest raw logit, its index); words
+// 5-7, written by part 0 only, are the group's next row and that row's
+// target (low, high). Each word travels as a 64-bit atomic store of
+// (word, epoch), where the epoch is a number the host makes unique per call:
+// a reader that sees this call's epoch in a pair has that pair's word, with
+// no wait between data and flag on the writer's side. Nothing has to be
+// reset between calls: a slot left by an earlier call carries an older
+// epoch.
 constexpr int kPairWords = 5;
 constexpr int kSlotWords = 8;
 
-// Thread 0: publishes words [A, B) of `mine`, then polls words [C, D) of
-// the partner's slot until all carry this call's epoch; returns false if
-// the partner did not publish within `limit` polls.
-template <int A, int B, int C, int D>
-__device__ __forceinline__ bool pair_exchange(const Params& p, int64_t row, int h,
-                                              const uint32_t (&mine)[kSlotWords],
-                                              uint32_t (&other)[kSlotWords], int limit) {
-  uint64_t* slot = reinterpret_cast<uint64_t*>(p.part + row * 4);  // 2 x 64 bytes
+template <int G>
+__device__ __forceinline__ uint64_t* row_slots(const Params& p, int64_t row) {
+  return reinterpret_cast<uint64_t*>(p.part) + row * (G * kSlotWords);
+}
+
+// Thread 0: words [a, b) of `w` into a slot.
+__device__ __forceinline__ void slot_publish(const Params& p, uint64_t* slot,
+                                             const uint32_t (&w)[kSlotWords], int a, int b) {
   const uint64_t ep = static_cast<uint64_t>(p.epoch) << 32;
 #pragma unroll
-  for (int i = A; i < B; ++i)
-    __hip_atomic_store(slot + kSlotWords * h + i, ep | mine[i], __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-  if constexpr (C == D) return true;
-  const uint64_t* osrc = slot + kSlotWords * (1 - h);
+  for (int i = 0; i < kSlotWords; ++i)
+    if (i >= a && i < b)
+      __hip_atomic_store(slot + i, ep | w[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Thread 0: polls words [a, b) of a slot until all carry this call's epoch;
+// false if they did not within `limit` polls.
+__device__ __forceinline__ bool slot_poll(const Params& p, const uint64_t* slot,
+                                          uint32_t (&w)[kSlotWords], int a, int b, int limit) {
   int it = 0;
   while (true) {
     bool all = true;
 #pragma unroll
-    for (int i = C; i < D; ++i) {
-      const uint64_t v = __hip_atomic_load(osrc + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      other[i] = static_cast<uint32_t>(v);
-      all = all && (static_cast<uint32_t>(v >> 32) == p.epoch);
+    for (int i = 0; i < kSlotWords; ++i) {
+      if (i >= a && i < b) {
+        const uint64_t v = __hip_atomic_load(slot + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        w[i] = static_cast<uint32_t>(v);
+        all = all && (static_cast<uint32_t>(v >> 32) == p.epoch);
+      }
     }
     if (all) return true;
     if (++it >= limit) return false;
@@ -82,13 +90,14 @@ __device__ __forceinline__ bool pair_exchange(const Params& p, int64_t row, int 
 }
 
 // Block-shared state of the part in flight.
+template <int BLOCK>
 struct WideShared {
-  Acc acc[kWideBlock / 64];
-  int cand[kWideBlock / 64];
+  Acc acc[BLOCK / 64];
+  int cand[BLOCK / 64];
   RowScalars rs;
   float xy;
   int64_t next_t, next_y;  // the part (whole rows) or row (pairs) next, and its target
-  int limit;               // poll limit of the pair exchange (thread 0 only)
+  int limit;               // poll limit of the group exchange (thread 0 only)
 };
 
 // Whole-row parts are claimed: workgroup b starts with part b; thread 0
@@ -96,12 +105,12 @@ struct WideShared {
 // part's pass 1 is done, so parts go to workgroups in the order they finish.
 // Every part processed takes exactly one claim, so the claim that returns
 // parts - 1 is the launch's last and resets the counter for the next launch.
-// Half rows are not claimed one by one (a workgroup that claimed before
-// waiting for its partner could be handed that partner's half and wait on
-// itself): half 0 of a fixed pair claims whole rows (pairs + the counter)
-// when it starts a row, so it holds its next row before it can wait; the
-// launch makes one claim per row, and the claim that returns rows - 1
-// resets the counter.
+// Parts of a split row are not claimed one by one (a workgroup that claimed
+// before waiting for its partners could be handed a partner's part and wait
+// on itself): part 0 of a fixed group claims whole rows (groups + the
+// counter) when it starts a row, so it holds its next row before it can
+// wait; the launch makes one claim per row, and the claim that returns
+// rows - 1 resets the counter.
 __device__ __forceinline__ uint32_t claim_issue(const Params& p) {
   return __hip_atomic_fetch_add(&p.hdr->next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -115,8 +124,8 @@ __device__ __forceinline__ uint32_t claim_issue_early(const Params& p) {
   return __hip_atomic_fetch_add(&p.hdr->next + zero, 1u, __ATOMIC_RELAXED,
                                 __HIP_MEMORY_SCOPE_AGENT);
 }
-template <int HALVES>
-__device__ __forceinline__ void claim_finish(const Params& p, uint32_t c, WideShared& sh) {
+template <int HALVES, class SH>
+__device__ __forceinline__ void claim_finish(const Params& p, uint32_t c, SH& sh) {
   const int64_t parts = p.rows * HALVES;
   if (c == static_cast<uint32_t>(parts - 1))
     __hip_atomic_store(&p.hdr->next, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -125,14 +134,16 @@ __device__ __forceinline__ void claim_finish(const Params& p, uint32_t c, WideSh
   sh.next_y = nt < parts ? p.target[nt / HALVES] : 0;
 }
 
-// Half 0 of a pair (thread 0): the row a claim `c` stands for (issued when
+// Part 0 of a group (thread 0): the row a claim `c` stands for (issued when
 // the current row started, so its target is read while the row is in
 // flight); the launch's last claim resets the counter.
+template <int G>
 __device__ __forceinline__ int64_t pair_row(const Params& p, uint32_t c) {
-  return static_cast<int64_t>(gridDim.x >> 1) + c;
+  return static_cast<int64_t>(gridDim.x / G) + c;
 }
+template <int G>
 __device__ __forceinline__ int64_t pair_target(const Params& p, uint32_t c) {
-  const int64_t nr = pair_row(p, c);
+  const int64_t nr = pair_row<G>(p, c);
   return nr < p.rows ? p.target[nr] : 0;
 }
 __device__ __forceinline__ void pair_reset(const Params& p, uint32_t c) {
@@ -140,18 +151,18 @@ __device__ __forceinline__ void pair_reset(const Params& p, uint32_t c) {
     __hip_atomic_store(&p.hdr->next, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Thread 0: the pair's next row and its target into the block-shared state
-// (half 1 takes them from half 0's words 5-7; if they never came, the
-// workgroup stops).
+// Thread 0: the group's next row and its target into the block-shared
+// state (the other parts take them from part 0's words 5-7; if they never
+// came, the workgroup stops).
+template <int G, class SH>
 __device__ __forceinline__ void pair_next(const Params& p, int h, bool ok, uint32_t c,
-                                          int64_t ny, const uint32_t (&other)[kSlotWords],
-                                          WideShared& sh) {
+                                          int64_t ny, const uint32_t (&w0)[kSlotWords], SH& sh) {
   if (h == 0) {
-    sh.next_t = pair_row(p, c);
+    sh.next_t = pair_row<G>(p, c);
     sh.next_y = ny;
   } else {
-    sh.next_t = ok ? static_cast<int64_t>(other[5]) : p.rows;
-    sh.next_y = static_cast<int64_t>((static_cast<uint64_t>(other[7]) << 32) | other[6]);
+    sh.next_t = ok ? static_cast<int64_t>(w0[5]) : p.rows;
+    sh.next_y = static_cast<int64_t>((static_cast<uint64_t>(w0[7]) << 32) | w0[6]);
   }
   if (!ok) {
     atomicOr(&p.hdr->err, 2u);
@@ -159,19 +170,21 @@ __device__ __forceinline__ void pair_next(const Params& p, int h, bool ok, uint3
   }
 }
 
-// Half 0's words 5-7: the pair's next row and its target.
+// Part 0's words 5-7: the group's next row and its target.
+template <int G>
 __device__ __forceinline__ void next_words(const Params& p, uint32_t c, int64_t ny,
                                            uint32_t (&w)[kSlotWords]) {
-  w[5] = static_cast<uint32_t>(pair_row(p, c));
+  w[5] = static_cast<uint32_t>(pair_row<G>(p, c));
   w[6] = static_cast<uint32_t>(ny);
   w[7] = static_cast<uint32_t>(static_cast<uint64_t>(ny) >> 32);
 }
 
-// One part (a whole row, or half of one) of the persistent wide kernel.
-template <class E, int NREG, int HALVES, int SC, int SM>
+// One part (a whole row, or a half or quarter of one) of the persistent
+// wide kernel.
+template <class E, int BLOCK, int NREG, int HALVES, int SC, int SM>
 __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
-                                          WideShared& sh, int64_t& next_t, int64_t& next_y) {
-  constexpr int BLOCK = kWideBlock;
+                                          WideShared<BLOCK>& sh, int64_t& next_t,
+                                          int64_t& next_y) {
   constexpr int NW = BLOCK / 64;
   constexpr int EPV = E::EPV;
   constexpr int GS = (EPV == 4) ? 4 : 2;  // slots per pass-1 group
@@ -212,7 +225,7 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
       next_y = uniform_i64(sh.next_y);
     }
     uint32_t claim = 0;
-    if constexpr (HALVES == 2) {
+    if constexpr (HALVES > 1) {
       if (tid == 0 && h == 0) claim = claim_issue(p);
     }
     if (p.grad) {
@@ -220,22 +233,23 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
       for (int j = tid; j < nv; j += BLOCK) __builtin_nontemporal_store(u4{0u, 0u, 0u, 0u}, vp + j);
       if (tid < tail) E::st(rp, tail0 + tid, 0.0f);
     }
-    if constexpr (HALVES == 2) {
-      // no partials to combine: half 0 only hands over the pair's next row
+    if constexpr (HALVES > 1) {
+      // no partials to combine: part 0 only hands over the group's next row
       __syncthreads();  // every thread has read the previous part's next_t
       if (tid == 0) {
-        uint32_t mine_w[kSlotWords] = {}, other_w[kSlotWords] = {};
+        uint32_t w[kSlotWords] = {};
         bool ok = true;
         int64_t ny = 0;
+        uint64_t* slots = row_slots<HALVES>(p, row);
         if (h == 0) {
           pair_reset(p, claim);
-          ny = pair_target(p, claim);
-          next_words(p, claim, ny, mine_w);
-          pair_exchange<5, kSlotWords, 0, 0>(p, row, h, mine_w, other_w, sh.limit);
+          ny = pair_target<HALVES>(p, claim);
+          next_words<HALVES>(p, claim, ny, w);
+          slot_publish(p, slots, w, kPairWords, kSlotWords);
         } else {
-          ok = pair_exchange<0, 0, 5, kSlotWords>(p, row, h, mine_w, other_w, sh.limit);
+          ok = slot_poll(p, slots, w, kPairWords, kSlotWords, sh.limit);
         }
-        pair_next(p, h, ok, claim, ny, other_w, sh);
+        pair_next<HALVES>(p, h, ok, claim, ny, w, sh);
       }
       __syncthreads();
       next_t = uniform_i64(sh.next_t);
@@ -253,9 +267,9 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
     // spanning exactly the part's vectors: lanes past it read 0 and their
     // stores are dropped. Both halves read the target logit before either
     // can write a gradient (each writes only after both have published).
-    // Half 0 of a pair claims the pair's next row before its loads go out.
+    // Part 0 of a group claims the group's next row before its loads go out.
     uint32_t claim = 0;
-    if constexpr (HALVES == 2) {
+    if constexpr (HALVES > 1) {
       if (tid == 0 && h == 0) claim = claim_issue_early(p);
     }
     // The target logit and the row tail as stored, read by every lane of wave
@@ -277,9 +291,9 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
 #pragma unroll
     for (int k = 0; k < NREG; ++k)
       r[k] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, k * BLOCK * 16, kLoadNT);
-    int64_t ny = 0;  // target of the pair's next row (half 0, thread 0)
-    if constexpr (HALVES == 2) {
-      if (tid == 0 && h == 0) ny = pair_target(p, claim);
+    int64_t ny = 0;  // target of the group's next row (part 0, thread 0)
+    if constexpr (HALVES > 1) {
+      if (tid == 0 && h == 0) ny = pair_target<HALVES>(p, claim);
     }
 
     // ---- pass 1, group by group in load order ----
@@ -461,40 +475,95 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
       }
       t.bv = bmax;
       t.bi = arg;
-      if (lane == 0) {
-        if constexpr (HALVES == 1) claim = claim_issue(p);
-        if constexpr (HALVES == 2) {
-          // Exchange partials with the other half (half 0 adds the pair's
-          // next row); both combine half 0 first.
+      if constexpr (HALVES > 1) {
+        // Lane 0 publishes this part's partial (part 0 adds the group's
+        // next row); lanes 0 .. G-1 poll the other parts' slots, one slot
+        // per lane, so the group costs one round trip; then every lane folds
+        // the G partials in part order, part 0 first, so every part of the
+        // row gets bitwise identical row scalars.
+        uint64_t* slots = row_slots<HALVES>(p, row);
+        if (lane == 0) {
           uint32_t mine_w[kSlotWords] = {
               __builtin_bit_cast(uint32_t, t.m), __builtin_bit_cast(uint32_t, t.s),
               __builtin_bit_cast(uint32_t, t.sz), __builtin_bit_cast(uint32_t, t.bv),
               static_cast<uint32_t>(t.bi), 0u, 0u, 0u};
-          uint32_t other_w[kSlotWords] = {};
-          bool ok;
           if (h == 0) {
             pair_reset(p, claim);
-            next_words(p, claim, ny, mine_w);
-            ok = pair_exchange<0, kSlotWords, 0, kPairWords>(p, row, h, mine_w, other_w,
-                                                             sh.limit);
-          } else {
-            ok = pair_exchange<0, kPairWords, 0, kSlotWords>(p, row, h, mine_w, other_w,
-                                                             sh.limit);
+            next_words<HALVES>(p, claim, ny, mine_w);
           }
-          pair_next(p, h, ok, claim, ny, other_w, sh);
-          const uint32_t* q0 = h == 0 ? mine_w : other_w;
-          const uint32_t* q1 = h == 0 ? other_w : mine_w;
-          float m = __builtin_bit_cast(float, q0[0]), sum = __builtin_bit_cast(float, q0[1]);
-          ms_combine(m, sum, __builtin_bit_cast(float, q1[0]), __builtin_bit_cast(float, q1[1]));
-          t.m = m;
-          t.s = sum;
-          t.sz = __builtin_bit_cast(float, q0[2]) + __builtin_bit_cast(float, q1[2]);
-          const float bv0 = __builtin_bit_cast(float, q0[3]);
-          const float bv1 = __builtin_bit_cast(float, q1[3]);
-          const bool take1 = bv1 > bv0;  // ties keep half 0 (the lower indices)
-          t.bv = take1 ? bv1 : bv0;
-          t.bi = static_cast<int>(take1 ? q1[4] : q0[4]);
+          slot_publish(p, slots + kSlotWords * h, mine_w, 0, h == 0 ? kSlotWords : kPairWords);
         }
+        uint32_t w[kSlotWords] = {};
+        const int nwords = lane == 0 ? kSlotWords : kPairWords;
+        bool done = !(lane < HALVES && lane != h);
+        const int limit = sh.limit;
+        int it = 0;
+        while (true) {
+          if (!done) {
+            const uint64_t* src = slots + kSlotWords * lane;
+            bool all = true;
+#pragma unroll
+            for (int i = 0; i < kSlotWords; ++i) {
+              if (i < nwords) {
+                const uint64_t v =
+                    __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                w[i] = static_cast<uint32_t>(v);
+                all = all && (static_cast<uint32_t>(v >> 32) == p.epoch);
+              }
+            }
+            done = all;
+          }
+          if (__all(done)) break;
+          if (++it >= limit) break;
+          __builtin_amdgcn_s_sleep(1);
+        }
+        const bool ok = __all(done);
+        const float own_m = __shfl(t.m, 0, 64), own_s = __shfl(t.s, 0, 64);
+        const float own_z = __shfl(t.sz, 0, 64), own_b = __shfl(t.bv, 0, 64);
+        const int own_i = __shfl(t.bi, 0, 64);
+        float m = 0.0f, sum = 0.0f, sz = 0.0f, bv = 0.0f;
+        int bi = kNoIndex;
+#pragma unroll
+        for (int q = 0; q < HALVES; ++q) {
+          float mq = __builtin_bit_cast(float, __shfl(w[0], q, 64));
+          float sq = __builtin_bit_cast(float, __shfl(w[1], q, 64));
+          float zq = __builtin_bit_cast(float, __shfl(w[2], q, 64));
+          float bq = __builtin_bit_cast(float, __shfl(w[3], q, 64));
+          int iq = static_cast<int>(__shfl(w[4], q, 64));
+          if (q == h) {
+            mq = own_m;
+            sq = own_s;
+            zq = own_z;
+            bq = own_b;
+            iq = own_i;
+          }
+          if (q == 0) {
+            m = mq;
+            sum = sq;
+            sz = zq;
+            bv = bq;
+            bi = iq;
+          } else {
+            ms_combine(m, sum, mq, sq);
+            sz += zq;
+            const bool take = bq > bv;  // ties keep the earlier part (lower indices)
+            bv = take ? bq : bv;
+            bi = take ? iq : bi;
+          }
+        }
+        uint32_t w0[kSlotWords] = {};  // part 0's words 5-7: the next row (parts 1 .. G-1)
+        w0[5] = __shfl(w[5], 0, 64);
+        w0[6] = __shfl(w[6], 0, 64);
+        w0[7] = __shfl(w[7], 0, 64);
+        if (lane == 0) pair_next<HALVES>(p, h, ok, claim, ny, w0, sh);
+        t.m = m;
+        t.s = sum;
+        t.sz = sz;
+        t.bv = bv;
+        t.bi = bi;
+      }
+      if (lane == 0) {
+        if constexpr (HALVES == 1) claim = claim_issue(p);
         if (t.bi == kNoIndex) t.bi = 0;  // no finite or infinite value: index 0
         double W, alpha, beta;
         load_scales(p, W, alpha, beta);
@@ -564,28 +633,31 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
 }
 
 // Persistent: as many workgroups as fit on the device at once (at most one
-// per part; an even number for half rows); each processes parts until the
-// claims run out, then arrives once at the epilogue. The next part's loads
-// are issued as soon as the current part's gradient stores are (they drain
-// while the next part arrives).
-template <class E, int NREG, int HALVES, int SC, int SM>
-__global__ __launch_bounds__(kWideBlock) void wide_kernel(Params p) {
-  static_assert(HALVES == 1 || HALVES == 2, "whole rows or half rows");
-  __shared__ WideShared sh;
+// per part; a multiple of G for rows split over G parts); each processes
+// parts until the claims run out, then arrives once at the epilogue. The
+// next part's loads are issued as soon as the current part's gradient
+// stores are (they drain while the next part arrives).
+// Four waves per SIMD: one 1024-thread workgroup or two 512-thread ones per
+// CU, so at most 128 VGPRs.
+template <class E, int BLOCK, int NREG, int HALVES, int SC, int SM>
+__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void wide_kernel(
+    Params p) {
+  static_assert(HALVES == 1 || HALVES == 2 || HALVES == 4, "whole, half or quarter rows");
+  __shared__ WideShared<BLOCK> sh;
   __shared__ int s_last;
   // self_scales: every workgroup counts n and D once, before its parts
   // (kept out of the part loop, whose registers it would otherwise crowd)
-  if (p.self_scales) compute_self_scales<kWideBlock>(p);
+  if (p.self_scales) compute_self_scales<BLOCK>(p);
   if (threadIdx.x == 0) sh.limit = kPairSpinLimit;
-  if constexpr (HALVES == 2) {
-    // pair j = workgroups 2j, 2j + 1 starts with row j (the grid holds at
-    // most one pair per row)
-    const int h = blockIdx.x & 1;
-    int64_t row = blockIdx.x >> 1;
+  if constexpr (HALVES > 1) {
+    // group j = workgroups G j ... G j + G - 1 starts with row j (the grid
+    // holds at most one group per row)
+    const int h = static_cast<int>(blockIdx.x % HALVES);
+    int64_t row = blockIdx.x / HALVES;
     int64_t y = p.target[row];
     while (row < p.rows) {
       int64_t nr, ny;
-      wide_part<E, NREG, HALVES, SC, SM>(p, 2 * row + h, y, sh, nr, ny);
+      wide_part<E, BLOCK, NREG, HALVES, SC, SM>(p, HALVES * row + h, y, sh, nr, ny);
       row = nr;
       y = ny;
     }
@@ -595,7 +667,7 @@ __global__ __launch_bounds__(kWideBlock) void wide_kernel(Params p) {
     int64_t y = p.target[t];
     while (t < parts) {
       int64_t nt, ny;
-      wide_part<E, NREG, HALVES, SC, SM>(p, t, y, sh, nt, ny);
+      wide_part<E, BLOCK, NREG, HALVES, SC, SM>(p, t, y, sh, nt, ny);
       t = nt;
       y = ny;
     }
@@ -603,7 +675,7 @@ __global__ __launch_bounds__(kWideBlock) void wide_kernel(Params p) {
   if (p.epilogue) {
     if (threadIdx.x == 0) s_last = arrive(p, gridDim.x);
     __syncthreads();
-    if (s_last) epilogue_finish<kWideBlock>(p);
+    if (s_last) epilogue_finish<BLOCK>(p);
   }
 }
 

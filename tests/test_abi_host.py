@@ -146,9 +146,11 @@ def test_workspace_bytes():
     assert base >= 256 and base % 256 == 0
     # header + three per-row arrays, each rounded to 256 bytes
     assert ws(1023, 32768, _lib.CE_F32, 0) == 256 + 3 * 4096
-    # a row pair (rows of 16 K to 32 K vectors) adds two 64-byte exchange slots per
-    # row (rounded to 256 bytes)
-    assert ws(1023, 128256, _lib.CE_F32, 0) == 256 + 3 * 4096 + 1023 * 128 + 128
+    # quarter rows (rows of 16 K to 32 K vectors) add four 64-byte exchange slots
+    # per row, the row pair of the alternative layout two (rounded to 256 bytes)
+    assert ws(1023, 128256, _lib.CE_F32, 0) == 256 + 3 * 4096 + 1023 * 256
+    assert (ws(1023, 128256, _lib.CE_F32, _lib.CE_F_SHAPE_ALT)
+            == 256 + 3 * 4096 + 1023 * 128 + 128)
     # forced split-V adds the (rows, chunks) partials (32 bytes each)
     s = ws(64, 4096, _lib.CE_F32, _lib.CE_F_FORCE_SPLITV)
     assert s == 256 + 3 * 256 + 64 * 4 * 32
