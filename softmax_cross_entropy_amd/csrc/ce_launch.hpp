@@ -22,14 +22,14 @@ constexpr Shape kShapes[kNumShapes] = {
     {256, 16, 1},   // 4096 vectors:  64 KiB
     {512, 16, 1},   // 8192 vectors: 128 KiB
     {512, 32, 1},   // 16384 vectors: 256 KiB
-    {1024, 16, 1},  // 16384 vectors: 256 KiB (wide_kernel, 16 waves)
+    {512, 16, 2},   // 16384 vectors: 256 KiB (row pair of 512-thread workgroups, two per CU)
     {1024, 16, 2},  // 32768 vectors: 512 KiB (row pair of 1024-thread workgroups)
     {1024, 4, 1},   // 4096 vectors:  64 KiB (wide_kernel, 16 waves)
     {1024, 8, 1},   // 8192 vectors: 128 KiB (wide_kernel, 16 waves)
     {512, 16, 4},   // 32768 vectors: 512 KiB (four 512-thread workgroups, two per CU)
 };
-constexpr int kWideShape = 5;
-constexpr int kPairShape = 6;
+constexpr int kPair512Shape = 5;
+constexpr int kPair1024Shape = 6;
 constexpr int kWide4Shape = 7;
 constexpr int kWide8Shape = 8;
 constexpr int kQuadShape = 9;
@@ -46,10 +46,10 @@ struct Plan {
 };
 
 hipError_t launch_prologue(const cedev::Params& p, hipStream_t st);
-// wide_kernel with nreg VGPR slots per thread and halves (1, 2 or 4)
-// workgroups per row (1024 threads each; 512 for quarter rows).
-hipError_t launch_wide_f32(int nreg, int halves, const cedev::Params& p, hipStream_t st);
-hipError_t launch_wide_bf16(int nreg, int halves, const cedev::Params& p, hipStream_t st);
+// wide_kernel with block threads, nreg VGPR slots per thread and halves
+// (1, 2 or 4) workgroups per row: one of the wide shapes of kShapes.
+hipError_t launch_wide_f32(const Shape& s, const cedev::Params& p, hipStream_t st);
+hipError_t launch_wide_bf16(const Shape& s, const cedev::Params& p, hipStream_t st);
 hipError_t launch_forward_f32(const Plan& plan, const cedev::Params& p, hipStream_t st);
 hipError_t launch_forward_bf16(const Plan& plan, const cedev::Params& p, hipStream_t st);
 hipError_t launch_recompute_f32(const cedev::Params& p, void* grad, int64_t grad_stride,

@@ -54,15 +54,13 @@ hipError_t launch_fused(int shape, const Params& p, hipStream_t st) {
     case 2: return launch_rows<E, SC, SM, 256, 16>(p, st);
     case 3: return launch_rows<E, SC, SM, 512, 16>(p, st);
     case 4: return launch_rows<E, SC, SM, 512, 32>(p, st);
-    case kWideShape:
-    case kPairShape:
+    case kPair512Shape:
+    case kPair1024Shape:
     case kWide4Shape:
     case kWide8Shape:
-    case kQuadShape: {
-      const int halves = kShapes[shape].halves, nreg = kShapes[shape].nreg;
-      if constexpr (E::EPV == 4) return launch_wide_f32(nreg, halves, p, st);
-      return launch_wide_bf16(nreg, halves, p, st);
-    }
+    case kQuadShape:
+      if constexpr (E::EPV == 4) return launch_wide_f32(kShapes[shape], p, st);
+      return launch_wide_bf16(kShapes[shape], p, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -31,8 +31,6 @@
 
 namespace cedev {
 
-constexpr int kWideBlock = 1024;
-constexpr int kWideSlots = 16;  // VGPR slots per thread of the largest wide shapes
 // Polls of the partner's words before a pair gives up and flags the row
 // (each poll is one device-coherent load, about a microsecond); a partner
 // that never arrives would otherwise hold the workgroup forever. After one
