@@ -25,13 +25,13 @@ constexpr Shape kShapes[kNumShapes] = {
     {512, 16, 2},   // 16384 vectors: 256 KiB (row pair of 512-thread workgroups, two per CU)
     {1024, 16, 2},  // 32768 vectors: 512 KiB (row pair of 1024-thread workgroups)
     {1024, 4, 1},   // 4096 vectors:  64 KiB (wide_kernel, 16 waves)
-    {1024, 8, 1},   // 8192 vectors: 128 KiB (wide_kernel, 16 waves)
+    {512, 8, 2},    // 8192 vectors: 128 KiB (row pair of 512-thread workgroups, two per CU)
     {512, 16, 4},   // 32768 vectors: 512 KiB (four 512-thread workgroups, two per CU)
 };
 constexpr int kPair512Shape = 5;
 constexpr int kPair1024Shape = 6;
 constexpr int kWide4Shape = 7;
-constexpr int kWide8Shape = 8;
+constexpr int kPair8Shape = 8;
 constexpr int kQuadShape = 9;
 constexpr int kSplitShapeSmall = 0;  // split-V chunk shapes
 constexpr int kSplitShapeLarge = 3;

@@ -57,7 +57,7 @@ hipError_t launch_fused(int shape, const Params& p, hipStream_t st) {
     case kPair512Shape:
     case kPair1024Shape:
     case kWide4Shape:
-    case kWide8Shape:
+    case kPair8Shape:
     case kQuadShape:
       if constexpr (E::EPV == 4) return launch_wide_f32(kShapes[shape], p, st);
       return launch_wide_bf16(kShapes[shape], p, st);

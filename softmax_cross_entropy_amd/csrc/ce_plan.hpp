@@ -73,7 +73,7 @@ inline int fused_shape(int64_t nvec, uint32_t flags) {
   for (int s = 0; s <= 1; ++s)
     if (nvec <= kShapes[s].cap()) return s;
   if (nvec <= kShapes[2].cap()) return alt ? cehost::kWide4Shape : 2;
-  if (nvec <= kShapes[3].cap()) return alt ? 3 : cehost::kWide8Shape;
+  if (nvec <= kShapes[3].cap()) return alt ? 3 : cehost::kPair8Shape;
   if (nvec <= kShapes[4].cap()) return alt ? 4 : cehost::kPair512Shape;
   if (nvec <= kShapes[cehost::kQuadShape].cap())
     return alt ? cehost::kPair1024Shape : cehost::kQuadShape;

@@ -145,7 +145,10 @@ def test_workspace_bytes():
     base = ws(0, 16, _lib.CE_F32, 0)
     assert base >= 256 and base % 256 == 0
     # header + three per-row arrays, each rounded to 256 bytes
-    assert ws(1023, 32768, _lib.CE_F32, 0) == 256 + 3 * 4096
+    assert ws(1023, 16384, _lib.CE_F32, 0) == 256 + 3 * 4096
+    # rows of 4 K to 16 K vectors on a pair of workgroups add two 64-byte
+    # exchange slots per row
+    assert ws(1023, 32768, _lib.CE_F32, 0) == 256 + 3 * 4096 + 1023 * 128 + 128
     # quarter rows (rows of 16 K to 32 K vectors) add four 64-byte exchange slots
     # per row, the row pair of the alternative layout two (rounded to 256 bytes)
     assert ws(1023, 128256, _lib.CE_F32, 0) == 256 + 3 * 4096 + 1023 * 256
