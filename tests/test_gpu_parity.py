@@ -378,20 +378,20 @@ def test_determinism_bitwise():
 SHAPE_CASES = [
     # (dtype, V, rows, options): V picks the shape (the default layout / the
     # CE_F_SHAPE_ALT one where a row size has two); rows exceed the resident
-    # grid, so persistent workgroups claim rows (or half rows) as they finish
+    # grid, so persistent workgroups claim rows as they finish
     (torch.float32, 4001, 2600, dict()),                              # 256 x 4
-    (torch.float32, 16001, 1100, dict(eps=0.1, lam=1e-3)),            # 256 x 16
-    (torch.float32, 65001, 300, dict(weight=True, eps=0.05)),         # 1024 x 16 / 512 x 32
-    (torch.float32, 129001, 300, dict(lam=1e-4)),                     # row pair / 512 x (45 + 19)
+    (torch.float32, 16001, 1100, dict(eps=0.1, lam=1e-3)),            # 256 x 16 / 1024 x 4
+    (torch.float32, 65001, 300, dict(weight=True, eps=0.05)),         # 512 x 16 pair / 512 x 32
+    (torch.float32, 129001, 300, dict(lam=1e-4)),                     # quarters / 1024 x 16 pair
     (torch.bfloat16, 16001, 2600, dict(softcap=20.0)),                # 256 x 8
-    (torch.bfloat16, 65001, 600, dict()),                             # 512 x 16
+    (torch.bfloat16, 65001, 600, dict()),                             # 512 x 8 pair / 512 x 16
     (torch.bfloat16, 131001, 300, dict(weight=True, eps=0.1, softcap=30.0, lam=1e-4)),
     # the largest shapes with every per-element option (fewer rows: oracle time)
-    (torch.float32, 130001, 40, dict(weight=True, eps=0.1, softcap=15.0)),    # pair / 45 + 19
-    (torch.bfloat16, 250001, 40, dict(eps=0.1, softcap=30.0, lam=1e-4)),      # pair / 44 + 19
-    (torch.bfloat16, 262001, 24, dict(weight=True, eps=0.2)),                 # pair / 45 + 19
-    # row pairs: argmax and target in either half, a tie across the halves,
-    # small logits (|max| < 2: the argmax re-reads raw logits), no row tail
+    (torch.float32, 130001, 40, dict(weight=True, eps=0.1, softcap=15.0)),    # quarters / pair
+    (torch.bfloat16, 250001, 40, dict(eps=0.1, softcap=30.0, lam=1e-4)),      # quarters / pair
+    (torch.bfloat16, 262001, 24, dict(weight=True, eps=0.2)),                 # quarters / pair
+    # split rows: argmax and target in any part, a tie across parts, small
+    # logits (|max| < 2: the argmax re-reads raw logits), no row tail
     (torch.float32, 128256, 64, dict(sigma=0.3, tie=1.5)),
     (torch.bfloat16, 262144, 48, dict(sigma=0.5, tie=4.0)),
 ]
@@ -406,8 +406,8 @@ def test_fused_shapes_many_rows(case, reduction, layout):
     x = synth.make_logits(rows, V, dtype, o.get("sigma", 2.5), seed)
     t = synth.make_targets(rows, V, seed, rows * 3 // 10)
     if o.get("tie"):
-        # equal maxima in both halves of every other row (first one in half 0),
-        # the single maximum in the second half of the rest
+        # equal maxima in the first and the last part of every other row (the
+        # first one must win), the single maximum in the last part of the rest
         for r in range(rows):
             x[r, V - 5] = o["tie"]
             if r % 2 == 0:
@@ -420,6 +420,30 @@ def test_fused_shapes_many_rows(case, reduction, layout):
     run_case(x, t, weight=wt, eps=o.get("eps", 0.0), lam=o.get("lam", 0.0),
              softcap=o.get("softcap"), reduction=reduction, path=layout, stride=stride,
              name=f"shape-{case}")
+
+
+# Rows split over a group of workgroups (pairs, quarters) with fewer rows than
+# the resident grid holds: the grid shrinks to rows x G workgroups, a
+# multiple of G, and each group's part 0 still claims the next row (none).
+SPLIT_CASES = [
+    (torch.float32, 24001),    # 6000 vectors: 512 x 8 pair / 512 x 16 row kernel
+    (torch.float32, 50001),    # 12500: 512 x 16 pair / 512 x 32 row kernel
+    (torch.float32, 120001),   # 30000: quarter rows / 1024 x 16 pair
+    (torch.bfloat16, 250001),  # 31250: quarter rows / 1024 x 16 pair
+]
+
+
+@pytest.mark.parametrize("case", range(len(SPLIT_CASES)))
+@pytest.mark.parametrize("rows", [1, 2, 5])
+@pytest.mark.parametrize("layout", ["fused", "fused_alt"])
+def test_split_rows_few_rows(case, rows, layout):
+    dtype, V = SPLIT_CASES[case]
+    seed = 300 + 10 * case + rows
+    x = synth.make_logits(rows, V, dtype, 2.0, seed)
+    t = synth.make_targets(rows, V, seed, 1 if rows == 5 else 0)
+    stride = (V + 7) // 8 * 8  # 16-byte aligned rows: the vector path
+    run_case(x, t, eps=0.1, reduction="none", path=layout, stride=stride,
+             name=f"split-{case}")
 
 
 @pytest.mark.parametrize("alt", [False, True])
