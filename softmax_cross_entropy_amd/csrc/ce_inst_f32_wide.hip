@@ -5,8 +5,8 @@
 
 namespace cehost {
 hipError_t launch_wide_f32(const Shape& s, const cedev::Params& p, hipStream_t st) {
-  if (s.halves == 4) return launch_wide_h<cedev::F32, 512, 16, 4>(p, st);
-  if (s.halves == 2) {
+  if (s.parts == 4) return launch_wide_h<cedev::F32, 512, 16, 4>(p, st);
+  if (s.parts == 2) {
     if (s.block == 1024) return launch_wide_h<cedev::F32, 1024, 16, 2>(p, st);
     return s.nreg == 8 ? launch_wide_h<cedev::F32, 512, 8, 2>(p, st)
                        : launch_wide_h<cedev::F32, 512, 16, 2>(p, st);

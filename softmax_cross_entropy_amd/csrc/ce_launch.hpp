@@ -9,11 +9,11 @@
 namespace cehost {
 
 // Fused row shapes: BLOCK threads, each holding NREG vectors in VGPRs,
-// HALVES workgroups per row (2: a row pair of wide_kernel, 4: four quarter
-// rows); capacity = BLOCK * NREG * HALVES 16-byte vectors per row.
+// PARTS workgroups per row (2: a row pair of wide_kernel, 4: four quarter
+// rows); capacity = BLOCK * NREG * PARTS 16-byte vectors per row.
 struct Shape {
-  int block, nreg, halves;
-  int cap() const { return block * nreg * halves; }
+  int block, nreg, parts;
+  int cap() const { return block * nreg * parts; }
 };
 constexpr int kNumShapes = 10;
 constexpr Shape kShapes[kNumShapes] = {
@@ -46,7 +46,7 @@ struct Plan {
 };
 
 hipError_t launch_prologue(const cedev::Params& p, hipStream_t st);
-// wide_kernel with block threads, nreg VGPR slots per thread and halves
+// wide_kernel with block threads, nreg VGPR slots per thread and parts
 // (1, 2 or 4) workgroups per row: one of the wide shapes of kShapes.
 hipError_t launch_wide_f32(const Shape& s, const cedev::Params& p, hipStream_t st);
 hipError_t launch_wide_bf16(const Shape& s, const cedev::Params& p, hipStream_t st);

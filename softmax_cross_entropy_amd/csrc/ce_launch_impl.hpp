@@ -68,31 +68,31 @@ hipError_t launch_fused(int shape, const Params& p, hipStream_t st) {
 // wide_kernel launch (instantiated in the ce_inst_*_wide units): persistent,
 // at most one workgroup per part; rows split over G parts take a multiple
 // of G workgroups (fixed groups G j ... G j + G - 1), at least one group.
-template <class E, int BLOCK, int NREG, int HALVES, int SC, int SM>
+template <class E, int BLOCK, int NREG, int PARTS, int SC, int SM>
 hipError_t launch_wide_t(const Params& p, hipStream_t st) {
   static int cache[64] = {};
   int r = 0;
   const hipError_t e =
-      resident_blocks(cedev::wide_kernel<E, BLOCK, NREG, HALVES, SC, SM>, BLOCK, cache, &r);
+      resident_blocks(cedev::wide_kernel<E, BLOCK, NREG, PARTS, SC, SM>, BLOCK, cache, &r);
   if (e != hipSuccess) return e;
-  const int64_t parts = p.rows * HALVES;
+  const int64_t parts = p.rows * PARTS;
   int64_t grid = parts < r ? parts : r;
-  if (HALVES > 1) grid = grid >= HALVES ? grid - grid % HALVES : HALVES;
-  cedev::wide_kernel<E, BLOCK, NREG, HALVES, SC, SM>
+  if (PARTS > 1) grid = grid >= PARTS ? grid - grid % PARTS : PARTS;
+  cedev::wide_kernel<E, BLOCK, NREG, PARTS, SC, SM>
       <<<dim3(static_cast<unsigned>(grid)), BLOCK, 0, st>>>(p);
   return hipGetLastError();
 }
 
-template <class E, int BLOCK, int NREG, int HALVES>
+template <class E, int BLOCK, int NREG, int PARTS>
 hipError_t launch_wide_h(const Params& p, hipStream_t st) {
   const bool sc = p.softcap > 0.0f;
   const bool sm = p.eps > 0.0f;
   if (sc) {
-    return sm ? launch_wide_t<E, BLOCK, NREG, HALVES, 1, 1>(p, st)
-              : launch_wide_t<E, BLOCK, NREG, HALVES, 1, 0>(p, st);
+    return sm ? launch_wide_t<E, BLOCK, NREG, PARTS, 1, 1>(p, st)
+              : launch_wide_t<E, BLOCK, NREG, PARTS, 1, 0>(p, st);
   }
-  return sm ? launch_wide_t<E, BLOCK, NREG, HALVES, 0, 1>(p, st)
-            : launch_wide_t<E, BLOCK, NREG, HALVES, 0, 0>(p, st);
+  return sm ? launch_wide_t<E, BLOCK, NREG, PARTS, 0, 1>(p, st)
+            : launch_wide_t<E, BLOCK, NREG, PARTS, 0, 0>(p, st);
 }
 
 template <class E, int SC, int SM>

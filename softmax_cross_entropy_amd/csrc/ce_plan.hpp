@@ -128,8 +128,8 @@ struct Layout {
 // Partials per row: S for split-V, 2 for a row pair, none otherwise.
 inline int plan_partials(const Plan& pl) {
   if (pl.path == CE_PATH_SPLITV) return pl.S;
-  if (pl.path == CE_PATH_FUSED && kShapes[pl.shape].halves > 1)
-    return 2 * kShapes[pl.shape].halves;  // 64 B per part
+  if (pl.path == CE_PATH_FUSED && kShapes[pl.shape].parts > 1)
+    return 2 * kShapes[pl.shape].parts;  // 64 B per part
   return 0;
 }
 

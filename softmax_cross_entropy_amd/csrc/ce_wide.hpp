@@ -1,7 +1,7 @@
 // Wide row kernel: rows of up to 16 K 16-byte vectors (256 KiB) per
 // workgroup of 1024 threads, or rows of up to 32 K vectors (512 KiB) split
 // into G parts held by a group of workgroups: four quarters on 512-thread
-// workgroups (two per CU), or two halves on 1024-thread ones. Each
+// workgroups (two per CU), or two halves on 512- or 1024-thread ones. Each
 // workgroup reads its part of the row from HBM once, keeps it in VGPRs
 // (NREG vectors per thread) and writes the gradient over it.
 //
@@ -31,12 +31,12 @@
 
 namespace cedev {
 
-// Polls of the partner's words before a pair gives up and flags the row
-// (each poll is one device-coherent load, about a microsecond); a partner
-// that never arrives would otherwise hold the workgroup forever. After one
+// Polls of the other parts' words before a group gives up and flags the row
+// (each poll is one device-coherent load, about a microsecond); a part that
+// never arrives would otherwise hold the workgroup forever. After one
 // such failure the workgroup polls once per row: the error bit is set and
 // the launch ends in bounded time.
-constexpr int kPairSpinLimit = 1 << 22;
+constexpr int kGroupSpinLimit = 1 << 22;
 
 // Exchange within a row's group of G parts (a pair, or four quarters)
 // through the row's G 64-byte slots, one per part. Words 0-4 are a part's
@@ -48,7 +48,7 @@ constexpr int kPairSpinLimit = 1 << 22;
 // no wait between data and flag on the writer's side. Nothing has to be
 // reset between calls: a slot left by an earlier call carries an older
 // epoch.
-constexpr int kPairWords = 5;
+constexpr int kPartialWords = 5;
 constexpr int kSlotWords = 8;
 
 template <int G>
@@ -94,7 +94,7 @@ struct WideShared {
   int cand[BLOCK / 64];
   RowScalars rs;
   float xy;
-  int64_t next_t, next_y;  // the part (whole rows) or row (pairs) next, and its target
+  int64_t next_t, next_y;  // the part (whole rows) or row (split rows) next, and its target
   int limit;               // poll limit of the group exchange (thread 0 only)
 };
 
@@ -122,29 +122,29 @@ __device__ __forceinline__ uint32_t claim_issue_early(const Params& p) {
   return __hip_atomic_fetch_add(&p.hdr->next + zero, 1u, __ATOMIC_RELAXED,
                                 __HIP_MEMORY_SCOPE_AGENT);
 }
-template <int HALVES, class SH>
+template <int PARTS, class SH>
 __device__ __forceinline__ void claim_finish(const Params& p, uint32_t c, SH& sh) {
-  const int64_t parts = p.rows * HALVES;
+  const int64_t parts = p.rows * PARTS;
   if (c == static_cast<uint32_t>(parts - 1))
     __hip_atomic_store(&p.hdr->next, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int64_t nt = static_cast<int64_t>(gridDim.x) + c;
   sh.next_t = nt;
-  sh.next_y = nt < parts ? p.target[nt / HALVES] : 0;
+  sh.next_y = nt < parts ? p.target[nt / PARTS] : 0;
 }
 
 // Part 0 of a group (thread 0): the row a claim `c` stands for (issued when
 // the current row started, so its target is read while the row is in
 // flight); the launch's last claim resets the counter.
 template <int G>
-__device__ __forceinline__ int64_t pair_row(const Params& p, uint32_t c) {
+__device__ __forceinline__ int64_t group_row(const Params& p, uint32_t c) {
   return static_cast<int64_t>(gridDim.x / G) + c;
 }
 template <int G>
-__device__ __forceinline__ int64_t pair_target(const Params& p, uint32_t c) {
-  const int64_t nr = pair_row<G>(p, c);
+__device__ __forceinline__ int64_t group_target(const Params& p, uint32_t c) {
+  const int64_t nr = group_row<G>(p, c);
   return nr < p.rows ? p.target[nr] : 0;
 }
-__device__ __forceinline__ void pair_reset(const Params& p, uint32_t c) {
+__device__ __forceinline__ void group_reset(const Params& p, uint32_t c) {
   if (c == static_cast<uint32_t>(p.rows - 1))
     __hip_atomic_store(&p.hdr->next, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -153,10 +153,10 @@ __device__ __forceinline__ void pair_reset(const Params& p, uint32_t c) {
 // state (the other parts take them from part 0's words 5-7; if they never
 // came, the workgroup stops).
 template <int G, class SH>
-__device__ __forceinline__ void pair_next(const Params& p, int h, bool ok, uint32_t c,
+__device__ __forceinline__ void group_next(const Params& p, int h, bool ok, uint32_t c,
                                           int64_t ny, const uint32_t (&w0)[kSlotWords], SH& sh) {
   if (h == 0) {
-    sh.next_t = pair_row<G>(p, c);
+    sh.next_t = group_row<G>(p, c);
     sh.next_y = ny;
   } else {
     sh.next_t = ok ? static_cast<int64_t>(w0[5]) : p.rows;
@@ -172,14 +172,14 @@ __device__ __forceinline__ void pair_next(const Params& p, int h, bool ok, uint3
 template <int G>
 __device__ __forceinline__ void next_words(const Params& p, uint32_t c, int64_t ny,
                                            uint32_t (&w)[kSlotWords]) {
-  w[5] = static_cast<uint32_t>(pair_row<G>(p, c));
+  w[5] = static_cast<uint32_t>(group_row<G>(p, c));
   w[6] = static_cast<uint32_t>(ny);
   w[7] = static_cast<uint32_t>(static_cast<uint64_t>(ny) >> 32);
 }
 
 // One part (a whole row, or a half or quarter of one) of the persistent
 // wide kernel.
-template <class E, int BLOCK, int NREG, int HALVES, int SC, int SM>
+template <class E, int BLOCK, int NREG, int PARTS, int SC, int SM>
 __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
                                           WideShared<BLOCK>& sh, int64_t& next_t,
                                           int64_t& next_y) {
@@ -191,8 +191,8 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
   Acc* s_acc = sh.acc;
   int* s_cand = sh.cand;
 
-  const int64_t row = t / HALVES;
-  const int h = HALVES == 1 ? 0 : static_cast<int>(t % HALVES);
+  const int64_t row = t / PARTS;
+  const int h = PARTS == 1 ? 0 : static_cast<int>(t % PARTS);
   // Opaque per part: values derived from the thread index are recomputed per
   // part instead of being kept live across the loop.
   int tid = threadIdx.x;
@@ -203,10 +203,10 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
   const bool bad = !ignored && (y < 0 || y >= p.V);
   char* rp = row_ptr(p, row, E::BYTES);
   const int nv_row = static_cast<int>(p.V / EPV);
-  const int half = (nv_row + HALVES - 1) / HALVES;
+  const int half = (nv_row + PARTS - 1) / PARTS;
   const int v0 = h * half;
   const int nv = max(0, min(half, nv_row - v0));  // vectors of this part
-  const bool last = (h == HALVES - 1);
+  const bool last = (h == PARTS - 1);
   const int tail = last ? static_cast<int>(p.V - static_cast<int64_t>(nv_row) * EPV) : 0;
   const int64_t tail0 = static_cast<int64_t>(nv_row) * EPV;
   char* hp = rp + static_cast<int64_t>(v0) * 16;  // this part's first vector
@@ -215,15 +215,15 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
   if (ignored || bad) {
     // Ignored rows are never read; their gradient is exactly +0.0
     // (tt-mlir PR #9324 page: ignored rows, also with non-finite logits).
-    if constexpr (HALVES == 1) {
+    if constexpr (PARTS == 1) {
       __syncthreads();  // every thread has read the previous part's next_t
-      if (tid == 0) claim_finish<HALVES>(p, claim_issue(p), sh);
+      if (tid == 0) claim_finish<PARTS>(p, claim_issue(p), sh);
       __syncthreads();
       next_t = uniform_i64(sh.next_t);
       next_y = uniform_i64(sh.next_y);
     }
     uint32_t claim = 0;
-    if constexpr (HALVES > 1) {
+    if constexpr (PARTS > 1) {
       if (tid == 0 && h == 0) claim = claim_issue(p);
     }
     if (p.grad) {
@@ -231,23 +231,23 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
       for (int j = tid; j < nv; j += BLOCK) __builtin_nontemporal_store(u4{0u, 0u, 0u, 0u}, vp + j);
       if (tid < tail) E::st(rp, tail0 + tid, 0.0f);
     }
-    if constexpr (HALVES > 1) {
+    if constexpr (PARTS > 1) {
       // no partials to combine: part 0 only hands over the group's next row
       __syncthreads();  // every thread has read the previous part's next_t
       if (tid == 0) {
         uint32_t w[kSlotWords] = {};
         bool ok = true;
         int64_t ny = 0;
-        uint64_t* slots = row_slots<HALVES>(p, row);
+        uint64_t* slots = row_slots<PARTS>(p, row);
         if (h == 0) {
-          pair_reset(p, claim);
-          ny = pair_target<HALVES>(p, claim);
-          next_words<HALVES>(p, claim, ny, w);
-          slot_publish(p, slots, w, kPairWords, kSlotWords);
+          group_reset(p, claim);
+          ny = group_target<PARTS>(p, claim);
+          next_words<PARTS>(p, claim, ny, w);
+          slot_publish(p, slots, w, kPartialWords, kSlotWords);
         } else {
-          ok = slot_poll(p, slots, w, kPairWords, kSlotWords, sh.limit);
+          ok = slot_poll(p, slots, w, kPartialWords, kSlotWords, sh.limit);
         }
-        pair_next<HALVES>(p, h, ok, claim, ny, w, sh);
+        group_next<PARTS>(p, h, ok, claim, ny, w, sh);
       }
       __syncthreads();
       next_t = uniform_i64(sh.next_t);
@@ -263,11 +263,11 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
     // ---- every load of this part, issued up front ----
     // Non-temporal buffer loads (each logit is read once) over a descriptor
     // spanning exactly the part's vectors: lanes past it read 0 and their
-    // stores are dropped. Both halves read the target logit before either
-    // can write a gradient (each writes only after both have published).
+    // stores are dropped. Every part reads the target logit before any
+    // can write a gradient (each writes only after all have published).
     // Part 0 of a group claims the group's next row before its loads go out.
     uint32_t claim = 0;
-    if constexpr (HALVES > 1) {
+    if constexpr (PARTS > 1) {
       if (tid == 0 && h == 0) claim = claim_issue_early(p);
     }
     // The target logit and the row tail as stored, read by every lane of wave
@@ -290,8 +290,8 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
     for (int k = 0; k < NREG; ++k)
       r[k] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, k * BLOCK * 16, kLoadNT);
     int64_t ny = 0;  // target of the group's next row (part 0, thread 0)
-    if constexpr (HALVES > 1) {
-      if (tid == 0 && h == 0) ny = pair_target<HALVES>(p, claim);
+    if constexpr (PARTS > 1) {
+      if (tid == 0 && h == 0) ny = group_target<PARTS>(p, claim);
     }
 
     // ---- pass 1, group by group in load order ----
@@ -473,27 +473,27 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
       }
       t.bv = bmax;
       t.bi = arg;
-      if constexpr (HALVES > 1) {
+      if constexpr (PARTS > 1) {
         // Lane 0 publishes this part's partial (part 0 adds the group's
         // next row); lanes 0 .. G-1 poll the other parts' slots, one slot
         // per lane, so the group costs one round trip; then every lane folds
         // the G partials in part order, part 0 first, so every part of the
         // row gets bitwise identical row scalars.
-        uint64_t* slots = row_slots<HALVES>(p, row);
+        uint64_t* slots = row_slots<PARTS>(p, row);
         if (lane == 0) {
           uint32_t mine_w[kSlotWords] = {
               __builtin_bit_cast(uint32_t, t.m), __builtin_bit_cast(uint32_t, t.s),
               __builtin_bit_cast(uint32_t, t.sz), __builtin_bit_cast(uint32_t, t.bv),
               static_cast<uint32_t>(t.bi), 0u, 0u, 0u};
           if (h == 0) {
-            pair_reset(p, claim);
-            next_words<HALVES>(p, claim, ny, mine_w);
+            group_reset(p, claim);
+            next_words<PARTS>(p, claim, ny, mine_w);
           }
-          slot_publish(p, slots + kSlotWords * h, mine_w, 0, h == 0 ? kSlotWords : kPairWords);
+          slot_publish(p, slots + kSlotWords * h, mine_w, 0, h == 0 ? kSlotWords : kPartialWords);
         }
         uint32_t w[kSlotWords] = {};
-        const int nwords = lane == 0 ? kSlotWords : kPairWords;
-        bool done = !(lane < HALVES && lane != h);
+        const int nwords = lane == 0 ? kSlotWords : kPartialWords;
+        bool done = !(lane < PARTS && lane != h);
         const int limit = sh.limit;
         int it = 0;
         while (true) {
@@ -522,7 +522,7 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
         float m = 0.0f, sum = 0.0f, sz = 0.0f, bv = 0.0f;
         int bi = kNoIndex;
 #pragma unroll
-        for (int q = 0; q < HALVES; ++q) {
+        for (int q = 0; q < PARTS; ++q) {
           float mq = __builtin_bit_cast(float, __shfl(w[0], q, 64));
           float sq = __builtin_bit_cast(float, __shfl(w[1], q, 64));
           float zq = __builtin_bit_cast(float, __shfl(w[2], q, 64));
@@ -553,7 +553,7 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
         w0[5] = __shfl(w[5], 0, 64);
         w0[6] = __shfl(w[6], 0, 64);
         w0[7] = __shfl(w[7], 0, 64);
-        if (lane == 0) pair_next<HALVES>(p, h, ok, claim, ny, w0, sh);
+        if (lane == 0) group_next<PARTS>(p, h, ok, claim, ny, w0, sh);
         t.m = m;
         t.s = sum;
         t.sz = sz;
@@ -561,7 +561,7 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
         t.bi = bi;
       }
       if (lane == 0) {
-        if constexpr (HALVES == 1) claim = claim_issue(p);
+        if constexpr (PARTS == 1) claim = claim_issue(p);
         if (t.bi == kNoIndex) t.bi = 0;  // no finite or infinite value: index 0
         double W, alpha, beta;
         load_scales(p, W, alpha, beta);
@@ -572,7 +572,7 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
         rs.ok = (t.bi == y);
         sh.rs = rs;
         sh.xy = E::widen(xy_raw);
-        if constexpr (HALVES == 1) claim_finish<HALVES>(p, claim, sh);
+        if constexpr (PARTS == 1) claim_finish<PARTS>(p, claim, sh);
         if (h == 0) {
           write_row_outputs(p, row, rs.ce, rs.zl, rs.ok, t.bi);
           write_row_stats(p, row, rs.m, rs.l2s);
@@ -637,25 +637,25 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
 // stores are (they drain while the next part arrives).
 // Four waves per SIMD: one 1024-thread workgroup or two 512-thread ones per
 // CU, so at most 128 VGPRs.
-template <class E, int BLOCK, int NREG, int HALVES, int SC, int SM>
+template <class E, int BLOCK, int NREG, int PARTS, int SC, int SM>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void wide_kernel(
     Params p) {
-  static_assert(HALVES == 1 || HALVES == 2 || HALVES == 4, "whole, half or quarter rows");
+  static_assert(PARTS == 1 || PARTS == 2 || PARTS == 4, "whole, half or quarter rows");
   __shared__ WideShared<BLOCK> sh;
   __shared__ int s_last;
   // self_scales: every workgroup counts n and D once, before its parts
   // (kept out of the part loop, whose registers it would otherwise crowd)
   if (p.self_scales) compute_self_scales<BLOCK>(p);
-  if (threadIdx.x == 0) sh.limit = kPairSpinLimit;
-  if constexpr (HALVES > 1) {
+  if (threadIdx.x == 0) sh.limit = kGroupSpinLimit;
+  if constexpr (PARTS > 1) {
     // group j = workgroups G j ... G j + G - 1 starts with row j (the grid
     // holds at most one group per row)
-    const int h = static_cast<int>(blockIdx.x % HALVES);
-    int64_t row = blockIdx.x / HALVES;
+    const int h = static_cast<int>(blockIdx.x % PARTS);
+    int64_t row = blockIdx.x / PARTS;
     int64_t y = p.target[row];
     while (row < p.rows) {
       int64_t nr, ny;
-      wide_part<E, BLOCK, NREG, HALVES, SC, SM>(p, HALVES * row + h, y, sh, nr, ny);
+      wide_part<E, BLOCK, NREG, PARTS, SC, SM>(p, PARTS * row + h, y, sh, nr, ny);
       row = nr;
       y = ny;
     }
@@ -665,7 +665,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
     int64_t y = p.target[t];
     while (t < parts) {
       int64_t nt, ny;
-      wide_part<E, BLOCK, NREG, HALVES, SC, SM>(p, t, y, sh, nt, ny);
+      wide_part<E, BLOCK, NREG, PARTS, SC, SM>(p, t, y, sh, nt, ny);
       t = nt;
       y = ny;
     }
