@@ -323,7 +323,7 @@ def main(argv=None) -> int:
 
     if a.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (the path shards "
-              "by rows with no communication; see the design notes).", file=sys.stderr)
+              "by rows, with no communication between GPUs on the hot path).", file=sys.stderr)
         return 2
 
     import torch

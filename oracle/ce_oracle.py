@@ -35,8 +35,7 @@ PR #9339.
   description (row count clamped so an all-ignored batch gives zero
   gradients): the mean loss stays NaN, the gradients are exactly zero.
 
-Readings where the pages are silent (each is a plain reading; the same list
-is kept with the design notes):
+Readings where the pages are silent (each is a plain reading):
 
 * Formula: the PyTorch cross-entropy convention, which the PR #9324 page
   uses as ground truth (tests "against CPU") and the Liger CE profile
