@@ -45,7 +45,10 @@
  *  - Arguments are validated on the host before anything is enqueued: on
  *    an error status nothing has been written.
  *  - Concurrent calls that share a workspace race; give each stream its
- *    own workspace.
+ *    own workspace. After its first zero fill a workspace needs no reset
+ *    between calls: rows split over several workgroups exchange words
+ *    stamped with a per-call number that repeats only after 2^30 - 1 calls
+ *    in the process.
  */
 #ifndef CE_MI355X_H
 #define CE_MI355X_H

@@ -187,11 +187,14 @@ inline void fill_options(cedev::Params& p, void* logits, int64_t rows, int64_t V
 }
 
 
-// Row pairs stamp their partials with a number unique to each launch, so no
-// reset is needed between calls that share the workspace. Stamps are taken
-// from [0xC0000001, 0xFFFFFFFF]: as fp32 bit patterns these are negative
-// numbers, which no per-row loss array holds, and no other workspace word
-// (counts, flags, split-V padding) takes such values either.
+// Split rows stamp their exchanged words with a number unique to each
+// launch, so no reset is needed between calls that share the workspace.
+// Stamps are taken from [0xC0000001, 0xFFFFFFFF]: as fp32 bit patterns these
+// are negative numbers, which no per-row loss array holds, and no other
+// workspace word (counts, flags, split-V padding) takes such values either.
+// They repeat after 2^30 - 1 calls: a slot could be misread only if it was
+// last written exactly that many calls earlier and no call since reached its
+// row.
 inline uint32_t next_epoch() {
   static std::atomic<uint32_t> calls{0};
   return 0xC0000000u | (calls.fetch_add(1, std::memory_order_relaxed) % 0x3FFFFFFFu + 1u);
