@@ -62,12 +62,12 @@ inline void split_plan(int64_t rows, int64_t nvec, bool forced, Plan* pl) {
 }
 
 // Fused shape for rows of nvec vectors: the smallest capacity that holds the
-// row. Rows of 4 K to 32 K vectors take the 1024-thread layouts (one
-// workgroup, or a row pair), measured faster on MI355X than 512-thread
-// workgroups holding the whole row; rows of up to 4 K vectors stay with
-// 256/512-thread workgroups (a 1024-thread workgroup per 64 KiB row was
-// slower). CE_F_SHAPE_ALT takes the other layout where a row size has two
-// (a test hook for comparing them). -1: no fused shape.
+// row. Rows of 4 K to 16 K vectors take a pair of 512-thread workgroups, rows
+// of 16 K to 32 K four of them (two workgroups per CU, so one streams while
+// the other waits for its group), measured faster on MI355X than one
+// workgroup per row or per CU; rows of up to 4 K vectors stay with the
+// 256/512-thread row kernel. CE_F_SHAPE_ALT takes the other layout where a
+// row size has two (a test hook for comparing them). -1: no fused shape.
 inline int fused_shape(int64_t nvec, uint32_t flags) {
   const bool alt = (flags & CE_F_SHAPE_ALT) != 0;
   for (int s = 0; s <= 1; ++s)

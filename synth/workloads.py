@@ -1,4 +1,4 @@
-"""The five synthetic workloads and their seeded generators.
+"""The synthetic workloads and their seeded generators.
 
 Shapes follow the pages' workloads: the Liger-Kernel cross-entropy profile's
 benchmark sweep (B=8, T=512 rows, bf16, V from 4096 to 131072) and the
@@ -80,6 +80,9 @@ WORKLOADS = {
     "ce_512x262144_bf16_allignored": Workload("ce_512x262144_bf16_allignored", 512, 262144,
                                               torch.bfloat16, 1.0, 1055, reductions=("mean",),
                                               all_ignored_nonfinite=True),
+    # one GPU's slice of the 1023 x 128256 batch split over 8 vocabulary shards
+    "ce_1023x16032_f32_shard": Workload("ce_1023x16032_f32_shard", 1023, 16032, torch.float32,
+                                        1.0, 107, ignore_frac=0.02, reductions=("sum",)),
 }
 
 
