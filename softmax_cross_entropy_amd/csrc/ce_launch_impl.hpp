@@ -31,8 +31,21 @@ hipError_t resident_blocks(K kernel, int block, int* cache, int* out) {
   return hipSuccess;
 }
 
-// Persistent row kernel: as many workgroups as fit on the device at once
-// (occupancy x compute units, cached per device), at most one per row.
+// Persistent grid for `units` rows (or row groups) of which at most
+// `resident` run at once: the fewest workers that need no more rounds than
+// `resident` would. Each worker then gets the same number of units, give or
+// take one, so the last round is not left to a small share of the device
+// (4096 rows on 1280 resident workgroups: 1024 workgroups of 4 rows, not
+// 256 of 4 and 1024 of 3).
+inline int64_t balanced_grid(int64_t units, int64_t resident) {
+  if (resident < 1) resident = 1;
+  if (units <= resident) return units;
+  const int64_t rounds = (units + resident - 1) / resident;
+  return (units + rounds - 1) / rounds;
+}
+
+// Persistent row kernel: at most as many workgroups as fit on the device at
+// once (occupancy x compute units, cached per device), balanced over rows.
 template <class E, int SC, int SM, int BLOCK, int NREG>
 hipError_t launch_rows(const Params& p, hipStream_t st) {
   static int cache[64] = {};
@@ -40,7 +53,7 @@ hipError_t launch_rows(const Params& p, hipStream_t st) {
   const hipError_t e =
       resident_blocks(cedev::rows_kernel<E, BLOCK, NREG, SC, SM>, BLOCK, cache, &r);
   if (e != hipSuccess) return e;
-  const int64_t grid = p.rows < r ? p.rows : r;
+  const int64_t grid = balanced_grid(p.rows, r);
   cedev::rows_kernel<E, BLOCK, NREG, SC, SM>
       <<<dim3(static_cast<unsigned>(grid)), BLOCK, 0, st>>>(p);
   return hipGetLastError();
@@ -67,7 +80,8 @@ hipError_t launch_fused(int shape, const Params& p, hipStream_t st) {
 
 // wide_kernel launch (instantiated in the ce_inst_*_wide units): persistent,
 // at most one workgroup per part; rows split over G parts take a multiple
-// of G workgroups (fixed groups G j ... G j + G - 1), at least one group.
+// of G workgroups (fixed groups G j ... G j + G - 1), at least one group,
+// balanced over rows like the row kernel.
 template <class E, int BLOCK, int NREG, int PARTS, int SC, int SM>
 hipError_t launch_wide_t(const Params& p, hipStream_t st) {
   static int cache[64] = {};
@@ -75,9 +89,8 @@ hipError_t launch_wide_t(const Params& p, hipStream_t st) {
   const hipError_t e =
       resident_blocks(cedev::wide_kernel<E, BLOCK, NREG, PARTS, SC, SM>, BLOCK, cache, &r);
   if (e != hipSuccess) return e;
-  const int64_t parts = p.rows * PARTS;
-  int64_t grid = parts < r ? parts : r;
-  if (PARTS > 1) grid = grid >= PARTS ? grid - grid % PARTS : PARTS;
+  const int64_t groups = balanced_grid(p.rows, r / PARTS);
+  const int64_t grid = (groups > 0 ? groups : 1) * PARTS;
   cedev::wide_kernel<E, BLOCK, NREG, PARTS, SC, SM>
       <<<dim3(static_cast<unsigned>(grid)), BLOCK, 0, st>>>(p);
   return hipGetLastError();
