@@ -196,7 +196,7 @@ ce_status ce_backward_recompute(const void* logits, int dtype, int64_t rows, int
 
 /* Bytes of device workspace ce_linear_forward needs (>= 256), or 0 for
  * invalid sizes. chunk_rows = 0 picks the default chunk (rows whose fp32
- * logits and bf16 gradient take at most 6 GiB). */
+ * logits, bf16 gradient and its transpose take at most 6 GiB). */
 size_t ce_linear_workspace_bytes(int64_t rows, int64_t H, int64_t V, int64_t chunk_rows,
                                  uint32_t flags);
 

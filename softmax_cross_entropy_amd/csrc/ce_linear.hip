@@ -53,6 +53,67 @@ __global__ __launch_bounds__(kNarrowBlock) void grad_narrow_kernel(
   }
 }
 
+// The same narrowing written transposed: G^T (V rows of ldt bf16) for the
+// weight gradient, whose product then reads both operands without a
+// transpose (NN; the NT form with G measured 4.16 against 3.49 ms at
+// 4096 x 4096 x 128256 on MI355X). If gout is not null the rows of G are
+// also written as grad_narrow_kernel does. A tile of 64 chunk rows x 128
+// vocabulary entries goes through LDS, so the fp32 reads are 512-byte row
+// runs and each G^T row segment is one 128-byte line. ldt is a multiple of
+// 64; entries of chunk rows past cr are written as zeros and never read.
+constexpr int kTileRows = 64;
+constexpr int kTileCols = 128;
+constexpr int kTBlock = 256;
+
+__global__ __launch_bounds__(kTBlock) void grad_narrow_t_kernel(
+    const float* __restrict__ g, int64_t ldl, int64_t cr, int64_t V,
+    uint32_t* __restrict__ gout, int64_t ldg, uint16_t* __restrict__ gt, int64_t ldt,
+    const float* go, int per_row) {
+  __shared__ __align__(16) uint16_t tile[kTileCols][kTileRows + 8];
+  const int t = threadIdx.x;
+  const int64_t i0 = static_cast<int64_t>(blockIdx.y) * kTileRows;
+  const int64_t v0 = static_cast<int64_t>(blockIdx.x) * kTileCols;
+  const int c4 = t % (kTileCols / 4);  // 16-byte column of the tile
+  const int rsub = t / (kTileCols / 4);
+  constexpr int kRowStep = kTBlock / (kTileCols / 4);
+  const int64_t v = v0 + 4 * c4;
+#pragma unroll
+  for (int u = 0; u < kTileRows / kRowStep; ++u) {
+    const int r = u * kRowStep + rsub;
+    const int64_t i = i0 + r;
+    const bool in = i < cr && v < ldl;
+    cedev::f4 x = {0.0f, 0.0f, 0.0f, 0.0f};
+    float s = 0.0f;
+    if (in) {
+      x = __builtin_nontemporal_load(reinterpret_cast<const cedev::f4*>(g + i * ldl + v));
+      s = go ? (per_row ? go[i] : go[0]) : 1.0f;
+    }
+    const uint32_t lo = cedev::pack_bf16x2(x[0] * s, x[1] * s);
+    const uint32_t hi = cedev::pack_bf16x2(x[2] * s, x[3] * s);
+    if (gout && in) {
+      uint32_t* dst = gout + i * (ldg / 2) + v / 2;
+      dst[0] = lo;
+      dst[1] = hi;
+    }
+    tile[4 * c4 + 0][r] = static_cast<uint16_t>(lo);
+    tile[4 * c4 + 1][r] = static_cast<uint16_t>(lo >> 16);
+    tile[4 * c4 + 2][r] = static_cast<uint16_t>(hi);
+    tile[4 * c4 + 3][r] = static_cast<uint16_t>(hi >> 16);
+  }
+  __syncthreads();
+  constexpr int kSegs = kTileRows / 8;  // 16-byte pieces of a G^T row segment
+#pragma unroll
+  for (int u = 0; u < kTileCols / (kTBlock / kSegs); ++u) {
+    const int vr = u * (kTBlock / kSegs) + t / kSegs;
+    const int seg = t % kSegs;
+    const int64_t vv = v0 + vr;
+    if (vv < V) {
+      const uint4 w = *reinterpret_cast<const uint4*>(&tile[vr][seg * 8]);
+      *reinterpret_cast<uint4*>(gt + vv * ldt + i0 + seg * 8) = w;
+    }
+  }
+}
+
 // grad_weight = 0 for an empty batch (no chunk runs the weight product).
 __global__ __launch_bounds__(256) void zero_rows_kernel(float* a, int64_t rows, int64_t cols,
                                                         int64_t ld) {
@@ -72,22 +133,24 @@ struct LinLayout {
   int64_t C;        // rows per chunk
   int64_t ldl;      // fp32 logits row stride (16-byte rows)
   int64_t ldg;      // bf16 gradient row stride (16-byte rows)
-  size_t row_ce, row_z, row_ok, part, logits, gbuf, total;
+  int64_t ldt;      // bf16 transposed gradient row stride (chunk rows, 128-byte rows)
+  size_t row_ce, row_z, row_ok, part, logits, gbuf, gtbuf, total;
 };
 
 // Workspace: the cross-entropy header and per-row arrays for every row,
 // partials for one chunk (the larger of a full and the last chunk's plan),
-// then one chunk of fp32 logits and one of bf16 gradient.
+// then one chunk of fp32 logits, one of bf16 gradient and its transpose.
 LinLayout lin_layout(int64_t rows, int64_t V, int64_t chunk_rows, uint32_t flags) {
   LinLayout L;
   L.ldl = round_up(V, 4);
   L.ldg = round_up(V, 8);
-  const int64_t per_row = L.ldl * 4 + L.ldg * 2;
+  const int64_t per_row = L.ldl * 4 + L.ldg * 2 + V * 2;
   int64_t C = chunk_rows > 0 ? chunk_rows
                              : static_cast<int64_t>(kDefaultChunkBytes / static_cast<size_t>(per_row));
   if (C < 1) C = 1;
   if (C > rows) C = rows;
   L.C = C;
+  L.ldt = round_up(C > 0 ? C : 1, kTileRows);
   int64_t parts = 0;
   if (rows > 0) {
     const int64_t sizes[2] = {C, rows % C};
@@ -112,6 +175,8 @@ LinLayout lin_layout(int64_t rows, int64_t V, int64_t chunk_rows, uint32_t flags
   off += align_up(static_cast<size_t>(C) * static_cast<size_t>(L.ldl) * 4);
   L.gbuf = off;
   off += align_up(static_cast<size_t>(C) * static_cast<size_t>(L.ldg) * 2);
+  L.gtbuf = off;
+  off += align_up(static_cast<size_t>(rows > 0 ? V : 0) * static_cast<size_t>(L.ldt) * 2);
   L.total = off;
   return L;
 }
@@ -196,6 +261,7 @@ CE_API ce_status ce_linear_forward(const void* hidden, int64_t ld_hidden, const 
   char* ws = static_cast<char*>(workspace);
   float* logits = reinterpret_cast<float*>(ws + L.logits);
   uint32_t* gbuf = reinterpret_cast<uint32_t*>(ws + L.gbuf);
+  uint16_t* gtbuf = reinterpret_cast<uint16_t*>(ws + L.gtbuf);
   cedev::Params base;
   fill_options(base, logits, rows, V, L.ldl, target, class_weight, ignore_index,
                label_smoothing, lse_square_scale, softcap, reduction);
@@ -250,13 +316,21 @@ CE_API ce_status ce_linear_forward(const void* hidden, int64_t ld_hidden, const 
     pc.epoch = next_epoch();
     if (cehost::launch_forward_f32(pl, pc, st) != hipSuccess) return CE_E_HIP;
     if (!want_grad) continue;
-    const int64_t nv4 = L.ldl / 4;
-    const dim3 ngrid(static_cast<unsigned>((nv4 + kNarrowBlock * kNarrowUnroll - 1) /
-                                           (kNarrowBlock * kNarrowUnroll)),
-                     static_cast<unsigned>(cr));
-    grad_narrow_kernel<<<ngrid, kNarrowBlock, 0, st>>>(
-        logits, L.ldl, gbuf, L.ldg, nv4, grad_output ? grad_output + (per_row ? c0 : 0) : nullptr,
-        per_row);
+    const float* go = grad_output ? grad_output + (per_row ? c0 : 0) : nullptr;
+    if (grad_weight) {
+      const dim3 tgrid(static_cast<unsigned>((L.ldl + kTileCols - 1) / kTileCols),
+                       static_cast<unsigned>((cr + kTileRows - 1) / kTileRows));
+      grad_narrow_t_kernel<<<tgrid, kTBlock, 0, st>>>(logits, L.ldl, cr, V,
+                                                     grad_hidden ? gbuf : nullptr, L.ldg, gtbuf,
+                                                     L.ldt, go, per_row);
+    } else {
+      const int64_t nv4 = L.ldl / 4;
+      const dim3 ngrid(static_cast<unsigned>((nv4 + kNarrowBlock * kNarrowUnroll - 1) /
+                                             (kNarrowBlock * kNarrowUnroll)),
+                       static_cast<unsigned>(cr));
+      grad_narrow_kernel<<<ngrid, kNarrowBlock, 0, st>>>(logits, L.ldl, gbuf, L.ldg, nv4, go,
+                                                         per_row);
+    }
     if (hipGetLastError() != hipSuccess) return CE_E_HIP;
     // d hidden_chunk (cr x H) = G_chunk @ weight
     if (grad_hidden &&
@@ -264,10 +338,10 @@ CE_API ce_status ce_linear_forward(const void* hidden, int64_t ld_hidden, const 
                        ld_weight, gbuf, L.ldg, 0.0f, grad_hidden + c0 * ld_grad_hidden,
                        ld_grad_hidden))
       return CE_E_HIP;
-    // d weight (V x H) (+)= G_chunk^T @ hidden_chunk
+    // d weight (V x H) (+)= G_chunk^T @ hidden_chunk, from the stored G^T
     if (grad_weight &&
-        !gemm_bf16_f32(blas, rocblas_operation_none, rocblas_operation_transpose, H, V, cr, xc,
-                       ld_hidden, gbuf, L.ldg, c0 == 0 ? 0.0f : 1.0f, grad_weight, ld_grad_weight))
+        !gemm_bf16_f32(blas, rocblas_operation_none, rocblas_operation_none, H, V, cr, xc,
+                       ld_hidden, gtbuf, L.ldt, c0 == 0 ? 0.0f : 1.0f, grad_weight, ld_grad_weight))
       return CE_E_HIP;
   }
   if (rows == 0 && grad_weight) {
