@@ -18,6 +18,7 @@ typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef float f2 __attribute__((ext_vector_type(2)));
 typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.69314718055994530942f;
@@ -135,6 +136,11 @@ struct F32 {
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const b2 r = __builtin_convertvector((f2{lo, hi}), b2);
   return __builtin_bit_cast(uint32_t, r);
+}
+
+// One fp32 value rounded to bf16 (nearest even), as pack_bf16x2 rounds it.
+__device__ __forceinline__ uint16_t to_bf16(float v) {
+  return static_cast<uint16_t>(pack_bf16x2(v, 0.0f));
 }
 
 struct BF16 {

@@ -50,6 +50,12 @@ hipError_t launch_prologue(const cedev::Params& p, hipStream_t st);
 // (1, 2 or 4) workgroups per row: one of the wide shapes of kShapes.
 hipError_t launch_wide_f32(const Shape& s, const cedev::Params& p, hipStream_t st);
 hipError_t launch_wide_bf16(const Shape& s, const cedev::Params& p, hipStream_t st);
+// wide_kernel_gbf16 (fp32 logits, gradient times gscale written as bf16 rows
+// compacted in place) for the split-row shapes (parts 2 or 4):
+// hipErrorInvalidValue for any other shape.
+bool gbf16_shape(int shape);
+hipError_t launch_wide_gbf16(int shape, const cedev::Params& p, const float* gscale,
+                             int per_row, hipStream_t st);
 hipError_t launch_forward_f32(const Plan& plan, const cedev::Params& p, hipStream_t st);
 hipError_t launch_forward_bf16(const Plan& plan, const cedev::Params& p, hipStream_t st);
 hipError_t launch_recompute_f32(const cedev::Params& p, void* grad, int64_t grad_stride,

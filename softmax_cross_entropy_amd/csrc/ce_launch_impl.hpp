@@ -108,6 +108,35 @@ hipError_t launch_wide_h(const Params& p, hipStream_t st) {
             : launch_wide_t<E, BLOCK, NREG, PARTS, 0, 0>(p, st);
 }
 
+// wide_kernel_gbf16: the same grid as wide_kernel.
+template <class E, int BLOCK, int NREG, int PARTS, int SC, int SM>
+hipError_t launch_wide_gbf16_t(const Params& p, const float* gscale, int per_row,
+                               hipStream_t st) {
+  static int cache[64] = {};
+  int r = 0;
+  const hipError_t e = resident_blocks(cedev::wide_kernel_gbf16<E, BLOCK, NREG, PARTS, SC, SM>,
+                                       BLOCK, cache, &r);
+  if (e != hipSuccess) return e;
+  const int64_t groups = balanced_grid(p.rows, r / PARTS);
+  const int64_t grid = (groups > 0 ? groups : 1) * PARTS;
+  cedev::wide_kernel_gbf16<E, BLOCK, NREG, PARTS, SC, SM>
+      <<<dim3(static_cast<unsigned>(grid)), BLOCK, 0, st>>>(p, gscale, per_row);
+  return hipGetLastError();
+}
+
+template <class E, int BLOCK, int NREG, int PARTS>
+hipError_t launch_wide_gbf16_h(const Params& p, const float* gscale, int per_row,
+                               hipStream_t st) {
+  const bool sc = p.softcap > 0.0f;
+  const bool sm = p.eps > 0.0f;
+  if (sc) {
+    return sm ? launch_wide_gbf16_t<E, BLOCK, NREG, PARTS, 1, 1>(p, gscale, per_row, st)
+              : launch_wide_gbf16_t<E, BLOCK, NREG, PARTS, 1, 0>(p, gscale, per_row, st);
+  }
+  return sm ? launch_wide_gbf16_t<E, BLOCK, NREG, PARTS, 0, 1>(p, gscale, per_row, st)
+            : launch_wide_gbf16_t<E, BLOCK, NREG, PARTS, 0, 0>(p, gscale, per_row, st);
+}
+
 template <class E, int SC, int SM>
 hipError_t launch_splitv(int shape, const Params& p, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>(p.rows * p.S));

@@ -58,15 +58,18 @@ __global__ __launch_bounds__(kNarrowBlock) void grad_narrow_kernel(
 // transpose (NN; the NT form with G measured 4.16 against 3.49 ms at
 // 4096 x 4096 x 128256 on MI355X). If gout is not null the rows of G are
 // also written as grad_narrow_kernel does. A tile of 64 chunk rows x 128
-// vocabulary entries goes through LDS, so the fp32 reads are 512-byte row
-// runs and each G^T row segment is one 128-byte line. ldt is a multiple of
-// 64; entries of chunk rows past cr are written as zeros and never read.
+// vocabulary entries goes through LDS, so the reads are row runs of 512
+// (fp32) or 256 (bf16) bytes and each G^T row segment is one 128-byte line.
+// ldt is a multiple of 64; entries of chunk rows past cr are written as
+// zeros and never read. BF16IN: g holds G already in bf16 (rows of ldin
+// elements, no scale, no gout); else fp32 rows of ldin elements.
 constexpr int kTileRows = 64;
 constexpr int kTileCols = 128;
 constexpr int kTBlock = 256;
 
+template <bool BF16IN>
 __global__ __launch_bounds__(kTBlock) void grad_narrow_t_kernel(
-    const float* __restrict__ g, int64_t ldl, int64_t cr, int64_t V,
+    const void* __restrict__ g, int64_t ldin, int64_t ncols, int64_t cr, int64_t V,
     uint32_t* __restrict__ gout, int64_t ldg, uint16_t* __restrict__ gt, int64_t ldt,
     const float* go, int per_row) {
   __shared__ __align__(16) uint16_t tile[kTileCols][kTileRows + 8];
@@ -81,16 +84,27 @@ __global__ __launch_bounds__(kTBlock) void grad_narrow_t_kernel(
   for (int u = 0; u < kTileRows / kRowStep; ++u) {
     const int r = u * kRowStep + rsub;
     const int64_t i = i0 + r;
-    const bool in = i < cr && v < ldl;
-    cedev::f4 x = {0.0f, 0.0f, 0.0f, 0.0f};
-    float s = 0.0f;
-    if (in) {
-      x = __builtin_nontemporal_load(reinterpret_cast<const cedev::f4*>(g + i * ldl + v));
-      s = go ? (per_row ? go[i] : go[0]) : 1.0f;
+    const bool in = i < cr && v < ncols;
+    uint32_t lo = 0u, hi = 0u;
+    if constexpr (BF16IN) {
+      if (in) {
+        const cedev::u2 w = __builtin_nontemporal_load(
+            reinterpret_cast<const cedev::u2*>(static_cast<const uint16_t*>(g) + i * ldin + v));
+        lo = w[0];
+        hi = w[1];
+      }
+    } else {
+      cedev::f4 x = {0.0f, 0.0f, 0.0f, 0.0f};
+      float s = 0.0f;
+      if (in) {
+        x = __builtin_nontemporal_load(
+            reinterpret_cast<const cedev::f4*>(static_cast<const float*>(g) + i * ldin + v));
+        s = go ? (per_row ? go[i] : go[0]) : 1.0f;
+      }
+      lo = cedev::pack_bf16x2(x[0] * s, x[1] * s);
+      hi = cedev::pack_bf16x2(x[2] * s, x[3] * s);
     }
-    const uint32_t lo = cedev::pack_bf16x2(x[0] * s, x[1] * s);
-    const uint32_t hi = cedev::pack_bf16x2(x[2] * s, x[3] * s);
-    if (gout && in) {
+    if (!BF16IN && gout && in) {
       uint32_t* dst = gout + i * (ldg / 2) + v / 2;
       dst[0] = lo;
       dst[1] = hi;
@@ -314,15 +328,31 @@ CE_API ce_status ce_linear_forward(const void* hidden, int64_t ld_hidden, const 
     pc.S = pl.S;
     pc.chunk_vec = pl.chunk_vec;
     pc.epoch = next_epoch();
-    if (cehost::launch_forward_f32(pl, pc, st) != hipSuccess) return CE_E_HIP;
-    if (!want_grad) continue;
     const float* go = grad_output ? grad_output + (per_row ? c0 : 0) : nullptr;
-    if (grad_weight) {
-      const dim3 tgrid(static_cast<unsigned>((L.ldl + kTileCols - 1) / kTileCols),
-                       static_cast<unsigned>((cr + kTileRows - 1) / kTileRows));
-      grad_narrow_t_kernel<<<tgrid, kTBlock, 0, st>>>(logits, L.ldl, cr, V,
-                                                     grad_hidden ? gbuf : nullptr, L.ldg, gtbuf,
-                                                     L.ldt, go, per_row);
+    // Split-row plans write G x grad_output as bf16 straight from the
+    // cross-entropy kernel, compacted into the first half of each logits row
+    // (rows of 2 ldl bf16); other plans write fp32 G, narrowed below.
+    const bool gb = want_grad && pl.path == CE_PATH_FUSED && cehost::gbf16_shape(pl.shape);
+    if (gb) {
+      if (cehost::launch_wide_gbf16(pl.shape, pc, go, per_row, st) != hipSuccess) return CE_E_HIP;
+    } else if (cehost::launch_forward_f32(pl, pc, st) != hipSuccess) {
+      return CE_E_HIP;
+    }
+    if (!want_grad) continue;
+    const dim3 tgrid(static_cast<unsigned>((L.ldl + kTileCols - 1) / kTileCols),
+                     static_cast<unsigned>((cr + kTileRows - 1) / kTileRows));
+    const void* gsrc = gbuf;  // G (bf16) for the d hidden product
+    int64_t ldgs = L.ldg;
+    if (gb) {
+      gsrc = logits;
+      ldgs = 2 * L.ldl;
+      if (grad_weight)
+        grad_narrow_t_kernel<true><<<tgrid, kTBlock, 0, st>>>(logits, ldgs, L.ldl, cr, V, nullptr,
+                                                              0, gtbuf, L.ldt, nullptr, 0);
+    } else if (grad_weight) {
+      grad_narrow_t_kernel<false><<<tgrid, kTBlock, 0, st>>>(logits, L.ldl, L.ldl, cr, V,
+                                                             grad_hidden ? gbuf : nullptr, L.ldg,
+                                                             gtbuf, L.ldt, go, per_row);
     } else {
       const int64_t nv4 = L.ldl / 4;
       const dim3 ngrid(static_cast<unsigned>((nv4 + kNarrowBlock * kNarrowUnroll - 1) /
@@ -335,7 +365,7 @@ CE_API ce_status ce_linear_forward(const void* hidden, int64_t ld_hidden, const 
     // d hidden_chunk (cr x H) = G_chunk @ weight
     if (grad_hidden &&
         !gemm_bf16_f32(blas, rocblas_operation_none, rocblas_operation_none, H, cr, V, weight,
-                       ld_weight, gbuf, L.ldg, 0.0f, grad_hidden + c0 * ld_grad_hidden,
+                       ld_weight, gsrc, ldgs, 0.0f, grad_hidden + c0 * ld_grad_hidden,
                        ld_grad_hidden))
       return CE_E_HIP;
     // d weight (V x H) (+)= G_chunk^T @ hidden_chunk, from the stored G^T

@@ -179,10 +179,17 @@ __device__ __forceinline__ void next_words(const Params& p, uint32_t c, int64_t 
 
 // One part (a whole row, or a half or quarter of one) of the persistent
 // wide kernel.
-template <class E, int BLOCK, int NREG, int PARTS, int SC, int SM>
+// GB = 1 (fp32 logits only): the gradient is written as bf16 (nearest even),
+// times gscale (one value, or one per row with gscale_per_row; null = 1),
+// compacted in place at the start of the row's bytes (element e at byte
+// 2 e), not as fp32 over the logits. A part writes only after every
+// part of its row has published its partial, i.e. after every logit of the
+// row has been consumed, so the compacted writes never meet a pending read.
+template <class E, int BLOCK, int NREG, int PARTS, int SC, int SM, int GB = 0>
 __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
                                           WideShared<BLOCK>& sh, int64_t& next_t,
-                                          int64_t& next_y) {
+                                          int64_t& next_y, const float* gscale = nullptr,
+                                          int gscale_per_row = 0) {
   constexpr int NW = BLOCK / 64;
   constexpr int EPV = E::EPV;
   constexpr int GS = (EPV == 4) ? 4 : 2;  // slots per pass-1 group
@@ -227,9 +234,16 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
       if (tid == 0 && h == 0) claim = claim_issue(p);
     }
     if (p.grad) {
-      u4* vp = reinterpret_cast<u4*>(hp);
-      for (int j = tid; j < nv; j += BLOCK) __builtin_nontemporal_store(u4{0u, 0u, 0u, 0u}, vp + j);
-      if (tid < tail) E::st(rp, tail0 + tid, 0.0f);
+      if constexpr (GB) {
+        u2* vp = reinterpret_cast<u2*>(rp + e0 * 2);
+        for (int j = tid; j < nv; j += BLOCK) __builtin_nontemporal_store(u2{0u, 0u}, vp + j);
+        if (tid < tail) reinterpret_cast<uint16_t*>(rp)[tail0 + tid] = 0;
+      } else {
+        u4* vp = reinterpret_cast<u4*>(hp);
+        for (int j = tid; j < nv; j += BLOCK)
+          __builtin_nontemporal_store(u4{0u, 0u, 0u, 0u}, vp + j);
+        if (tid < tail) E::st(rp, tail0 + tid, 0.0f);
+      }
     }
     if constexpr (PARTS > 1) {
       // no partials to combine: part 0 only hands over the group's next row
@@ -590,6 +604,13 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
     // ---- pass 2: the gradient from on-chip data, written over the logits ----
     if (p.grad) {
       const RowScalars rs = sh.rs;
+      // GB: this part's bf16 gradient bytes and the scale applied before rounding
+      __amdgpu_buffer_rsrc_t rsrc_g = rsrc;
+      float gsc = 1.0f;
+      if constexpr (GB) {
+        rsrc_g = make_rsrc_bytes(rp + e0 * 2, nv * 8);
+        if (gscale) gsc = gscale[gscale_per_row ? row : 0];
+      }
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
         if (g * GS * BLOCK < nv) {
@@ -606,7 +627,14 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
                 gv = grad_vec<E, SC, SM>(p, rs, r[k], v0 + k * BLOCK + tid, -1);
               }
               // lanes past the part are outside the descriptor: the store is dropped
-              __builtin_amdgcn_raw_buffer_store_b128(gv, rsrc, voff, k * BLOCK * 16, kStoreNT);
+              if constexpr (GB) {
+                const f4 gf = __builtin_bit_cast(f4, gv);
+                const u2 gb = {pack_bf16x2(gf[0] * gsc, gf[1] * gsc),
+                               pack_bf16x2(gf[2] * gsc, gf[3] * gsc)};
+                __builtin_amdgcn_raw_buffer_store_b64(gb, rsrc_g, tid * 8, k * BLOCK * 8, kStoreNT);
+              } else {
+                __builtin_amdgcn_raw_buffer_store_b128(gv, rsrc, voff, k * BLOCK * 16, kStoreNT);
+              }
             }
           }
         }
@@ -614,7 +642,11 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
       if (tid < tail) {
         const int64_t k = tail0 + tid;
         const float wk = (SM && p.weight) ? p.weight[k] : 1.0f;
-        E::st(rp, k, grad_one<SC, SM>(p, rs, xt, wk, k == y));
+        if constexpr (GB) {
+          reinterpret_cast<uint16_t*>(rp)[k] = to_bf16(grad_one<SC, SM>(p, rs, xt, wk, k == y) * gsc);
+        } else {
+          E::st(rp, k, grad_one<SC, SM>(p, rs, xt, wk, k == y));
+        }
       }
       // The one-hot term: the vectors above were written without it; the
       // thread that wrote the target's vector rewrites that one element (its
@@ -623,8 +655,14 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
       if (yl >= 0 && yl < static_cast<int64_t>(nv) * EPV &&
           tid == static_cast<int>((yl / EPV) % BLOCK)) {
         const float wy = (SM && p.weight) ? p.weight[y] : 1.0f;
-        E::template st_buf<kStoreNT>(rsrc, static_cast<int>(yl),
-                                     grad_one<SC, SM>(p, rs, sh.xy, wy, true));
+        if constexpr (GB) {
+          __builtin_amdgcn_raw_buffer_store_b16(
+              to_bf16(grad_one<SC, SM>(p, rs, sh.xy, wy, true) * gsc), rsrc_g,
+              static_cast<int>(yl) * 2, 0, kStoreNT);
+        } else {
+          E::template st_buf<kStoreNT>(rsrc, static_cast<int>(yl),
+                                       grad_one<SC, SM>(p, rs, sh.xy, wy, true));
+        }
       }
     }
   }
@@ -669,6 +707,38 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
       t = nt;
       y = ny;
     }
+  }
+  if (p.epilogue) {
+    if (threadIdx.x == 0) s_last = arrive(p, gridDim.x);
+    __syncthreads();
+    if (s_last) epilogue_finish<BLOCK>(p);
+  }
+}
+
+// The same on fp32 logits, with the gradient times gscale (one value, or one
+// per row with gscale_per_row; null = 1) written as bf16 rows compacted in
+// place (the linear layer's gradient products read it directly). The scale
+// is an argument of its own, so wide_kernel's argument layout is left as it
+// is; the part loop is written out again rather than shared through an
+// inlined function, which changed wide_kernel's instruction schedule.
+template <class E, int BLOCK, int NREG, int PARTS, int SC, int SM>
+__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void wide_kernel_gbf16(
+    Params p, const float* gscale, int gscale_per_row) {
+  static_assert(PARTS == 2 || PARTS == 4, "bf16 gradients: split rows");
+  static_assert(E::EPV == 4, "bf16 gradients: fp32 logits");
+  __shared__ WideShared<BLOCK> sh;
+  __shared__ int s_last;
+  if (p.self_scales) compute_self_scales<BLOCK>(p);
+  if (threadIdx.x == 0) sh.limit = kGroupSpinLimit;
+  const int h = static_cast<int>(blockIdx.x % PARTS);
+  int64_t row = blockIdx.x / PARTS;
+  int64_t y = p.target[row];
+  while (row < p.rows) {
+    int64_t nr, ny;
+    wide_part<E, BLOCK, NREG, PARTS, SC, SM, 1>(p, PARTS * row + h, y, sh, nr, ny, gscale,
+                                                gscale_per_row);
+    row = nr;
+    y = ny;
   }
   if (p.epilogue) {
     if (threadIdx.x == 0) s_last = arrive(p, gridDim.x);

@@ -23,6 +23,7 @@ import torch
 import synth
 from oracle import grad_magnitudes, linear_forward
 from softmax_cross_entropy_amd import linear_cross_entropy, linear_forward_raw
+from softmax_cross_entropy_amd._lib import CE_F_FORCE_FUSED, CE_F_SHAPE_ALT
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -116,9 +117,19 @@ OPTS = {
 
 @pytest.mark.parametrize("opt", list(OPTS))
 @pytest.mark.parametrize("reduction", ["mean", "sum", "none"])
-@pytest.mark.parametrize("shape,chunk", [((37, 64, 3001), 0), ((300, 96, 4096), 64),
-                                         ((130, 128, 8000), 29)])
-def test_linear_parity(opt, reduction, shape, chunk):
+# The first three shapes take the row kernel on the chunk's fp32 logits (the
+# gradient narrowed to bf16 by its own kernel); the last three take split
+# rows, whose kernel writes the bf16 gradient itself: a row pair of 5000
+# vectors, a ragged row pair of 10000 vectors + 3 in three chunks (the last
+# partial), and quarter rows of 17500 vectors + 1. Chunks this small would
+# take split-V; CE_F_FORCE_FUSED keeps them on the split-row kernels, which
+# chunks of 256 rows and more take by themselves.
+@pytest.mark.parametrize("shape,chunk,flags", [((37, 64, 3001), 0, 0), ((300, 96, 4096), 64, 0),
+                                               ((130, 128, 8000), 29, 0),
+                                               ((40, 32, 20000), 0, CE_F_FORCE_FUSED),
+                                               ((33, 32, 40003), 16, CE_F_FORCE_FUSED),
+                                               ((24, 32, 70001), 0, CE_F_FORCE_FUSED)])
+def test_linear_parity(opt, reduction, shape, chunk, flags):
     rows, H, V = shape
     o = OPTS[opt]
     x, w, t = _make(rows, H, V, rows + V, rows // 6)
@@ -129,23 +140,26 @@ def test_linear_parity(opt, reduction, shape, chunk):
                              None if cw is None else cw.to(DEV), -100, o.get("eps", 0.0),
                              o.get("lam", 0.0), o.get("softcap"), reduction, grad=True,
                              z_loss=True, token_accuracy=True, argmax=True, counts=True,
-                             chunk_rows=chunk)
+                             chunk_rows=chunk, flags=flags)
     torch.cuda.synchronize()
     _check(x, w, t, res, cw=cw, eps=o.get("eps", 0.0), lam=o.get("lam", 0.0),
            softcap=o.get("softcap"), reduction=reduction, what=f"{opt}/{reduction}/{shape}")
 
 
+@pytest.mark.parametrize("rows,V,chunk", [(64, 5000, 24), (600, 20000, 300)])
 @pytest.mark.parametrize("reduction", ["mean", "none"])
-def test_linear_autograd_grad_output(reduction):
+def test_linear_autograd_grad_output(reduction, rows, V, chunk):
     """loss.backward(grad_output): mean scales the forward's gradients; none
-    recomputes them with the per-row grad_output."""
-    rows, H, V = 64, 64, 5000
+    recomputes them with the per-row grad_output (600 x 20000: two chunks of
+    300 rows on the split-row kernel, which applies each row's value before
+    it rounds the gradient to bf16)."""
+    H = 64
     x, w, t = _make(rows, H, V, 77, 8)
     _announce(name="linear-autograd", rows=rows, H=H, V=V, reduction=reduction)
     xd = x.to(DEV).requires_grad_(True)
     wd = w.to(DEV).requires_grad_(True)
     out = linear_cross_entropy(xd, wd, t.to(DEV), label_smoothing=0.1, reduction=reduction,
-                               chunk_rows=24)
+                               chunk_rows=chunk)
     if reduction == "none":
         go = torch.linspace(0.5, 2.0, rows)
         out.loss.backward(go.to(DEV))
@@ -185,6 +199,23 @@ def test_linear_all_ignored_and_empty():
     torch.cuda.synchronize()
     assert torch.isnan(loss).item() and int(cnt[0]) == 0
     assert gh.numel() == 0 and torch.count_nonzero(gw).item() == 0
+
+
+@pytest.mark.parametrize("reduction", ["mean", "none"])
+def test_linear_alt_layout(reduction):
+    """Quarter-row sizes on the alternative layout (a pair of 1024-thread
+    workgroups per row), every option on."""
+    rows, H, V = 20, 32, 70001
+    x, w, t = _make(rows, H, V, 71, 3)
+    cw = 0.5 + 1.5 * torch.rand(V, generator=torch.Generator().manual_seed(3))
+    _announce(name="linear-alt", rows=rows, H=H, V=V, reduction=reduction)
+    res = linear_forward_raw(x.to(DEV), w.to(DEV), t.to(DEV), cw.to(DEV), -100, 0.2, 1e-2, 3.0,
+                             reduction, grad=True, z_loss=True, token_accuracy=True,
+                             argmax=True, counts=True,
+                             flags=CE_F_FORCE_FUSED | CE_F_SHAPE_ALT)
+    torch.cuda.synchronize()
+    _check(x, w, t, res, cw=cw, eps=0.2, lam=1e-2, softcap=3.0, reduction=reduction,
+           what=f"alt/{reduction}")
 
 
 def test_linear_medium_default_chunk():
