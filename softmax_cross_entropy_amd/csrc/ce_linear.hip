@@ -65,6 +65,7 @@ __global__ __launch_bounds__(kNarrowBlock) void grad_narrow_kernel(
 // elements, no scale, no gout); else fp32 rows of ldin elements.
 constexpr int kTileRows = 64;
 constexpr int kTileCols = 128;
+constexpr int kTilePitch = kTileCols / 2 + 1;  // dwords per tile row
 constexpr int kTBlock = 256;
 
 template <bool BF16IN>
@@ -72,7 +73,11 @@ __global__ __launch_bounds__(kTBlock) void grad_narrow_t_kernel(
     const void* __restrict__ g, int64_t ldin, int64_t ncols, int64_t cr, int64_t V,
     uint32_t* __restrict__ gout, int64_t ldg, uint16_t* __restrict__ gt, int64_t ldt,
     const float* go, int per_row) {
-  __shared__ __align__(16) uint16_t tile[kTileCols][kTileRows + 8];
+  // The tile is kept as it was read (row r, entries 4 c4 ... 4 c4 + 3 in one
+  // 8-byte piece), rows kTilePitch dwords apart: an odd pitch puts the two
+  // dwords each lane stores, and the column entries each lane reads back, on
+  // distinct banks across a wave.
+  __shared__ uint32_t tile[kTileRows * kTilePitch];
   const int t = threadIdx.x;
   const int64_t i0 = static_cast<int64_t>(blockIdx.y) * kTileRows;
   const int64_t v0 = static_cast<int64_t>(blockIdx.x) * kTileCols;
@@ -109,10 +114,8 @@ __global__ __launch_bounds__(kTBlock) void grad_narrow_t_kernel(
       dst[0] = lo;
       dst[1] = hi;
     }
-    tile[4 * c4 + 0][r] = static_cast<uint16_t>(lo);
-    tile[4 * c4 + 1][r] = static_cast<uint16_t>(lo >> 16);
-    tile[4 * c4 + 2][r] = static_cast<uint16_t>(hi);
-    tile[4 * c4 + 3][r] = static_cast<uint16_t>(hi >> 16);
+    tile[r * kTilePitch + 2 * c4] = lo;
+    tile[r * kTilePitch + 2 * c4 + 1] = hi;
   }
   __syncthreads();
   constexpr int kSegs = kTileRows / 8;  // 16-byte pieces of a G^T row segment
@@ -122,8 +125,16 @@ __global__ __launch_bounds__(kTBlock) void grad_narrow_t_kernel(
     const int seg = t % kSegs;
     const int64_t vv = v0 + vr;
     if (vv < V) {
-      const uint4 w = *reinterpret_cast<const uint4*>(&tile[vr][seg * 8]);
-      *reinterpret_cast<uint4*>(gt + vv * ldt + i0 + seg * 8) = w;
+      // entries (seg * 8 + j, vr) of the tile: G^T row vr, chunk rows seg * 8 + j
+      const uint16_t* col = reinterpret_cast<const uint16_t*>(tile) + vr;
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r0 = seg * 8 + 2 * q;
+        w[q] = static_cast<uint32_t>(col[r0 * 2 * kTilePitch]) |
+               (static_cast<uint32_t>(col[(r0 + 1) * 2 * kTilePitch]) << 16);
+      }
+      *reinterpret_cast<uint4*>(gt + vv * ldt + i0 + seg * 8) = uint4{w[0], w[1], w[2], w[3]};
     }
   }
 }
