@@ -1,8 +1,8 @@
 """Float64 CPU oracle for fused softmax cross-entropy forward + gradient.
 
-TEST INFRASTRUCTURE. This module is the checker, not the product: only the
-test suite, the package entry's smoke check and the benchmark's CPU-baseline
-leg may import it. The product path (HIP kernels behind the C ABI) never
+TEST INFRASTRUCTURE. This module is the reference the kernels are tested
+against, not the product: only the test suite, the package entry's smoke
+check and the benchmark's CPU-baseline leg may import it. The product path (HIP kernels behind the C ABI) never
 calls it, and the two share no code, tables or helpers.
 
 What is computed, and where the pages define it

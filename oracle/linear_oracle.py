@@ -1,8 +1,9 @@
 """Float64 CPU oracle for the linear layer fused with the cross-entropy.
 
-TEST INFRASTRUCTURE. Like ce_oracle, this is the checker, not the product:
-only the test suite, the package entry's smoke check and the benchmark's
-CPU-baseline leg may import it, and it shares nothing with the HIP path.
+TEST INFRASTRUCTURE. Like ce_oracle, this is a test reference, not the
+product: only the test suite, the package entry's smoke check and the
+benchmark's CPU-baseline leg may import it, and it shares nothing with the
+HIP path.
 
 What is computed
 ----------------
