@@ -218,6 +218,35 @@ def test_linear_alt_layout(reduction):
            what=f"alt/{reduction}")
 
 
+@pytest.mark.parametrize("V", [3001, 20000])
+def test_linear_target_out_of_range(V):
+    """A target outside [0, V) that is not ignore_index: that row's loss is
+    NaN and its gradient zero (V = 20000: zeros written as bf16 by the
+    split-row kernel); every other value equals, bit for bit, the call with
+    that row ignored, which is checked against the oracle."""
+    rows, H = 40, 32
+    x, w, t = _make(rows, H, V, 211, 5)
+    bad = t.clone()
+    bad[7] = V + 5
+    ign = t.clone()
+    ign[7] = -100
+    _announce(name="linear-target-range", rows=rows, H=H, V=V)
+    kw = dict(reduction="none", grad=True, z_loss=True, token_accuracy=True, argmax=True,
+              counts=True, chunk_rows=16, flags=CE_F_FORCE_FUSED)
+    rb = linear_forward_raw(x.to(DEV), w.to(DEV), bad.to(DEV), **kw)
+    ri = linear_forward_raw(x.to(DEV), w.to(DEV), ign.to(DEV), **kw)
+    torch.cuda.synchronize()
+    lb, li = rb[0].cpu(), ri[0].cpu()
+    assert torch.isnan(lb[7]).item() and li[7].item() == 0.0
+    keep = torch.arange(rows) != 7
+    assert torch.equal(lb[keep], li[keep])
+    assert torch.equal(rb[3].cpu(), ri[3].cpu())  # argmax (-1 on both rows)
+    assert torch.equal(rb[5], ri[5]) and torch.equal(rb[6], ri[6])  # both gradients
+    assert torch.count_nonzero(rb[5][7]).item() == 0
+    assert torch.equal(rb[4].cpu(), ri[4].cpu())  # counts: neither row is counted
+    _check(x, w, ign, ri, reduction="none", what=f"target-range/{V}")
+
+
 def test_linear_medium_default_chunk():
     """512 x 1024 hidden, V = 32000 (one default chunk), mean, every output."""
     rows, H, V = 512, 1024, 32000
