@@ -50,7 +50,13 @@ Readings where the pages are silent (each is a plain reading):
 * Softcap: z = c * tanh(x / c) for c > 0, applied first; the gradient
   chains through it with the factor 1 - tanh(x / c)**2.
 * argmax: over the raw stored logits, lowest index on ties; -1 on rows that
-  are not counted.
+  are not counted. A NaN ranks above every number (the ordering of
+  numpy.argmax and torch.argmax), so a counted row holding a NaN has the
+  index of its first NaN as argmax; its loss and gradient are NaN (every
+  exponential of the row is).
+* Non-finite logits in counted rows are taken as IEEE arithmetic gives
+  them: a +inf logit makes the max shift inf and the row's loss and
+  gradient NaN, a -inf logit has probability 0.
 * token_accuracy: n_correct / n for "mean" and "sum" (NaN when n = 0); the
   per-row 0/1 value for "none".
 * Rows whose target equals ignore_index are never read (they may hold

@@ -71,6 +71,13 @@ _SIGNATURES = {
                                          ctypes.c_int, _I64, _P, _P, _P, _P, _P, _P, _I64, _P,
                                          _I64, _P, ctypes.c_size_t, _P]),
     "ce_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    # include/ce_stream.h: the measurement stream kernels
+    "ce_stream_num_configs": (ctypes.c_int, []),
+    "ce_stream_config": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_int),
+                                        ctypes.POINTER(ctypes.c_int)]),
+    "ce_stream_resident": (_I64, [ctypes.c_int, ctypes.c_int]),
+    "ce_stream_run": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _P, _P, ctypes.c_size_t, _I64,
+                                     _P, _P]),
 }
 SYMBOLS = tuple(_SIGNATURES)
 
@@ -171,6 +178,34 @@ def ce_linear_forward(hidden: int, ld_hidden: int, weight: int, ld_weight: int, 
                                        per_row, chunk_rows, loss, z_loss, token_accuracy, argmax,
                                        counts, grad_hidden, ld_grad_hidden, grad_weight,
                                        ld_grad_weight, workspace, workspace_bytes, stream))
+
+
+CE_STREAM_READ = 0
+CE_STREAM_WRITE = 1
+CE_STREAM_INPLACE = 2
+CE_STREAM_COPY = 3
+CE_STREAM_FLUSH = 4
+
+
+def ce_stream_num_configs() -> int:
+    return int(lib().ce_stream_num_configs())
+
+
+def ce_stream_config(config: int):
+    """(block, nreg) of a stream-kernel chunk shape."""
+    b, n = ctypes.c_int(0), ctypes.c_int(0)
+    check(lib().ce_stream_config(config, ctypes.byref(b), ctypes.byref(n)), "ce_stream_config")
+    return b.value, n.value
+
+
+def ce_stream_resident(kind: int, config: int) -> int:
+    return int(lib().ce_stream_resident(kind, config))
+
+
+def ce_stream_run(kind: int, config: int, dst: int, src: int, nbytes: int, grid: int,
+                  sink: int, stream: int) -> int:
+    """Raw call; returns the status (0 = CE_OK)."""
+    return int(lib().ce_stream_run(kind, config, dst, src, nbytes, grid, sink, stream))
 
 
 def check(status: int, where: str) -> None:

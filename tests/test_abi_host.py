@@ -13,13 +13,17 @@ import pytest
 from softmax_cross_entropy_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "ce.h")
+INCLUDE = os.path.join(ROOT, "include")
 
 
 def _declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(ce_[a-z_]+)\s*\(", src)))
+    names = set()
+    for h in sorted(os.listdir(INCLUDE)):
+        if h.endswith(".h"):
+            src = open(os.path.join(INCLUDE, h)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names.update(re.findall(r"\b(ce_[a-z_]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol():

@@ -114,3 +114,23 @@ def test_linear_bf16_inputs_widen_exactly():
     r64 = linear_forward(xb.double().numpy(), wb.double().numpy(), t)
     assert r.ce.loss == r64.ce.loss
     np.testing.assert_array_equal(r.grad_hidden, r64.grad_hidden)
+
+
+def test_tolerance_helpers_golden():
+    """logits_abs = |hidden| @ |weight|^T and grad_magnitudes = (|G| @ |weight|,
+    |G|^T @ |hidden|), which size every bar of the linear-path parity tests,
+    against hand-computed values (tests/golden/tolerance_helpers.json): a
+    transposed operand or a dropped absolute value fails here."""
+    import json
+    import os
+    from oracle import grad_magnitudes, linear_forward
+    path = os.path.join(os.path.dirname(__file__), "golden", "tolerance_helpers.json")
+    c = json.load(open(path))["linear_case"]
+    h = np.array(c["hidden"])
+    w = np.array(c["weight"])
+    G = np.array(c["G"])
+    r = linear_forward(h, w, np.array([0, 2]), want_grad=False)
+    np.testing.assert_array_equal(r.logits_abs, np.array(c["logits_abs"]))
+    gh, gw = grad_magnitudes(h, w, G)
+    np.testing.assert_array_equal(gh, np.array(c["grad_hidden_mag"]))
+    np.testing.assert_array_equal(gw, np.array(c["grad_weight_mag"]))

@@ -413,3 +413,80 @@ def test_argmax_uses_raw_logits_under_saturating_softcap():
     r = ce_forward(x, np.array([0]), softcap=1.0, reduction="none")
     assert np.tanh(100.0) == np.tanh(101.0)
     assert r.argmax[0] == 2
+
+
+# ---------------------------------------------------------------------------
+# The tolerance helper: the per-element magnitude M of the gradient's terms
+# (it sizes every bf16 gradient bar), pinned to hand-derived values.
+# ---------------------------------------------------------------------------
+
+HELPERS = os.path.join(os.path.dirname(__file__), "golden", "tolerance_helpers.json")
+
+
+def _helper_cases():
+    with open(HELPERS) as f:
+        return json.load(f)
+
+
+@pytest.mark.parametrize("case", _helper_cases()["mag_cases"], ids=lambda c: c["name"])
+def test_gradient_magnitude_helper_golden(case):
+    x = np.array([[_eval(e) for e in case["x_expr"]]])
+    t = np.array([case["target"]])
+    w = np.array(case["weight"]) if "weight" in case else None
+    summ = summarize_targets(t, x.shape[1], -100, w, case["reduction"])
+    r = rows_forward(x, t, V=x.shape[1], alpha=summ.alpha, beta=summ.beta, weight=w,
+                     label_smoothing=case.get("label_smoothing", 0.0),
+                     lse_square_scale=case.get("lse_square_scale", 0.0),
+                     softcap=case.get("softcap"), want_grad=True, want_mag=True)
+    want = np.array([_eval(e) for e in case["mag"]])
+    np.testing.assert_allclose(r.mag[0], want, rtol=1e-12, atol=0)
+    # M bounds the gradient it describes (triangle inequality), elementwise
+    assert np.all(np.abs(r.grad[0]) <= r.mag[0] * (1 + 1e-12))
+
+
+def test_gradient_magnitude_helper_rows_not_counted():
+    """Ignored and out-of-range rows have no gradient terms: M is 0 there."""
+    x = np.array([[0.0, 1.0, 2.0]] * 3)
+    t = np.array([-100, 7, 1])
+    summ = summarize_targets(t, 3, -100, None, "mean")
+    r = rows_forward(x, t, V=3, alpha=summ.alpha, beta=summ.beta, want_grad=True,
+                     want_mag=True)
+    assert np.all(r.mag[:2] == 0.0)
+    assert np.all(r.mag[2] > 0.0)
+
+
+def _argmax_nan_first(row):
+    """Brute force: a NaN ranks above every number, then the largest value;
+    the lowest index wins ties."""
+    best = None
+    for k, v in enumerate(row):
+        if best is None:
+            best = k
+            continue
+        b = row[best]
+        if math.isnan(b):
+            continue
+        if math.isnan(v) or v > b:
+            best = k
+    return best
+
+
+def test_argmax_nan_and_inf_convention():
+    g = _rng(77)
+    x = g.integers(-3, 4, size=(40, 9)).astype(np.float64)
+    for r in range(0, 40, 2):
+        x[r, g.integers(0, 9)] = np.nan
+    for r in range(1, 40, 4):
+        x[r, g.integers(0, 9)] = np.inf
+    x[3, :] = np.nan
+    x[5, 2] = np.nan
+    x[5, 6] = np.nan
+    t = g.integers(0, 9, size=40)
+    r = ce_forward(x, t, reduction="none")
+    want = np.array([_argmax_nan_first(row) for row in x])
+    np.testing.assert_array_equal(r.argmax, want)
+    # torch orders NaN the same way (first occurrence)
+    np.testing.assert_array_equal(torch.argmax(torch.from_numpy(x), dim=1).numpy(), want)
+    bad = np.isnan(x).any(1) | np.isposinf(x).any(1)
+    assert np.all(np.isnan(r.loss[bad])) and np.all(np.isfinite(r.loss[~bad]))
+    assert np.all(np.isnan(r.grad[bad])) and np.all(np.isfinite(r.grad[~bad]))
