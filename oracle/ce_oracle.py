@@ -44,6 +44,9 @@ Readings where the pages are silent (each is a plain reading):
   (all ones when absent), W = sum_k w_k:
       l_i = -(1 - eps) * w_y * log p_y - (eps / V) * sum_k w_k * log p_k
   and the mean divides sum_i l_i by D = sum over counted rows of w_y.
+  With eps = 0 (the Module Parameters default: no smoothing) the second
+  term is absent, not 0 times the sum: a -inf logit elsewhere in the row
+  leaves the loss finite, as torch's cross_entropy does.
 * z-loss: zeta_i = lse_square_scale * lse_i**2, not class-weighted, over the
   softcapped logits; the mean divides sum_i zeta_i by n (counted rows).
   The returned loss includes it; z_loss returns it alone.
@@ -208,7 +211,9 @@ def rows_forward(x_rows, target_rows, *, V: int, alpha: float, beta: float,
         logp = z - lse                                        # log-softmax
         logp_y = logp[np.arange(idx.size), y]
         w_y = w[y]
-        ce_rows = -(1.0 - eps) * w_y * logp_y - (eps / V) * (logp @ w)
+        ce_rows = -(1.0 - eps) * w_y * logp_y
+        if eps > 0.0:                                         # smoothing term only when on
+            ce_rows = ce_rows - (eps / V) * (logp @ w)
         zeta_rows = lam * lse[:, 0] ** 2
         ce[idx] = ce_rows
         zeta[idx] = zeta_rows

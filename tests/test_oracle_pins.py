@@ -490,3 +490,20 @@ def test_argmax_nan_and_inf_convention():
     bad = np.isnan(x).any(1) | np.isposinf(x).any(1)
     assert np.all(np.isnan(r.loss[bad])) and np.all(np.isfinite(r.loss[~bad]))
     assert np.all(np.isnan(r.grad[bad])) and np.all(np.isfinite(r.grad[~bad]))
+
+
+def test_minus_inf_logit_without_smoothing_matches_torch():
+    """A -inf logit away from the target: without smoothing the loss is
+    -log p_y (finite) and the gradient finite, as torch computes it; with
+    smoothing the term eps/V * log p_k of that class is +inf."""
+    x = np.array([[0.5, -np.inf, 2.0, -1.0], [1.0, 0.0, -np.inf, 3.0]])
+    t = np.array([2, 3])
+    r = ce_forward(x, t, reduction="none")
+    want = torch.nn.functional.cross_entropy(torch.from_numpy(x), torch.from_numpy(t),
+                                             reduction="none").numpy()
+    np.testing.assert_allclose(r.loss, want, rtol=1e-14)
+    xt = torch.from_numpy(x).requires_grad_(True)
+    torch.nn.functional.cross_entropy(xt, torch.from_numpy(t), reduction="sum").backward()
+    np.testing.assert_allclose(r.grad, xt.grad.numpy(), rtol=1e-14, atol=1e-300)
+    rs = ce_forward(x, t, label_smoothing=0.1, reduction="none")
+    assert np.all(np.isposinf(rs.loss))
