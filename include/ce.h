@@ -35,6 +35,15 @@
  * Rows whose target is outside [0, V) and not ignore_index get a NaN loss,
  * a zero gradient and argmax -1, are not counted, and set a device error
  * bit (see CE_F_CHECK_TARGETS).
+ * Non-finite logits in counted rows follow IEEE arithmetic: a NaN or a +inf
+ * makes the row's loss and gradient NaN; argmax ranks a NaN above every
+ * number (the first NaN of the row), as numpy and torch order it.
+ * Rows longer than one workgroup holds are split over a group of workgroups
+ * that exchange partials and wait (a bounded number of polls) for each
+ * other. If a wait gives up, which needs the group's workgroups not to be
+ * resident together, nothing wrong is returned silently: the rows involved
+ * get NaN loss and gradient, the reduced outputs are NaN, and
+ * CE_F_CHECK_TARGETS returns CE_E_EXCHANGE.
  *
  * Conventions for every call:
  *  - Pointers marked [device] are HIP device pointers; the library never
@@ -68,7 +77,10 @@ typedef enum {
   CE_E_PARAM = -4,        /* bad reduction, label_smoothing, softcap, scale    */
   CE_E_WORKSPACE = -5,    /* workspace NULL, too small or not 256-B aligned    */
   CE_E_HIP = -6,          /* a HIP runtime call or kernel launch failed        */
-  CE_E_TARGET_RANGE = -7  /* CE_F_CHECK_TARGETS: a target outside [0, V)      */
+  CE_E_TARGET_RANGE = -7, /* CE_F_CHECK_TARGETS: a target outside [0, V)      */
+  CE_E_EXCHANGE = -8      /* CE_F_CHECK_TARGETS: a row split over workgroups   */
+                          /* gave up waiting for one of its parts (its values */
+                          /* and the reduced outputs are NaN)                 */
 } ce_status;
 
 typedef enum { CE_F32 = 0, CE_BF16 = 1 } ce_dtype;
@@ -78,16 +90,20 @@ typedef enum { CE_RED_NONE = 0, CE_RED_MEAN = 1, CE_RED_SUM = 2 } ce_reduction;
 enum {
   CE_F_GRAD = 1u << 0,          /* overwrite logits with d loss / d logits     */
   CE_F_CHECK_TARGETS = 1u << 4, /* wait for the GPU; CE_E_TARGET_RANGE if any  */
-                                /* target is outside [0, V) and not ignored    */
+                                /* target is outside [0, V) and not ignored,   */
+                                /* CE_E_EXCHANGE if a split row's wait gave up */
   CE_F_FORCE_FUSED = 1u << 5,   /* test hooks: pick the kernel path            */
   CE_F_FORCE_SPLITV = 1u << 6,
   CE_F_FORCE_SCALAR = 1u << 7,
-  CE_F_SHAPE_ALT = 1u << 8      /* test hook: the other fused layout where a   */
+  CE_F_SHAPE_ALT = 1u << 8,     /* test hook: the other fused layout where a   */
                                 /* row size has two (rows of 2 K to 16 K       */
                                 /* 16-byte vectors: 1024-thread workgroups vs  */
                                 /* 256/512-thread ones; 16 K to 32 K: a pair   */
                                 /* of 1024-thread workgroups per row vs four   */
                                 /* 512-thread ones)                            */
+  CE_F_EXCHANGE_ONE_POLL = 1u << 9 /* test hook: a row split over workgroups  */
+                                /* polls its parts' partials once before it    */
+                                /* gives up (forces the failure path below)    */
 };
 
 /* Kernel paths (ce_plan_path). */

@@ -27,6 +27,7 @@ CE_E_PARAM = -4
 CE_E_WORKSPACE = -5
 CE_E_HIP = -6
 CE_E_TARGET_RANGE = -7
+CE_E_EXCHANGE = -8
 
 CE_F32 = 0
 CE_BF16 = 1
@@ -42,6 +43,7 @@ CE_F_FORCE_FUSED = 1 << 5
 CE_F_FORCE_SPLITV = 1 << 6
 CE_F_FORCE_SCALAR = 1 << 7
 CE_F_SHAPE_ALT = 1 << 8
+CE_F_EXCHANGE_ONE_POLL = 1 << 9
 
 CE_PATH_FUSED = 1
 CE_PATH_SPLITV = 2

@@ -88,6 +88,8 @@ CE_API ce_status ce_forward(void* logits, int dtype, int64_t rows, int64_t V, in
   p.part = reinterpret_cast<cedev::Partial*>(ws + L.part);
   const uint32_t ep = next_epoch();
   p.epoch = ep;
+  p.xstamp = ep;
+  p.spin_limit = (flags & CE_F_EXCHANGE_ONE_POLL) ? 1 : 0;
   p.S = pl.S;
   p.chunk_vec = pl.chunk_vec;
 
@@ -98,14 +100,7 @@ CE_API ce_status ce_forward(void* logits, int dtype, int64_t rows, int64_t V, in
                                           : cehost::launch_forward_f32(pl, p, st);
     if (e != hipSuccess) return CE_E_HIP;
   }
-  if (flags & CE_F_CHECK_TARGETS) {
-    uint32_t err = 0;
-    if (hipMemcpyAsync(&err, &p.hdr->err, sizeof(err), hipMemcpyDeviceToHost, st) != hipSuccess)
-      return CE_E_HIP;
-    if (hipStreamSynchronize(st) != hipSuccess) return CE_E_HIP;
-    if (err & 1u) return CE_E_TARGET_RANGE;
-    if (err & 2u) return CE_E_HIP;  // a row pair whose partner never published
-  }
+  if (flags & CE_F_CHECK_TARGETS) return check_status(p.hdr, ep, st);
   return CE_OK;
 }
 
@@ -188,6 +183,8 @@ CE_API const char* ce_status_string(int status) {
     case CE_E_WORKSPACE: return "workspace NULL, too small or not 256-byte aligned";
     case CE_E_HIP: return "HIP runtime or kernel launch error";
     case CE_E_TARGET_RANGE: return "a target is outside [0, V) and not ignore_index";
+    case CE_E_EXCHANGE:
+      return "a row split over workgroups gave up waiting for one of its parts (NaN results)";
     default: return "unknown status";
   }
 }

@@ -40,10 +40,13 @@ __device__ __forceinline__ float rcp(float v) { return __builtin_amdgcn_rcpf(v);
 // so tanh needs a small *relative* error near 0 (where 1 - 2/(e^{2u}+1)
 // cancels) as well as exact saturation:
 //  * |u| < 0.55: u + u^3 Q(u^2), Q of degree 4, coefficients fitted here by
-//    Lawson-weighted least squares to tanh(u)/u on [0, 0.55] (relative fit
-//    error 9e-10; about 1e-7 relative once evaluated in fp32).
+//    Lawson-weighted least squares to tanh(u)/u on [0, 0.55] (the polynomial
+//    with these fp32 coefficients is within 3.5e-9 relative of tanh in exact
+//    arithmetic; within 1e-7 relative once evaluated in fp32).
 //  * |u| >= 0.55: sign(u) (1 - 2 / (e^{2|u|} + 1)) with one Newton step on the
-//    reciprocal; |u| is clamped to 15, where tanh rounds to 1 in fp32.
+//    reciprocal; |u| is clamped to 15, where tanh rounds to 1 in fp32 (a
+//    NaN is not clamped: it reaches the exponential and stays NaN, as it
+//    does on the polynomial branch).
 constexpr float kTanhSplit = 0.55f;
 constexpr float kTanhQ1 = -0.3333331048488617f;
 constexpr float kTanhQ2 = 0.13332460820674896f;
@@ -62,7 +65,8 @@ __device__ __forceinline__ float tanh_poly(float u) {
 }
 
 __device__ __forceinline__ float tanh_exp(float u) {
-  const float a = __builtin_fminf(__builtin_fabsf(u), 15.0f);
+  const float au = __builtin_fabsf(u);
+  const float a = au > 15.0f ? 15.0f : au;  // false for NaN: NaN propagates
   const float d = ex2(a * (2.0f * kLog2e)) + 1.0f;
   float r = rcp(d);
   r = __builtin_fmaf(r, __builtin_fmaf(-d, r, 1.0f), r);
@@ -197,7 +201,9 @@ struct Header {
   float alpha;           // gradient scale of the cross-entropy part
   float beta;            // gradient scale of the z-loss part
   uint32_t err;          // bit 0: a target outside [0, V) that is not ignore_index
-  uint32_t pad0[23];
+  uint32_t xerr_epoch;   // stamp of the last call in which a split row's exchange
+                         // gave up waiting for a part (never reset: stamps are unique)
+  uint32_t pad0[22];
   uint32_t done;         // arrival counter of the last-block epilogue (byte 128)
   uint32_t pad1[15];
   uint32_t next;         // row claims of the persistent row kernel (byte 192)
@@ -244,6 +250,9 @@ struct Params {
   float* row_stats;                    // (rows, 2) shift m and log2 s per row, or null
   Partial* part;                       // (rows, S) split-V partials; 128 bytes per row for row pairs
   uint32_t epoch;                      // unique per forward call: row-pair exchange stamp
+  int spin_limit;                      // polls before a split row's exchange gives up (0: default)
+  uint32_t xstamp;                     // unique per call (non-zero): stamped into hdr->xerr_epoch
+                                       // when an exchange gives up, checked by the epilogue
   int S;                               // chunks per row (split-V)
   int chunk_vec;                       // vectors per chunk (split-V)
 };
@@ -261,9 +270,11 @@ __device__ __forceinline__ void ms_combine(float& m, float& s, float m2, float s
   m = mn;
 }
 
-// Larger value wins; on equal values the lower index wins.
+// Larger value wins, a NaN ranking above every number (the order numpy and
+// torch give argmax); on equal values, or two NaNs, the lower index wins.
 __device__ __forceinline__ void arg_combine(float& v, int& i, float v2, int i2) {
-  const bool take = (v2 > v) || (v2 == v && i2 < i);
+  const bool n1 = v != v, n2 = v2 != v2;
+  const bool take = n2 ? (!n1 || i2 < i) : (!n1 && ((v2 > v) || (v2 == v && i2 < i)));
   v = take ? v2 : v;
   i = take ? i2 : i;
 }
@@ -455,6 +466,11 @@ __device__ __forceinline__ void epilogue_reduce(const Params& p) {
       nc += s_cnt[0][w];
       ncount += s_cnt[1][w];
     }
+    // A split row whose exchange gave up in this call poisons the reduced
+    // outputs (its own values are NaN already when its part 0 gave up).
+    const bool xfail = p.xstamp != 0u && __hip_atomic_load(&p.hdr->xerr_epoch, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT) == p.xstamp;
+    if (xfail) tce = tz = __builtin_nan("");
     const double n = static_cast<double>(ncount);
     const double D = (p.has_hdr || p.self_scales)
                          ? __hip_atomic_load(&p.hdr->D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
@@ -466,7 +482,8 @@ __device__ __forceinline__ void epilogue_reduce(const Params& p) {
       if (p.loss) p.loss[0] = static_cast<float>(tce + tz);
       if (p.z_loss) p.z_loss[0] = static_cast<float>(tz);
     }
-    if (p.reduction != 0 && p.acc) p.acc[0] = static_cast<float>(static_cast<double>(nc) / n);
+    if (p.reduction != 0 && p.acc)
+      p.acc[0] = xfail ? __builtin_nanf("") : static_cast<float>(static_cast<double>(nc) / n);
     if (p.counts) {
       p.counts[0] = ncount;
       p.counts[1] = nc;

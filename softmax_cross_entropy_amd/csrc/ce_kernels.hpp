@@ -9,11 +9,11 @@
 // MI355X design (not the page's Triton loop):
 //  * rows_kernel: persistent workgroups, one row at a time each, rows claimed
 //    in the order workgroups finish. The whole row is read from HBM once
-//    with non-temporal dwordx4 buffer loads and kept on chip (VGPRs, plus
-//    LDS filled by buffer_load ... lds for the largest rows), so the
+//    with non-temporal dwordx4 buffer loads and kept in VGPRs, so the
 //    gradient pass reads registers instead of re-reading HBM: 1 read + 1
 //    write per logit. fp32 rows keep exp(x - group max) in place of x, so
-//    the gradient pass is one multiply per element.
+//    the gradient pass is one multiply per element. Longer rows are split
+//    over a group of workgroups (ce_wide.hpp).
 //  * splitv_partial_kernel + splitv_finish_kernel: the row is split into S
 //    chunks held by different workgroups; stage 1 writes per-chunk partials
 //    (max, sum, argmax, target logit), stage 2 combines them in a fixed
@@ -90,7 +90,9 @@ __device__ __forceinline__ void pass1_vec(const Params& p, Acc& a, const float (
   float vm = f[0];
 #pragma unroll
   for (int i = 1; i < EPV; ++i) vm = __builtin_fmaxf(vm, f[i]);
-  // Slots are visited LDS-first, so the tie-break compares indices.
+  // Slots may be visited out of index order (a wave reduction combines
+  // them), so the tie-break compares indices. vm ignores NaN; a chunk
+  // holding one is found by first_nan.
   const bool take = (vm > a.bv) || (vm == a.bv && slot < a.bi);
   a.bv = take ? vm : a.bv;
   a.bi = take ? slot : a.bi;
@@ -142,9 +144,7 @@ __device__ __forceinline__ void pass1_vec(const Params& p, Acc& a, const float (
 // Pass 1 over one scalar element (row tails and the unaligned path).
 template <int SC, int SM>
 __device__ __forceinline__ void pass1_one(const Params& p, Acc& a, float x, int slot, int64_t k) {
-  const bool take = (x > a.bv) || (x == a.bv && slot < a.bi);
-  a.bv = take ? x : a.bv;
-  a.bi = take ? slot : a.bi;
+  arg_combine(a.bv, a.bi, x, slot);
   const float z = zval<SC>(p, x);
   const float mn = __builtin_fmaxf(a.m, z);
   a.s = a.s * ex2((a.m - mn) * kLog2e) + ex2((z - mn) * kLog2e);
@@ -377,6 +377,57 @@ __device__ __forceinline__ u4 grad_vec_e(const Params& p, const RowScalars& rs, 
   return F32::pack(g);
 }
 
+// Argmax of a row (or part) holding a NaN: the lowest element index holding
+// a NaN, the order numpy and torch give argmax. Such a row's sum of
+// exponentials is NaN (so is one holding +inf, which this finds no NaN in),
+// so the search runs only then. Over a thread's slots k (vectors
+// k * BLOCK + tid < nv, the first at element e0) and its row-tail element
+// xt; REREAD: the slots hold exponentials, so the raw logits are loaded
+// again (before any gradient store). Reduced over the wave; kNoIndex if none.
+template <class E, int BLOCK, int NREG, bool REREAD>
+__device__ __forceinline__ int first_nan(const u4 (&r)[NREG], __amdgpu_buffer_rsrc_t rsrc,
+                                         int voff, int nv, int tid, int64_t e0, float xt,
+                                         bool has_tail, int64_t tail_idx) {
+  constexpr int EPV = E::EPV;
+  // the row tail comes after every vector, so any vector NaN replaces it
+  int nc = (has_tail && xt != xt) ? static_cast<int>(tail_idx) : kNoIndex;
+  if constexpr (REREAD) {
+    // one vector in flight at a time (a rolled loop): the slots stay live
+    // for the gradient pass, so this path must not add registers
+#pragma nounroll
+    for (int k = NREG - 1; k >= 0; --k) {
+      if (k * BLOCK < nv) {  // uniform
+        const u4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, k * BLOCK * 16, 0);
+        float f[EPV];
+        E::unpack(v, f);
+        const bool in = k * BLOCK + tid < nv;
+#pragma unroll
+        for (int i = EPV - 1; i >= 0; --i)
+          nc = (in && f[i] != f[i])
+                   ? static_cast<int>(e0 + static_cast<int64_t>(k * BLOCK + tid) * EPV + i)
+                   : nc;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = NREG - 1; k >= 0; --k) {
+      if (k * BLOCK < nv) {  // uniform
+        float f[EPV];
+        E::unpack(r[k], f);
+        const bool in = k * BLOCK + tid < nv;
+#pragma unroll
+        for (int i = EPV - 1; i >= 0; --i)
+          nc = (in && f[i] != f[i])
+                   ? static_cast<int>(e0 + static_cast<int64_t>(k * BLOCK + tid) * EPV + i)
+                   : nc;
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) nc = min(nc, __shfl_xor(nc, off, 64));
+  return nc;
+}
+
 // Outputs of a row that is ignored (gradient exactly +0.0, never read) or
 // whose target is out of range (NaN loss).
 template <class E, int BLOCK>
@@ -401,6 +452,7 @@ template <int BLOCK>
 struct RowShared {
   Acc acc[BLOCK / 64];
   int cand[BLOCK / 64];
+  int nanc[BLOCK / 64];      // per wave: first NaN index (rows holding one)
   RowScalars rs;
   float xy;
   int64_t next_row, next_y;  // persistent kernel: the row claimed next and its target
@@ -655,6 +707,12 @@ __device__ __forceinline__ void fused_row(const Params& p, int64_t row, int64_t 
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) cand = min(cand, __shfl_xor(cand, off, 64));
   if (lane == 0) s_cand[wave] = cand;
+  const bool row_nan = t.s != t.s;  // uniform: a NaN (or +inf) in the row
+  if (row_nan) {
+    const int nc = first_nan<E, BLOCK, NS, KEEP_E>(r, rsrc, voff, nv, tid, 0, xt, tid < tail,
+                                                   tail0 + tid);
+    if (lane == 0) sh.nanc[wave] = nc;
+  }
   __syncthreads();
 
   if (tid == 0) {
@@ -665,7 +723,13 @@ __device__ __forceinline__ void fused_row(const Params& p, int64_t row, int64_t 
     int arg = s_cand[0];
 #pragma unroll
     for (int w = 1; w < NW; ++w) arg = min(arg, s_cand[w]);
-    if (arg == kNoIndex) arg = 0;  // no finite or infinite value: index 0
+    if (row_nan) {
+      int na = kNoIndex;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) na = min(na, sh.nanc[w]);
+      if (na != kNoIndex) arg = na;
+    }
+    if (arg == kNoIndex) arg = 0;  // no value above -inf: index 0
     double W, alpha, beta;
     load_scales(p, W, alpha, beta);
     const float wy = p.weight ? p.weight[y] : 1.0f;
@@ -869,6 +933,15 @@ __global__ __launch_bounds__(BLOCK) void splitv_partial_kernel(Params p) {
       s_arg = t.bi * EPV + pos;
     }
   }
+  // a chunk holding a NaN: its first NaN is the chunk's argmax
+  __shared__ int s_nan[NW];
+  const bool chunk_nan = t.s != t.s;  // uniform
+  if (chunk_nan) {
+    const int nc = first_nan<E, BLOCK, NREG, false>(r, rsrc, voff, nv, tid,
+                                                    static_cast<int64_t>(v0) * EPV, xt,
+                                                    has_tail && tid < tail, tail0 + tid);
+    if (lane == 0) s_nan[wave] = nc;
+  }
   __syncthreads();
   if (tid == 0) {
     Partial q;
@@ -877,6 +950,14 @@ __global__ __launch_bounds__(BLOCK) void splitv_partial_kernel(Params p) {
     q.sz = t.sz;
     q.bv = t.bv;
     q.bi = s_arg;
+    if (chunk_nan) {
+      int na = kNoIndex;
+      for (int w = 0; w < NW; ++w) na = min(na, s_nan[w]);
+      if (na != kNoIndex) {
+        q.bv = __builtin_nanf("");
+        q.bi = na;
+      }
+    }
     q.xy = xy;
     q.has_y = y_here ? 1 : 0;
     q.pad = 0;

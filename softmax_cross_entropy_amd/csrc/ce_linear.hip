@@ -306,6 +306,8 @@ CE_API ce_status ce_linear_forward(const void* hidden, int64_t ld_hidden, const 
   base.row_z = reinterpret_cast<float*>(ws + L.row_z);
   base.row_ok = reinterpret_cast<int32_t*>(ws + L.row_ok);
   base.part = reinterpret_cast<cedev::Partial*>(ws + L.part);
+  base.xstamp = next_epoch();  // one stamp for the call; each chunk has its own epoch
+  base.spin_limit = (flags & CE_F_EXCHANGE_ONE_POLL) ? 1 : 0;
 
   // n, D and the mean scales over the whole batch, before any gradient.
   if (base.has_hdr && cehost::launch_prologue(base, st) != hipSuccess) return CE_E_HIP;
@@ -395,13 +397,6 @@ CE_API ce_status ce_linear_forward(const void* hidden, int64_t ld_hidden, const 
     linear_epilogue_kernel<<<1, kEpilogueBlock, 0, st>>>(base);
     if (hipGetLastError() != hipSuccess) return CE_E_HIP;
   }
-  if (flags & CE_F_CHECK_TARGETS) {
-    uint32_t err = 0;
-    if (hipMemcpyAsync(&err, &base.hdr->err, sizeof(err), hipMemcpyDeviceToHost, st) != hipSuccess)
-      return CE_E_HIP;
-    if (hipStreamSynchronize(st) != hipSuccess) return CE_E_HIP;
-    if (err & 1u) return CE_E_TARGET_RANGE;
-    if (err & 2u) return CE_E_HIP;  // a row pair whose partner never published
-  }
+  if (flags & CE_F_CHECK_TARGETS) return check_status(base.hdr, base.xstamp, st);
   return CE_OK;
 }

@@ -5,6 +5,7 @@
 
 #include <math.h>
 #include <stdint.h>
+#include <stddef.h>
 #include <string.h>
 
 #include <atomic>
@@ -198,6 +199,21 @@ inline void fill_options(cedev::Params& p, void* logits, int64_t rows, int64_t V
 inline uint32_t next_epoch() {
   static std::atomic<uint32_t> calls{0};
   return 0xC0000000u | (calls.fetch_add(1, std::memory_order_relaxed) % 0x3FFFFFFFu + 1u);
+}
+
+// CE_F_CHECK_TARGETS: wait for the call, then report a target out of range
+// (the prologue's error bit) or a split row's exchange that gave up (the
+// call's stamp in the header).
+inline ce_status check_status(const cedev::Header* hdr, uint32_t stamp, hipStream_t st) {
+  uint32_t w[2] = {0u, 0u};
+  static_assert(offsetof(cedev::Header, xerr_epoch) == offsetof(cedev::Header, err) + 4,
+                "err and xerr_epoch are adjacent");
+  if (hipMemcpyAsync(w, &hdr->err, sizeof(w), hipMemcpyDeviceToHost, st) != hipSuccess)
+    return CE_E_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return CE_E_HIP;
+  if (w[1] == stamp) return CE_E_EXCHANGE;
+  if (w[0] & 1u) return CE_E_TARGET_RANGE;
+  return CE_OK;
 }
 
 }  // namespace ceplan

@@ -31,11 +31,17 @@
 
 namespace cedev {
 
-// Polls of the other parts' words before a group gives up and flags the row
-// (each poll is one device-coherent load, about a microsecond); a part that
-// never arrives would otherwise hold the workgroup forever. After one
-// such failure the workgroup polls once per row: the error bit is set and
-// the launch ends in bounded time.
+// Polls of the other parts' words before a group gives up (each poll is one
+// device-coherent load, about a microsecond); a part that never arrives
+// would otherwise hold the workgroup forever. A part that gives up on a
+// row's partials poisons what it writes of that row: NaN gradient over its
+// part, and, in part 0, NaN over the rest of the row and NaN per-row loss
+// and z-loss with argmax -1; it stamps the call's epoch into the header
+// (hdr->xerr_epoch = xstamp), which turns the reduced outputs NaN and makes
+// CE_F_CHECK_TARGETS report CE_E_EXCHANGE. After one such failure the
+// workgroup polls once per row, so the launch ends in bounded time. Parts
+// other than 0 still wait the full limit for part 0's words 5-7 (their
+// next row), so they go on writing their part of every later row.
 constexpr int kGroupSpinLimit = 1 << 22;
 
 // Exchange within a row's group of G parts (a pair, or four quarters)
@@ -92,6 +98,7 @@ template <int BLOCK>
 struct WideShared {
   Acc acc[BLOCK / 64];
   int cand[BLOCK / 64];
+  int nanc[BLOCK / 64];    // per wave: first NaN index (parts holding one)
   RowScalars rs;
   float xy;
   int64_t next_t, next_y;  // the part (whole rows) or row (split rows) next, and its target
@@ -151,20 +158,43 @@ __device__ __forceinline__ void group_reset(const Params& p, uint32_t c) {
 
 // Thread 0: the group's next row and its target into the block-shared
 // state (the other parts take them from part 0's words 5-7; if they never
-// came, the workgroup stops).
+// came, the workgroup stops). ok: every part's words arrived in time; else
+// the call's epoch is stamped into the header and later exchanges of the
+// workgroup poll once.
 template <int G, class SH>
-__device__ __forceinline__ void group_next(const Params& p, int h, bool ok, uint32_t c,
-                                          int64_t ny, const uint32_t (&w0)[kSlotWords], SH& sh) {
+__device__ __forceinline__ void group_next(const Params& p, int h, bool ok, bool have_next,
+                                          uint32_t c, int64_t ny,
+                                          const uint32_t (&w0)[kSlotWords], SH& sh) {
   if (h == 0) {
     sh.next_t = group_row<G>(p, c);
     sh.next_y = ny;
   } else {
-    sh.next_t = ok ? static_cast<int64_t>(w0[5]) : p.rows;
+    sh.next_t = have_next ? static_cast<int64_t>(w0[5]) : p.rows;
     sh.next_y = static_cast<int64_t>((static_cast<uint64_t>(w0[7]) << 32) | w0[6]);
   }
   if (!ok) {
-    atomicOr(&p.hdr->err, 2u);
+    __hip_atomic_store(&p.hdr->xerr_epoch, p.xstamp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     sh.limit = 1;
+  }
+}
+
+// Part 0 of a row whose exchange gave up: NaN over the whole row's gradient
+// (its nv_row vectors and the row tail). GB: the compacted bf16 layout
+// (element e at byte 2 e).
+template <class E, int BLOCK, int GB>
+__device__ __forceinline__ void poison_row(char* rp, int nv_row, int64_t tail0, int tail,
+                                           int tid) {
+  if constexpr (GB) {
+    const u2 q = {0x7fc07fc0u, 0x7fc07fc0u};
+    for (int j = tid; j < nv_row; j += BLOCK)
+      __builtin_nontemporal_store(q, reinterpret_cast<u2*>(rp) + j);
+    if (tid < tail) reinterpret_cast<uint16_t*>(rp)[tail0 + tid] = 0x7fc0u;
+  } else {
+    const uint32_t w = E::EPV == 4 ? 0x7fc00000u : 0x7fc07fc0u;
+    const u4 q = {w, w, w, w};
+    for (int j = tid; j < nv_row; j += BLOCK)
+      __builtin_nontemporal_store(q, reinterpret_cast<u4*>(rp) + j);
+    if (tid < tail) E::st(rp, tail0 + tid, __builtin_nanf(""));
   }
 }
 
@@ -259,9 +289,9 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
           next_words<PARTS>(p, claim, ny, w);
           slot_publish(p, slots, w, kPartialWords, kSlotWords);
         } else {
-          ok = slot_poll(p, slots, w, kPartialWords, kSlotWords, sh.limit);
+          ok = slot_poll(p, slots, w, kPartialWords, kSlotWords, kGroupSpinLimit);
         }
-        group_next<PARTS>(p, h, ok, claim, ny, w, sh);
+        group_next<PARTS>(p, h, ok, ok, claim, ny, w, sh);
       }
       __syncthreads();
       next_t = uniform_i64(sh.next_t);
@@ -418,8 +448,12 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
     // Every thread needs only the part's largest raw logit here; thread 0
     // combines the full records (in wave order) below.
     float bmax = s_acc[0].bv;
+    bool part_nan = s_acc[0].s != s_acc[0].s;  // a NaN (or +inf) in the part
 #pragma unroll
-    for (int w = 1; w < NW; ++w) bmax = __builtin_fmaxf(bmax, s_acc[w].bv);
+    for (int w = 1; w < NW; ++w) {
+      bmax = __builtin_fmaxf(bmax, s_acc[w].bv);
+      part_nan = part_nan || s_acc[w].s != s_acc[w].s;
+    }
 
     // ---- argmax: threads holding the part's maximum look for its first
     // position in their first group holding it; the block takes the lowest
@@ -462,6 +496,11 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) cand = min(cand, __shfl_xor(cand, off, 64));
     if (lane == 0) s_cand[wave] = cand;
+    if (part_nan) {
+      const int nc = first_nan<E, BLOCK, NREG, KEEP_E>(r, rsrc, voff, nv, tid, e0, xt,
+                                                       tid < tail, tail0 + tid);
+      if (lane == 0) sh.nanc[wave] = nc;
+    }
     __syncthreads();
 
     if (wave == 0) {
@@ -469,10 +508,11 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
       // holds wave l's record; the same tree every time, so bitwise
       // deterministic); lane 0 then owns the part's totals.
       Acc t;
-      int arg = kNoIndex;
+      int arg = kNoIndex, nanarg = kNoIndex;
       if (lane < NW) {
         t = s_acc[lane];
         arg = s_cand[lane];
+        if (part_nan) nanarg = sh.nanc[lane];
       } else {
         acc_init(t);
       }
@@ -484,9 +524,14 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
         ms_combine(t.m, t.s, m2, s2);
         t.sz += z2;
         arg = min(arg, __shfl_xor(arg, off, 64));
+        nanarg = min(nanarg, __shfl_xor(nanarg, off, 64));
       }
       t.bv = bmax;
       t.bi = arg;
+      if (nanarg != kNoIndex) {  // the part's first NaN ranks above every number
+        t.bv = __builtin_nanf("");
+        t.bi = nanarg;
+      }
       if constexpr (PARTS > 1) {
         // Lane 0 publishes this part's partial (part 0 adds the group's
         // next row); lanes 0 .. G-1 poll the other parts' slots, one slot
@@ -508,7 +553,11 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
         uint32_t w[kSlotWords] = {};
         const int nwords = lane == 0 ? kSlotWords : kPartialWords;
         bool done = !(lane < PARTS && lane != h);
+        // After `limit` polls the exchange has failed; a part other than 0
+        // then waits on (the full limit) only for part 0's words 5-7, the
+        // group's next row.
         const int limit = sh.limit;
+        bool failed = false;
         int it = 0;
         while (true) {
           if (!done) {
@@ -526,10 +575,14 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
             done = all;
           }
           if (__all(done)) break;
-          if (++it >= limit) break;
+          ++it;  // counts every poll round, so the limits below always end the loop
+          failed = failed || it >= limit;
+          if (failed && (h == 0 || __shfl(done ? 1 : 0, 0, 64) != 0)) break;
+          if (it >= kGroupSpinLimit) break;
           __builtin_amdgcn_s_sleep(1);
         }
-        const bool ok = __all(done);
+        const bool ok = !failed;
+        const bool have_next = h == 0 || __shfl(done ? 1 : 0, 0, 64) != 0;
         const float own_m = __shfl(t.m, 0, 64), own_s = __shfl(t.s, 0, 64);
         const float own_z = __shfl(t.sz, 0, 64), own_b = __shfl(t.bv, 0, 64);
         const int own_i = __shfl(t.bi, 0, 64);
@@ -558,16 +611,22 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
           } else {
             ms_combine(m, sum, mq, sq);
             sz += zq;
-            const bool take = bq > bv;  // ties keep the earlier part (lower indices)
+            // ties keep the earlier part (lower indices); a NaN ranks above
+            // every number, the earliest part's first
+            const bool take = (bq != bq) ? (bv == bv) : (bv == bv && bq > bv);
             bv = take ? bq : bv;
             bi = take ? iq : bi;
           }
+        }
+        if (!ok) {  // poisoned: NaN row scalars, no argmax
+          m = sum = sz = bv = __builtin_nanf("");
+          bi = -1;
         }
         uint32_t w0[kSlotWords] = {};  // part 0's words 5-7: the next row (parts 1 .. G-1)
         w0[5] = __shfl(w[5], 0, 64);
         w0[6] = __shfl(w[6], 0, 64);
         w0[7] = __shfl(w[7], 0, 64);
-        if (lane == 0) group_next<PARTS>(p, h, ok, claim, ny, w0, sh);
+        if (lane == 0) group_next<PARTS>(p, h, ok, have_next, claim, ny, w0, sh);
         t.m = m;
         t.s = sum;
         t.sz = sz;
@@ -602,7 +661,12 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
     next_y = uniform_i64(sh.next_y);
 
     // ---- pass 2: the gradient from on-chip data, written over the logits ----
-    if (p.grad) {
+    // (part 0 of a row whose exchange gave up, argmax -1, writes NaN over the
+    // whole row instead, so no part of it keeps stale logits even if another
+    // part stopped)
+    if (PARTS > 1 && p.grad && h == 0 && sh.rs.arg < 0) {
+      poison_row<E, BLOCK, GB>(rp, nv_row, tail0, static_cast<int>(p.V - tail0), tid);
+    } else if (p.grad) {
       const RowScalars rs = sh.rs;
       // GB: this part's bf16 gradient bytes and the scale applied before rounding
       __amdgpu_buffer_rsrc_t rsrc_g = rsrc;
@@ -684,7 +748,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
   // self_scales: every workgroup counts n and D once, before its parts
   // (kept out of the part loop, whose registers it would otherwise crowd)
   if (p.self_scales) compute_self_scales<BLOCK>(p);
-  if (threadIdx.x == 0) sh.limit = kGroupSpinLimit;
+  if (threadIdx.x == 0) sh.limit = p.spin_limit > 0 ? p.spin_limit : kGroupSpinLimit;
   if constexpr (PARTS > 1) {
     // group j = workgroups G j ... G j + G - 1 starts with row j (the grid
     // holds at most one group per row)
@@ -729,7 +793,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
   __shared__ WideShared<BLOCK> sh;
   __shared__ int s_last;
   if (p.self_scales) compute_self_scales<BLOCK>(p);
-  if (threadIdx.x == 0) sh.limit = kGroupSpinLimit;
+  if (threadIdx.x == 0) sh.limit = p.spin_limit > 0 ? p.spin_limit : kGroupSpinLimit;
   const int h = static_cast<int>(blockIdx.x % PARTS);
   int64_t row = blockIdx.x / PARTS;
   int64_t y = p.target[row];

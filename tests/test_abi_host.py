@@ -59,7 +59,7 @@ def test_missing_library_fails_loudly(tmp_path):
 
 
 def test_status_strings():
-    for s in range(-7, 1):
+    for s in range(-8, 1):
         assert _lib.ce_status_string(s) and _lib.ce_status_string(s) != "unknown status"
     assert _lib.ce_status_string(42) == "unknown status"
 

@@ -146,6 +146,30 @@ def test_linear_parity(opt, reduction, shape, chunk, flags):
            softcap=o.get("softcap"), reduction=reduction, what=f"{opt}/{reduction}/{shape}")
 
 
+@pytest.mark.parametrize("reduction", ["mean", "sum", "none"])
+@pytest.mark.parametrize("shape,chunk", [((40, 32, 20000), 0), ((33, 32, 40003), 16)])
+def test_linear_auto_splitv(reduction, shape, chunk):
+    """Chunks of fewer than 256 rows of more than 4096 vectors take the
+    split-V path on their own (no test hook), every option on."""
+    from softmax_cross_entropy_amd import _lib
+    rows, H, V = shape
+    o = OPTS["all"]
+    cr = chunk or rows
+    ldl = (V + 3) // 4 * 4
+    plan = _lib.ce_plan_path(1 << 20, _lib.CE_F32, cr, V, ldl, 1 << 20, o["eps"], 0)
+    assert _lib.PATH_NAMES[plan] == "splitv"
+    x, w, t = _make(rows, H, V, rows + V + 1, rows // 6)
+    cw = 0.5 + 1.5 * torch.rand(V, generator=torch.Generator().manual_seed(V + 1))
+    _announce(name="linear-auto-splitv", rows=rows, H=H, V=V, chunk=chunk, reduction=reduction)
+    res = linear_forward_raw(x.to(DEV), w.to(DEV), t.to(DEV), cw.to(DEV), -100, o["eps"],
+                             o["lam"], o["softcap"], reduction, grad=True, z_loss=True,
+                             token_accuracy=True, argmax=True, counts=True, chunk_rows=chunk,
+                             flags=0)
+    torch.cuda.synchronize()
+    _check(x, w, t, res, cw=cw, eps=o["eps"], lam=o["lam"], softcap=o["softcap"],
+           reduction=reduction, what=f"auto-splitv/{reduction}/{shape}")
+
+
 @pytest.mark.parametrize("rows,V,chunk", [(64, 5000, 24), (600, 20000, 300)])
 @pytest.mark.parametrize("reduction", ["mean", "none"])
 def test_linear_autograd_grad_output(reduction, rows, V, chunk):

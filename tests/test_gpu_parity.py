@@ -1,9 +1,11 @@
 """GPU parity: the HIP path through the C ABI against the float64 oracle.
 
 Every case prints its name, shape, dtype, options and kernel path before it
-touches the GPU. Small cases compare every output element; the full-size
-workloads run in the benchmark's launch configuration (automatic path) and
-compare sampled rows with the oracle plus properties that hold at any size.
+touches the GPU. Every case compares every row's loss terms, argmax, counts
+and accuracy with the oracle; small and medium cases compare every gradient
+element, and the full-size workloads (run in the benchmark's launch
+configuration, automatic path) compare every row's gradient except at
+16384 x 262144, where a seeded sample of rows is compared.
 """
 
 import math
@@ -13,12 +15,13 @@ import pytest
 import torch
 
 import synth
-from oracle import rows_forward, summarize_targets
+from oracle import reduce_rows
 from parity import (OracleRef, assert_acc_exact, assert_grad_close, assert_loss_close,
-                    host_logits)
+                    host_logits, oracle_rows)
 from softmax_cross_entropy_amd import _lib, backward_, backward_recompute, forward_raw
-from softmax_cross_entropy_amd._lib import (CE_F_FORCE_FUSED, CE_F_FORCE_SCALAR,
-                                            CE_F_FORCE_SPLITV, CE_F_SHAPE_ALT)
+from softmax_cross_entropy_amd._lib import (CE_F_EXCHANGE_ONE_POLL, CE_F_FORCE_FUSED,
+                                            CE_F_FORCE_SCALAR, CE_F_FORCE_SPLITV,
+                                            CE_F_SHAPE_ALT)
 
 pytestmark = pytest.mark.gpu
 
@@ -473,7 +476,168 @@ def test_persistent_claims_reset_between_calls(alt):
 
 
 # ---------------------------------------------------------------------------
-# Full-size workloads in the benchmark's launch configuration
+# The planner's own split-V path (no test hook): batches of fewer than 256
+# rows with long rows, and rows longer than any fused shape holds. Chunks of
+# up to 1024 vectors take the 256 x 4 stage 1, longer ones the 512 x 16 one.
+# ---------------------------------------------------------------------------
+
+AUTO_SPLITV = [
+    # (dtype, V, rows, options); the comment gives the plan the library makes
+    (torch.bfloat16, 262144, 8, dict(weight=True, eps=0.1, softcap=30.0, lam=1e-4)),  # S 32 x 1024
+    (torch.bfloat16, 262144, 200, dict(weight=True, eps=0.1, softcap=30.0, lam=1e-4)),  # S 6 x 5462
+    (torch.float32, 1048576, 64, dict(eps=0.05, lam=1e-4)),                           # S 32 x 8192
+    (torch.float32, 262144, 300, dict(weight=True, eps=0.2)),                         # S 8 x 8192
+    (torch.float32, 200003, 40, dict(softcap=15.0)),                                  # ragged tail
+]
+
+
+@pytest.mark.parametrize("case", range(len(AUTO_SPLITV)))
+@pytest.mark.parametrize("reduction", ["mean", "none"])
+def test_planner_splitv(case, reduction):
+    dtype, V, rows, o = AUTO_SPLITV[case]
+    seed = 500 + case
+    x = synth.make_logits(rows, V, dtype, 2.0, seed)
+    t = synth.make_targets(rows, V, seed, max(1, rows // 10))
+    t[0] = V - 1  # a target in the last chunk (and the row tail)
+    wt = None
+    if o.get("weight"):
+        wt = 0.5 + 1.5 * torch.rand(V, generator=torch.Generator().manual_seed(seed))
+    stride = (V + 7) // 8 * 8
+    xd = _padded(x, stride)
+    assert _plan(xd, None if wt is None else wt.to(DEV), o.get("eps", 0.0), 0) == "splitv"
+    del xd
+    run_case(x, t, weight=wt, eps=o.get("eps", 0.0), lam=o.get("lam", 0.0),
+             softcap=o.get("softcap"), reduction=reduction, path="auto", stride=stride,
+             name=f"auto-splitv-{case}")
+
+
+# ---------------------------------------------------------------------------
+# Non-finite logits in counted rows: NaN makes the row's loss and gradient
+# NaN and is the row's argmax (its first NaN), +inf makes the row NaN (its
+# argmax stays the first +inf); with softcap, +inf saturates to the cap.
+# ---------------------------------------------------------------------------
+
+NAN_CASES = [
+    # (dtype, V, rows, path, options)
+    (torch.float32, 4099, 40, "fused", dict()),           # row kernel, exponentials kept
+    (torch.float32, 4099, 40, "fused", dict(softcap=5.0)),
+    (torch.bfloat16, 8195, 40, "fused", dict()),
+    (torch.bfloat16, 8195, 40, "fused", dict(softcap=5.0, eps=0.1)),
+    (torch.float32, 4099, 40, "splitv", dict()),
+    (torch.bfloat16, 4099, 40, "splitv", dict(softcap=5.0)),
+    (torch.float32, 4099, 40, "scalar", dict()),
+    (torch.bfloat16, 4099, 40, "scalar", dict(softcap=5.0)),
+    (torch.float32, 129001, 24, "fused", dict()),         # quarter rows
+    (torch.float32, 129001, 24, "fused", dict(softcap=20.0, lam=1e-3)),
+    (torch.bfloat16, 131001, 24, "fused", dict()),        # row pairs
+    (torch.bfloat16, 131001, 24, "fused_alt", dict(eps=0.1)),
+]
+
+
+@pytest.mark.parametrize("case", range(len(NAN_CASES)))
+@pytest.mark.parametrize("reduction", ["mean", "none"])
+def test_nonfinite_logits_in_counted_rows(case, reduction):
+    dtype, V, rows, path, o = NAN_CASES[case]
+    seed = 700 + case
+    x = synth.make_logits(rows, V, dtype, 2.0, seed)
+    t = synth.make_targets(rows, V, seed, 3)
+    g = torch.Generator().manual_seed(seed)
+    cols = lambda k: torch.randperm(V, generator=g)[:k].tolist()  # noqa: E731
+    for r in range(rows):
+        kind = r % 6
+        if kind == 0:
+            x[r, cols(1)[0]] = float("nan")
+        elif kind == 1:  # two NaNs and a large logit before them
+            c = sorted(cols(3))
+            x[r, c[0]] = 50.0
+            x[r, c[1]] = float("nan")
+            x[r, c[2]] = float("nan")
+        elif kind == 2:
+            x[r, cols(1)[0]] = float("inf")
+        elif kind == 3:
+            x[r, V - 1] = float("nan")  # in the row tail (V is not a multiple of a vector)
+        elif kind == 4:
+            x[r, cols(1)[0]] = float("-inf")
+    stride = (V + 7) // 8 * 8 if path != "scalar" else V
+    run_case(x, t, eps=o.get("eps", 0.0), lam=o.get("lam", 0.0), softcap=o.get("softcap"),
+             reduction=reduction, path=path, stride=stride, name=f"nonfinite-{case}")
+
+
+# ---------------------------------------------------------------------------
+# A split row's exchange that gives up is loud: forced from the host
+# (CE_F_EXCHANGE_ONE_POLL: one poll before giving up), every kernel still
+# ends normally, CE_F_CHECK_TARGETS reports CE_E_EXCHANGE, the reduced
+# outputs are NaN, and every value is either NaN or the oracle's.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,V,rows,layout", [(torch.float32, 129001, 300, "fused"),
+                                                 (torch.bfloat16, 131001, 300, "fused"),
+                                                 (torch.float32, 129001, 300, "fused_alt")])
+@pytest.mark.parametrize("reduction", ["mean", "none"])
+def test_exchange_timeout_is_loud(dtype, V, rows, layout, reduction):
+    seed = 900 + V % 97
+    x = synth.make_logits(rows, V, dtype, 2.0, seed)
+    t = synth.make_targets(rows, V, seed, rows // 10)
+    stride = (V + 7) // 8 * 8
+    xd = _padded(x, stride)
+    td = t.to(DEV)
+    flags = PATH_FLAGS[layout] | CE_F_EXCHANGE_ONE_POLL | _lib.CE_F_GRAD | _lib.CE_F_CHECK_TARGETS
+    _announce(name="exchange-timeout", rows=rows, V=V, dtype=dtype, reduction=reduction,
+              layout=layout, plan=_plan(xd, None, 0.0, flags))
+    assert _plan(xd, None, 0.0, flags) == "fused"
+    dt = _lib.dtype_code(dtype)
+    shape = (rows,) if reduction == "none" else ()
+    loss = torch.empty(shape, device=DEV)
+    acc = torch.empty(shape, device=DEV)
+    arg = torch.empty((rows,), device=DEV, dtype=torch.int64)
+    counts = torch.empty((2,), device=DEV, dtype=torch.int64)
+    wsb = _lib.ce_workspace_bytes(rows, V, dt, flags)
+    ws = torch.zeros((wsb,), device=DEV, dtype=torch.uint8)
+    s = torch.cuda.current_stream().cuda_stream
+    st = _lib.ce_forward(xd.data_ptr(), dt, rows, V, stride, td.data_ptr(), 0, -100, 0.0, 0.0,
+                         0.0, _lib.REDUCTION_CODES[reduction], flags, loss.data_ptr(), 0,
+                         acc.data_ptr(), arg.data_ptr(), counts.data_ptr(), 0, ws.data_ptr(),
+                         wsb, s)
+    torch.cuda.synchronize()
+    assert st == _lib.CE_E_EXCHANGE, _lib.ce_status_string(st)
+    ref = OracleRef(host_logits(x), t.numpy(), reduction=reduction)
+    if reduction == "none":
+        lg = loss.cpu().double().numpy()
+        ok = ~np.isnan(lg)
+        assert not ok.all(), "no row carries the failure"
+        assert_loss_close(lg[ok], np.asarray(ref.loss)[ok], "per-row loss (rows not poisoned)")
+    else:
+        assert math.isnan(loss.item()) and math.isnan(acc.item())
+    am = arg.cpu().numpy()
+    assert np.all((am == -1) | (am == ref.argmax))
+    g = x_cpu_grad = xd.detach().float().cpu().double().numpy()
+    nan = np.isnan(g)
+    assert nan.any() and not nan[ref.not_counted].any()
+    # every value that is not NaN is the oracle's
+    filled = torch.from_numpy(np.where(nan, ref.grad, g)).to(dtype)
+    assert_grad_close(filled, ref.grad, ref.mag, zero_rows=ref.not_counted,
+                      what="gradient outside the poisoned parts")
+    del x_cpu_grad
+    # the next call on the same workspace, without the hook, is clean
+    xd2 = _padded(x, stride)
+    flags2 = flags & ~CE_F_EXCHANGE_ONE_POLL
+    st = _lib.ce_forward(xd2.data_ptr(), dt, rows, V, stride, td.data_ptr(), 0, -100, 0.0, 0.0,
+                         0.0, _lib.REDUCTION_CODES[reduction], flags2, loss.data_ptr(), 0,
+                         acc.data_ptr(), arg.data_ptr(), counts.data_ptr(), 0, ws.data_ptr(),
+                         wsb, s)
+    torch.cuda.synchronize()
+    assert st == _lib.CE_OK, _lib.ce_status_string(st)
+    assert_loss_close(loss.cpu().numpy(), ref.loss, "loss after a clean call")
+    np.testing.assert_array_equal(arg.cpu().numpy(), ref.argmax)
+    assert_grad_close(xd2, ref.grad, ref.mag, zero_rows=ref.not_counted)
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads in the benchmark's launch configuration, against the
+# oracle on every row: loss, z-loss, token accuracy, argmax and counts of
+# the whole batch, and every row's gradient (a seeded sample of rows at
+# 16384 x 262144, where the float64 gradient of every row would take the
+# host minutes).
 # ---------------------------------------------------------------------------
 
 def _sample_rows(rows, k, seed, extra=()):
@@ -484,59 +648,46 @@ def _sample_rows(rows, k, seed, extra=()):
     return np.array(sorted(s))
 
 
-def _full_workload(name, reductions=None, k=48):
+def _full_workload(name, grad_sample=None):
     w = synth.WORKLOADS[name]
-    for red in reductions or w.reductions:
+    for red in w.reductions:
         _announce(name=w.name, rows=w.rows, V=w.V, dtype=w.dtype, reduction=red)
         inp = synth.make_inputs(w, DEV)
-        t_host = inp.target.cpu().numpy()
-        ign = np.nonzero(t_host == -100)[0][:4]
-        sel = _sample_rows(w.rows, k, w.seed, list(inp.spike_rows) + list(ign))
-        xh = host_logits(inp.logits[torch.from_numpy(sel).to(DEV)])
-        wh = None if inp.weight is None else inp.weight.cpu().numpy()
         x = inp.logits
+        xh = host_logits(x)  # every row, before the forward overwrites them
+        t_host = inp.target.cpu().numpy()
+        wh = None if inp.weight is None else inp.weight.cpu().numpy()
+        opts = dict(weight=wh, label_smoothing=w.label_smoothing,
+                    lse_square_scale=w.lse_square_scale, softcap=w.softcap or None)
         loss, z, acc, arg, counts = forward_raw(
             x, inp.target, inp.weight, -100, w.label_smoothing, w.lse_square_scale,
             w.softcap or None, red, grad=True, z_loss=True, token_accuracy=True, argmax=True,
             counts=True)
         torch.cuda.synchronize()
-        # sampled rows: per-row values (from a "none" run when reducing) and gradients
-        summ = summarize_targets(t_host, w.V, -100, wh, red)
-        rr = rows_forward(xh, t_host[sel], V=w.V, alpha=summ.alpha, beta=summ.beta, weight=wh,
-                          label_smoothing=w.label_smoothing, lse_square_scale=w.lse_square_scale,
-                          softcap=w.softcap or None, want_grad=True, want_mag=True)
-        assert_grad_close(x[torch.from_numpy(sel).to(DEV)], rr.grad, rr.mag,
-                          zero_rows=~summ.counted[sel], what=f"{w.name} grad")
-        np.testing.assert_array_equal(arg.cpu().numpy()[sel], rr.argmax)
+        print(f"  gpu done; oracle over {w.rows} rows", flush=True)
+        o, summ = oracle_rows(xh, t_host, reduction=red, **opts)
+        want_loss, want_z, want_acc, n_correct = reduce_rows(
+            o["ce"], o["zeta"], o["correct"], summ.counted, summ.n, summ.D, red)
+        np.testing.assert_array_equal(arg.cpu().numpy(), o["argmax"])
         c = counts.cpu().numpy()
-        am = arg.cpu().numpy()
-        n_correct = int(np.sum((am == t_host) & summ.counted))
         assert int(c[0]) == summ.n and int(c[1]) == n_correct
         if red == "none":
-            assert_loss_close(loss.cpu().numpy()[sel], rr.ce + rr.zeta, "per-row loss")
-            assert_loss_close(z.cpu().numpy()[sel], rr.zeta, "per-row z_loss")
-            per_row_ce = loss.double().cpu().numpy() - z.double().cpu().numpy()
-            per_row_z = z.double().cpu().numpy()
+            assert_loss_close(loss.cpu().numpy(), want_loss, "per-row loss")
+            assert_loss_close(z.cpu().numpy(), want_z, "per-row z_loss")
+            np.testing.assert_array_equal(acc.cpu().numpy(), want_acc.astype(np.float32))
         else:
+            assert_loss_close(np.array(loss.item()), np.array(want_loss), "loss")
+            assert_loss_close(np.array(z.item()), np.array(want_z), "z_loss")
             assert_acc_exact(acc.item(), n_correct, summ.n)
-            # per-row values of the same batch from a "none" run
-            inp2 = synth.make_inputs(w, DEV)
-            l2, z2, _, _, _ = forward_raw(inp2.logits, inp2.target, inp2.weight, -100,
-                                          w.label_smoothing, w.lse_square_scale,
-                                          w.softcap or None, "none", grad=False, z_loss=True)
-            del inp2
-            assert_loss_close(l2.cpu().numpy()[sel], rr.ce + rr.zeta, "per-row loss")
-            assert_loss_close(z2.cpu().numpy()[sel], rr.zeta, "per-row z_loss")
-            per_row_z = z2.double().cpu().numpy()
-            per_row_ce = l2.double().cpu().numpy() - per_row_z
-            with np.errstate(divide="ignore", invalid="ignore"):
-                if red == "mean":
-                    want = per_row_ce.sum() / summ.D + per_row_z.sum() / summ.n
-                else:
-                    want = per_row_ce.sum() + per_row_z.sum()
-            # the reduction of the per-row values (each within the parity bar)
-            assert abs(loss.item() - want) <= 2e-6 * abs(want), (loss.item(), want)
-        del inp, x
+        sel = (np.arange(w.rows) if grad_sample is None else
+               _sample_rows(w.rows, grad_sample, w.seed, inp.spike_rows))
+        print(f"  scalars and argmax match; gradients of {sel.size} rows", flush=True)
+        for a in range(0, sel.size, 512):
+            rr = sel[a:a + 512]
+            og, _ = oracle_rows(xh, t_host, reduction=red, want_grad=True, rows=rr, **opts)
+            assert_grad_close(x[torch.from_numpy(rr).to(DEV)], og["grad"], og["mag"],
+                              zero_rows=~summ.counted[rr], what=f"{w.name} grad rows {rr[0]}..")
+        del inp, x, xh
 
 
 def test_full_c2_bf16_accuracy_argmax():
@@ -548,8 +699,8 @@ def test_full_c3_f32_large_vocab():
 
 
 def test_full_c4_bf16_all_options():
-    _full_workload("ce_4096x131072_bf16_opts", k=24)
+    _full_workload("ce_4096x131072_bf16_opts")
 
 
 def test_full_c5_bf16_huge():
-    _full_workload("ce_16384x262144_bf16", k=16)
+    _full_workload("ce_16384x262144_bf16", grad_sample=512)
