@@ -1,6 +1,7 @@
 """Benchmark of the fused softmax cross-entropy forward + gradient on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--mode MODE]
+    python bench.py --configs-only          # one JSON line per configuration
 
 A step is one pass of the whole hot path over one batch of synthetic logits
 already resident in HBM: ce_forward (loss + gradient written over the
@@ -12,10 +13,16 @@ before the timed region), so no step reads a gradient left by another.
 them (ce_backward_recompute) after that forward.
 
 The default workload is 1023 rows x V = 128256 fp32 logits, reduction
-"sum" (the tt-mlir PR #9324 page's before/after shape). Prints one JSON
-line with rows/s, the roofline of the fused kernel (achieved HBM GB/s from
-algorithmic bytes over its event-timed duration) and the float64 oracle
-timed on the host cores as a CPU baseline.
+"sum" (the tt-mlir PR #9324 page's before/after shape). The one JSON line
+printed holds rows/s over the K timed steps, the roofline of the forward
+call (algorithmic bytes over its HIP-event-timed duration on the launch
+stream) against 8 TB/s and against the in-place HBM ceiling that the
+stream kernels (include/ce_stream.h) measure over the same bytes in the
+same run, and the float64 oracle timed on the host cores. Unless
+--no-configs, it also holds every configuration's cold timings (batch
+restored and 1 GiB flushed through the caches before each launch):
+median / min / p90 of the forward, the backward at grad_output 1 and 0.5,
+and each one's fraction of 8 TB/s and of its measured ceiling.
 """
 
 from __future__ import annotations
@@ -24,7 +31,6 @@ import argparse
 import hashlib
 import json
 import os
-import resource
 import sys
 import time
 
@@ -246,34 +252,269 @@ def linear_bench(steps: int, warmup: int, rows: int = 4096, H: int = 4096, V: in
                      "frac": tf / 2500.0, "flops_per_step": flops}}), flush=True)
 
 
-def cpu_baseline(x_host, t_host, weight_host, w, reduction, budget_s=12.0):
-    """Time the float64 oracle, as it is, on a bounded sample of the rows."""
-    import numpy as np
-    from oracle import ce_forward as oracle_forward
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
+
+def cpu_baseline(x_host, t_host, weight_host, w, reduction, budget_s=12.0):
+    """Time the float64 oracle, as it is, on a bounded sample of the batch's
+    rows: once in this process alone, once over threads that each run it on
+    64-row chunks (numpy's array loops release the GIL), one thread per host
+    core this process may use (at most 16). The threaded rate is the
+    baseline; `cores` is the number of threads it used."""
+    import concurrent.futures as cf
+    import numpy as np
+    from oracle import rows_forward, summarize_targets
+
+    summ = summarize_targets(t_host, w.V, -100, weight_host, reduction)
     rows_per_call = 64
-    done_rows = 0
-    t0 = time.perf_counter()
-    c0 = resource.getrusage(resource.RUSAGE_SELF)
-    calls = 0
-    while True:
-        a = (calls * rows_per_call) % max(1, x_host.shape[0] - rows_per_call)
-        oracle_forward(x_host[a:a + rows_per_call], t_host[a:a + rows_per_call],
-                       weight=weight_host, label_smoothing=w.label_smoothing,
-                       lse_square_scale=w.lse_square_scale, softcap=w.softcap or None,
-                       reduction=reduction)
-        calls += 1
-        done_rows += rows_per_call
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    wall = time.perf_counter() - t0
-    c1 = resource.getrusage(resource.RUSAGE_SELF)
-    cpu = (c1.ru_utime - c0.ru_utime) + (c1.ru_stime - c0.ru_stime)
-    cores = max(1, int(round(cpu / wall)))
-    del np
-    return {"value": done_rows / wall, "unit": "rows/s", "cores": cores, "kind": "oracle",
-            "sample": f"{calls} oracle calls of {rows_per_call} rows of the {w.name} batch "
-                      f"({done_rows} rows, {wall:.1f} s wall, {cpu:.1f} s CPU)"}
+    n = x_host.shape[0]
+
+    def call(a):
+        b = min(n, a + rows_per_call)
+        rows_forward(x_host[a:b], t_host[a:b], V=w.V, alpha=summ.alpha, beta=summ.beta,
+                     weight=weight_host, label_smoothing=w.label_smoothing,
+                     lse_square_scale=w.lse_square_scale, softcap=w.softcap or None,
+                     want_grad=True)
+        return b - a
+
+    def run(workers, budget):
+        done = 0
+        t0 = time.perf_counter()
+        with cf.ThreadPoolExecutor(workers) as ex:
+            while time.perf_counter() - t0 < budget:
+                done += sum(ex.map(call, range(0, n, rows_per_call)))
+        return done / (time.perf_counter() - t0), done
+
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    single, n1 = run(1, budget_s / 2)
+    threaded, nt = run(cores, budget_s / 2)
+    digest = hashlib.sha256(np.ascontiguousarray(x_host).tobytes() +
+                            np.ascontiguousarray(t_host).tobytes()).hexdigest()[:16]
+    return {"value": threaded, "unit": "rows/s", "cores": cores, "kind": "oracle",
+            "sample": f"the first {n} rows of the {w.name} batch (inputs sha256 {digest}), "
+                      f"loss and gradient in float64, over {cores} threads of 64-row calls "
+                      f"for {budget_s / 2:.0f} s ({nt} rows); one thread alone: "
+                      f"{single:.1f} rows/s ({n1} rows)",
+            "single_thread_value": single,
+            "host_cpu": _cpu_model(), "host_cores_available": len(os.sched_getaffinity(0))}
+
+
+# ---------------------------------------------------------------------------
+# Per-config measurement on cold buffers: before each timed launch the batch
+# is restored from a pristine device copy and 1 GiB is read through the
+# caches (the flush stream kernel), so the launch reads its logits from HBM.
+# ---------------------------------------------------------------------------
+
+CONFIGS = (  # (label, workload, reduction)
+    ("C1", "ce_64x4096_f32", "mean"),
+    ("C2", "ce_4096x32768_bf16", "mean"),
+    ("C3", "ce_1023x128256_f32", "sum"),
+    ("C3none", "ce_1023x128256_f32", "none"),
+    ("C4", "ce_4096x131072_bf16_opts", "mean"),
+    ("C5", "ce_16384x262144_bf16", "mean"),
+    ("C5b", "ce_512x262144_bf16_allignored", "mean"),
+)
+
+
+class Case:
+    """One workload's inputs resident on the GPU and the raw forward/backward calls."""
+
+    def __init__(self, w, red, flags_extra=0, mode="fused", dev=None):
+        import torch
+        from softmax_cross_entropy_amd import _lib
+        from softmax_cross_entropy_amd.functional import _workspace
+        self.w, self.red, self.mode = w, red, mode
+        self.dev = dev
+        self.stream = torch.cuda.current_stream(dev)
+        self.inp = synth_inputs(w, dev)
+        t_host = self.inp.target.cpu().numpy()
+        self.n_counted = int(((t_host != -100) & (t_host >= 0) & (t_host < w.V)).sum())
+        self.dt = _lib.dtype_code(w.dtype)
+        self.flags = (_lib.CE_F_GRAD if mode == "fused" else 0) | flags_extra
+        rows, V = w.rows, w.V
+        f32 = dict(device=dev, dtype=torch.float32)
+        self.loss = torch.empty((rows,) if red == "none" else (), **f32)
+        self.z_loss = torch.empty_like(self.loss) if w.want_z_loss else None
+        self.acc = torch.empty_like(self.loss) if w.want_accuracy else None
+        self.arg = torch.empty((rows,), device=dev, dtype=torch.int64) if w.want_argmax else None
+        self.stats = torch.empty((rows, 2), **f32) if mode == "recompute" else None
+        self.ws_bytes = _lib.ce_workspace_bytes(rows, V, self.dt, self.flags)
+        self.ws = _workspace(dev, self.ws_bytes)
+        self.red_code = _lib.REDUCTION_CODES[red]
+        P = self.P
+        x = self.inp.logits
+        self.path = _lib.PATH_NAMES[_lib.ce_plan_path(P(x), self.dt, rows, V, x.stride(0),
+                                                      P(self.inp.weight), w.label_smoothing,
+                                                      self.flags)]
+
+    @staticmethod
+    def P(t):
+        return 0 if t is None else t.data_ptr()
+
+    def fwd(self, buf):
+        from softmax_cross_entropy_amd import _lib
+        w, P = self.w, self.P
+        st = _lib.ce_forward(P(buf), self.dt, w.rows, w.V, buf.stride(0), P(self.inp.target),
+                             P(self.inp.weight), -100, w.label_smoothing, w.lse_square_scale,
+                             w.softcap, self.red_code, self.flags, P(self.loss), P(self.z_loss),
+                             P(self.acc), P(self.arg), 0, P(self.stats), P(self.ws),
+                             self.ws_bytes, self.stream.cuda_stream)
+        if st:
+            raise _lib.CEError(st, "ce_forward")
+
+    def bwd(self, buf, go, out=None):
+        from softmax_cross_entropy_amd import _lib
+        w, P = self.w, self.P
+        if self.mode == "recompute":
+            st = _lib.ce_backward_recompute(P(buf), self.dt, w.rows, w.V, buf.stride(0),
+                                            P(self.inp.target), P(self.inp.weight), -100,
+                                            w.label_smoothing, w.lse_square_scale, w.softcap,
+                                            self.red_code, P(self.stats), P(go), 0, P(out),
+                                            out.stride(0), P(self.ws), self.ws_bytes,
+                                            self.stream.cuda_stream)
+        else:
+            st = _lib.ce_backward(P(buf), self.dt, w.rows, w.V, buf.stride(0), P(go), 0,
+                                  self.stream.cuda_stream)
+        if st:
+            raise _lib.CEError(st, "backward")
+
+
+def synth_inputs(w, dev):
+    import synth
+    return synth.make_inputs(w, dev)
+
+
+class Flusher:
+    """Reads 1 GiB through the caches (the stream kernels' flush), so the next
+    launch finds none of its data in L2 or the Infinity Cache."""
+
+    def __init__(self, dev):
+        import torch
+        self.buf = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
+        self.sink = torch.zeros(4, dtype=torch.int32, device=dev)
+
+    def __call__(self, stream):
+        from softmax_cross_entropy_amd import _lib
+        _lib.check(_lib.ce_stream_run(_lib.CE_STREAM_FLUSH, 4, 0, self.buf.data_ptr(),
+                                      self.buf.numel() * 4, 0, self.sink.data_ptr(),
+                                      stream.cuda_stream), "flush")
+
+
+def _stats(us):
+    import numpy as np
+    a = np.asarray(us, dtype=np.float64)
+    return {"median": float(np.median(a)), "min": float(a.min()),
+            "p90": float(np.percentile(a, 90)), "n": int(a.size)}
+
+
+def ceilings(nbytes, dev, flush, reps=5):
+    """HBM ceilings over `nbytes` measured with the stream kernels (each launch
+    cold, after the flush): in-place read-then-write, copy, read, write; the
+    best over a few chunk shapes and grids. GB/s of the best launch, and of
+    the median launch of that shape."""
+    import torch
+    from softmax_cross_entropy_amd import _lib
+    stream = torch.cuda.current_stream(dev)
+    nbytes = nbytes // 16 * 16
+    a = torch.zeros(nbytes // 4, dtype=torch.float32, device=dev)
+    b = torch.zeros_like(a)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    out = {}
+    for kind, name, moved in ((_lib.CE_STREAM_INPLACE, "inplace", 2), (_lib.CE_STREAM_COPY, "copy", 2),
+                              (_lib.CE_STREAM_READ, "read", 1), (_lib.CE_STREAM_WRITE, "write", 1)):
+        best = None
+        for cfg in (2, 5, 7):  # 256 x 16, 512 x 16, 1024 x 8 vectors per chunk
+            res = _lib.ce_stream_resident(kind, cfg)
+            for grid in (0, res):
+                ts = []
+                for _ in range(reps):
+                    flush(stream)
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    dst = a.data_ptr() if kind in (_lib.CE_STREAM_INPLACE, _lib.CE_STREAM_WRITE) else (
+                        b.data_ptr() if kind == _lib.CE_STREAM_COPY else 0)
+                    src = a.data_ptr() if kind in (_lib.CE_STREAM_COPY, _lib.CE_STREAM_READ) else 0
+                    _lib.check(_lib.ce_stream_run(kind, cfg, dst, src, nbytes, grid,
+                                                  sink.data_ptr(), stream.cuda_stream), name)
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    ts.append(e0.elapsed_time(e1) * 1e3)
+                st = _stats(ts)
+                if best is None or st["min"] < best["min"]:
+                    blk, nreg = _lib.ce_stream_config(cfg)
+                    best = dict(st, shape=f"{blk}x{nreg}", grid="one per chunk" if grid == 0 else grid)
+        best["GBps"] = moved * nbytes / (best["min"] * 1e-6) / 1e9
+        best["GBps_median"] = moved * nbytes / (best["median"] * 1e-6) / 1e9
+        out[name] = best
+    del a, b
+    return out
+
+
+def measure_config(label, wname, red, dev, flush, reps, ceil_reps=5):
+    """Cold per-launch timings of one workload: the forward (+ gradient) call,
+    the backward at grad_output 1 (exits at once) and 0.5 (a pass over the
+    gradient), with the roofline of the forward against 8 TB/s and against the
+    in-place ceiling measured over the same bytes in the same run."""
+    import torch
+    import synth
+    w = synth.WORKLOADS[wname]
+    c = Case(w, red, dev=dev)
+    stream = c.stream
+    pristine = c.inp.logits
+    buf = torch.empty_like(pristine)
+    go1 = torch.ones((), device=dev, dtype=torch.float32)
+    go05 = torch.full((), 0.5, device=dev, dtype=torch.float32)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    fwd_us, b1_us, b05_us = [], [], []
+    for i in range(reps + 1):  # the first round warms up
+        for go, sink in ((go1, b1_us), (go05, b05_us)):
+            buf.copy_(pristine)
+            flush(stream)
+            e = [ev() for _ in range(4)]
+            e[0].record(stream)
+            c.fwd(buf)
+            e[1].record(stream)
+            flush(stream)
+            e[2].record(stream)
+            c.bwd(buf, go)
+            e[3].record(stream)
+            torch.cuda.synchronize()
+            if i > 0:
+                if go is go1:
+                    fwd_us.append(e[0].elapsed_time(e[1]) * 1e3)
+                sink.append(e[2].elapsed_time(e[3]) * 1e3)
+    alg = algorithmic_bytes(w, red, c.n_counted)
+    f = _stats(fwd_us)
+    nbytes = w.rows * w.V * w.elem_bytes
+    ceil = ceilings(nbytes, dev, flush, ceil_reps)
+    bound = "write" if c.n_counted == 0 else "inplace"
+    ce = ceil[bound]
+    achieved = alg / (f["median"] * 1e-6) / 1e9
+    rec = {
+        "workload": w.name, "reduction": red, "path": c.path, "rows": w.rows, "V": w.V,
+        "dtype": "f32" if w.elem_bytes == 4 else "bf16",
+        "forward_us": f, "backward_go1_us": _stats(b1_us), "backward_go05_us": _stats(b05_us),
+        "rows_per_s": w.rows / (f["median"] * 1e-6),
+        "algorithmic_bytes": alg,
+        "roofline": {"bound": "hbm", "achieved_GBps": achieved, "peak_GBps": HBM_PEAK_GBPS,
+                     "frac": achieved / HBM_PEAK_GBPS,
+                     "ceiling": bound, "ceiling_GBps": ce["GBps_median"],
+                     "frac_of_ceiling": achieved / ce["GBps_median"],
+                     "best_launch_frac": alg / (f["min"] * 1e-6) / 1e9 / HBM_PEAK_GBPS},
+        "ceilings": {k: {"GBps": v["GBps"], "GBps_median": v["GBps_median"], "shape": v["shape"],
+                         "grid": v["grid"]} for k, v in ceil.items()},
+    }
+    del c, buf, pristine
+    torch.cuda.empty_cache()
+    return label, rec
 
 
 def main(argv=None) -> int:
@@ -285,6 +526,12 @@ def main(argv=None) -> int:
     ap.add_argument("--reduction", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the cold per-config measurements (faster; for profiling runs)")
+    ap.add_argument("--config-reps", type=int, default=10,
+                    help="cold launches per config and per backward variant")
+    ap.add_argument("--configs-only", action="store_true",
+                    help="print one JSON line per config (C1..C5b) and exit")
     ap.add_argument("--mode", choices=("fused", "nograd", "recompute"), default="fused",
                     help="fused: forward + gradient in place, then the scaling backward "
                          "(default); nograd: forward without the gradient (logits only "
@@ -312,6 +559,12 @@ def main(argv=None) -> int:
         write_traffic(a.workload, *a.traffic)
         return 0
 
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported: this build runs "
+              "on one GPU only (the path shards by rows, with no communication between GPUs "
+              "on the hot path).", file=sys.stderr)
+        return 2
+
     if a.linear:
         linear_bench(a.steps, a.warmup, chunk_rows=a.chunk_rows)
         return 0
@@ -321,83 +574,50 @@ def main(argv=None) -> int:
         sweep(a.steps, a.warmup, _lib.CE_F_SHAPE_ALT if a.alt_shape else 0)
         return 0
 
-    if a.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported (the path shards "
-              "by rows, with no communication between GPUs on the hot path).", file=sys.stderr)
-        return 2
-
     import torch
     import synth
     from softmax_cross_entropy_amd import _lib
-    from softmax_cross_entropy_amd.functional import _workspace
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    flush = Flusher(dev)
+
+    if a.configs_only:
+        for label, wname, red in CONFIGS:
+            lab, rec = measure_config(label, wname, red, dev, flush, a.config_reps)
+            print(json.dumps(dict(config=lab, **rec)), flush=True)
+        return 0
 
     w = synth.WORKLOADS[a.workload]
     red = a.reduction or DEFAULT_REDUCTION.get(w.name, w.reductions[0])
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    stream = torch.cuda.current_stream(dev)
-
-    inp = synth.make_inputs(w, dev)
-    t_host = inp.target.cpu().numpy()
-    n_counted = int(((t_host != -100) & (t_host >= 0) & (t_host < w.V)).sum())
-    nbuf = a.warmup + a.steps
-    bufs = [inp.logits.clone() for _ in range(nbuf)]
-    sample_host = None
-    if not a.no_cpu_baseline:
-        x = inp.logits[:256].detach().cpu()
-        sample_host = (x.view(torch.int16).numpy().view("uint16") if x.dtype == torch.bfloat16
-                       else x.numpy(), t_host[:256])
-    dt = _lib.dtype_code(w.dtype)
-    flags = _lib.CE_F_GRAD if a.mode == "fused" else 0
-    flags |= {"auto": 0, "fused": _lib.CE_F_FORCE_FUSED, "splitv": _lib.CE_F_FORCE_SPLITV,
-              "scalar": _lib.CE_F_FORCE_SCALAR}[a.path]
+    flags = {"auto": 0, "fused": _lib.CE_F_FORCE_FUSED, "splitv": _lib.CE_F_FORCE_SPLITV,
+             "scalar": _lib.CE_F_FORCE_SCALAR}[a.path]
     if a.alt_shape:
         flags |= _lib.CE_F_SHAPE_ALT
+    c = Case(w, red, flags, a.mode, dev)
+    stream = c.stream
     rows, V = w.rows, w.V
-    f32 = dict(device=dev, dtype=torch.float32)
-    loss = torch.empty((rows,) if red == "none" else (), **f32)
-    z_loss = torch.empty_like(loss) if w.want_z_loss else None
-    acc = torch.empty_like(loss) if w.want_accuracy else None
-    arg = torch.empty((rows,), device=dev, dtype=torch.int64) if w.want_argmax else None
-    go = torch.ones((), **f32)
-    stats = torch.empty((rows, 2), **f32) if a.mode == "recompute" else None
-    gbuf = torch.empty_like(inp.logits) if a.mode == "recompute" else None
-    ws_bytes = _lib.ce_workspace_bytes(rows, V, dt, flags)
-    ws = _workspace(dev, ws_bytes)
-    P = lambda t: 0 if t is None else t.data_ptr()  # noqa: E731
-    tgt, wt = P(inp.target), P(inp.weight)
-    s = stream.cuda_stream
-    path = _lib.PATH_NAMES[_lib.ce_plan_path(P(bufs[0]), dt, rows, V, bufs[0].stride(0), wt,
-                                             w.label_smoothing, flags)]
-    red_code = _lib.REDUCTION_CODES[red]
+    sample_host = None
+    if not a.no_cpu_baseline and a.mode == "fused":
+        x = c.inp.logits[:256].detach().cpu()
+        sample_host = (x.view(torch.int16).numpy().view("uint16") if x.dtype == torch.bfloat16
+                       else x.numpy(), c.inp.target[:256].cpu().numpy())
+    # every step on its own pristine copy of the batch, made before the timed region
+    nbuf = a.warmup + a.steps
+    bufs = [c.inp.logits.clone() for _ in range(nbuf)]
+    go = torch.ones((), device=dev, dtype=torch.float32)
+    gbuf = torch.empty_like(c.inp.logits) if a.mode == "recompute" else None
 
-    def fwd(buf):
-        st = _lib.ce_forward(P(buf), dt, rows, V, buf.stride(0), tgt, wt, -100,
-                             w.label_smoothing, w.lse_square_scale, w.softcap, red_code, flags,
-                             P(loss), P(z_loss), P(acc), P(arg), 0, P(stats), P(ws), ws_bytes, s)
-        if st:
-            raise _lib.CEError(st, "ce_forward")
+    def step(b):
+        c.fwd(b)
+        if a.mode != "nograd":
+            c.bwd(b, go, gbuf)
 
-    def bwd(buf):
-        if a.mode == "fused":
-            st = _lib.ce_backward(P(buf), dt, rows, V, buf.stride(0), P(go), 0, s)
-        elif a.mode == "recompute":
-            st = _lib.ce_backward_recompute(P(buf), dt, rows, V, buf.stride(0), tgt, wt, -100,
-                                            w.label_smoothing, w.lse_square_scale, w.softcap,
-                                            red_code, P(stats), P(go), 0, P(gbuf),
-                                            gbuf.stride(0), P(ws), ws_bytes, s)
-        else:
-            st = 0
-        if st:
-            raise _lib.CEError(st, "backward")
-
-    # The timed kernel: the fused forward, or the recomputing backward.
+    # The timed kernel: the forward call, or the recomputing backward.
     timed_first = a.mode != "recompute"
     for i in range(a.warmup):
-        fwd(bufs[i])
-        bwd(bufs[i])
+        step(bufs[i])
     torch.cuda.synchronize()
-
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(a.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -407,40 +627,30 @@ def main(argv=None) -> int:
         b = bufs[a.warmup + i]
         if timed_first:
             ev[i][0].record(stream)
-            fwd(b)
+            c.fwd(b)
             ev[i][1].record(stream)
-            bwd(b)
+            if a.mode != "nograd":
+                c.bwd(b, go, gbuf)
         else:
-            fwd(b)
+            c.fwd(b)
             ev[i][0].record(stream)
-            bwd(b)
+            c.bwd(b, go, gbuf)
             ev[i][1].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
-    fwd_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
-    kernel_ms = sum(fwd_ms) / len(fwd_ms)
+    kern_us = [e0.elapsed_time(e1) * 1e3 for e0, e1 in ev]
+    kernel_ms = sum(kern_us) / len(kern_us) / 1e3
     ms_per_step = total_ms / a.steps
     del bufs
 
-    # copy ceiling of the same size (read + write), for context
-    src = inp.logits
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record(stream)
-    for _ in range(10):
-        dst.copy_(src)
-    c1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbps = 2 * src.numel() * src.element_size() * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
-    del dst
-
-    alg = algorithmic_bytes(w, red, n_counted, a.mode)
+    alg = algorithmic_bytes(w, red, c.n_counted, a.mode)
     achieved = alg / (kernel_ms * 1e-3) / 1e9
-    kernel_key = "ce_fused" if path == "fused" else f"ce_{path}"
+    kernel_key = "ce_fused" if c.path == "fused" else f"ce_{c.path}"
     traffic = traffic_from_profiles(w.name, kernel_key) if a.mode == "fused" else None
+    nbytes = rows * V * w.elem_bytes
+    ceil = ceilings(nbytes, dev, flush)
+    ce = ceil["inplace"]
     out = {
         "metric": "fused CE fwd+grad rows/s and achieved HBM GB/s (% of peak), V=128256",
         "value": rows * a.steps / (total_ms * 1e-3),
@@ -455,18 +665,37 @@ def main(argv=None) -> int:
         "dtype": "f32" if w.dtype == torch.float32 else "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "mode": a.mode, "rows": rows, "V": V,
-                   "reduction": red, "path": path,
+                   "reduction": red, "path": c.path,
                    "layout": "alternative" if a.alt_shape else "default",
                    "label_smoothing": w.label_smoothing, "softcap": w.softcap,
                    "lse_square_scale": w.lse_square_scale, "class_weights": w.weights,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "kernel_ms": kernel_ms, "algorithmic_bytes": alg},
-        "copy_ceiling_GBps": copy_gbps,
+                     "kernel_ms": kernel_ms, "kernel_us_stats": _stats(kern_us),
+                     "algorithmic_bytes": alg,
+                     "ceiling_inplace_GBps": ce["GBps_median"],
+                     "frac_of_ceiling": achieved / ce["GBps_median"]},
+        "ceilings_GBps": {k: {"best": v["GBps"], "median": v["GBps_median"], "shape": v["shape"]}
+                          for k, v in ceil.items()},
     }
-    if sample_host is not None and a.mode == "fused":
-        wh = None if inp.weight is None else inp.weight.cpu().numpy()
+    if not a.no_configs and a.mode == "fused":
+        out["configs"] = {}
+        for label, wname, cred in CONFIGS:
+            lab, rec = measure_config(label, wname, cred, dev, flush, a.config_reps, ceil_reps=3)
+            out["configs"][lab] = {
+                "workload": rec["workload"], "reduction": rec["reduction"], "path": rec["path"],
+                "forward_us": {k: round(v, 2) for k, v in rec["forward_us"].items()},
+                "backward_go1_us_median": round(rec["backward_go1_us"]["median"], 2),
+                "backward_go05_us_median": round(rec["backward_go05_us"]["median"], 2),
+                "rows_per_s": rec["rows_per_s"],
+                "GBps": round(rec["roofline"]["achieved_GBps"], 1),
+                "frac_of_8TBps": round(rec["roofline"]["frac"], 4),
+                "ceiling": rec["roofline"]["ceiling"],
+                "ceiling_GBps": round(rec["roofline"]["ceiling_GBps"], 1),
+                "frac_of_ceiling": round(rec["roofline"]["frac_of_ceiling"], 4)}
+    if sample_host is not None:
+        wh = None if c.inp.weight is None else c.inp.weight.cpu().numpy()
         out["cpu_baseline"] = cpu_baseline(sample_host[0], sample_host[1], wh, w, red,
                                            a.cpu_budget)
     print(json.dumps(out), flush=True)
