@@ -315,6 +315,8 @@ struct RowScalars {
   float A;      // coefficient of p_k
   float B;      // constant term (times w_k when weighted smoothing)
   float C;      // extra term subtracted at the target class
+  float cA;     // log2 A - m log2 e - log2 s when A > 0, else NaN: A p_k as the single
+                // exponential 2^(z_k log2 e + cA) (bf16 gradients without smoothing)
   float ce;     // cross-entropy + smoothing loss of the row
   float zl;     // z-loss of the row
   int arg;      // argmax element index
@@ -343,9 +345,16 @@ __device__ __forceinline__ double grad_scalars(RowScalars& r, float m, float l2s
   const double ome = p.one_minus_eps, epv = p.eps_over_v, lam = p.lam_d;
   r.m = m;
   r.l2s = l2s;
-  r.A = static_cast<float>(alpha * (wyd * ome + epv * W) + beta * 2.0 * lam * lse);
+  const double A = alpha * (wyd * ome + epv * W) + beta * 2.0 * lam * lse;
+  r.A = static_cast<float>(A);
   r.B = static_cast<float>(alpha * epv);
   r.C = static_cast<float>(alpha * wyd * ome);
+  // (the hardware log2: a double-precision one is a library call, which this
+  // code keeps out of the kernels)
+  r.cA = A > 0.0 ? static_cast<float>(static_cast<double>(lg2(static_cast<float>(A))) -
+                                      static_cast<double>(m) * 1.4426950408889634 -
+                                      static_cast<double>(l2s))
+                 : __builtin_nanf("");
   return lse;
 }
 

@@ -180,7 +180,9 @@ __device__ __forceinline__ float grad_one(const Params& p, const RowScalars& rs,
   return grad_elem<SC, SM>(p, rs, x, t, wk, is_y);
 }
 
-template <class E, int SC, int SM>
+// FOLD (bf16 results without smoothing, where it is taken): A p_k as one
+// exponential when A > 0.
+template <class E, int SC, int SM, bool FOLD = false>
 __device__ __forceinline__ u4 grad_vec(const Params& p, const RowScalars& rs, const u4 v,
                                        int64_t jg, int yi) {
   constexpr int EPV = E::EPV;
@@ -208,6 +210,22 @@ __device__ __forceinline__ u4 grad_vec(const Params& p, const RowScalars& rs, co
     for (int i = 0; i < EPV; ++i) t[i] = 0.0f;
   }
   float g[EPV];
+  if constexpr (FOLD && E::EPV == 8 && !SM) {
+    // bf16 result without smoothing: A p_k as one exponential, 2^(z log2 e +
+    // cA), two operations fewer per element. Its relative error (about
+    // |z| 2^-23) is far below the bf16 rounding that follows; fp32 results
+    // keep the exact (z - m) form. (Taken by the row kernel: the split-row
+    // kernel measured slower with it, its registers being fuller.)
+    if (rs.cA == rs.cA && yi < 0) {  // uniform: A > 0
+#pragma unroll
+      for (int i = 0; i < EPV; ++i) {
+        const float z = SC ? p.softcap * t[i] : f[i];
+        g[i] = ex2(__builtin_fmaf(z, kLog2e, rs.cA));
+        if constexpr (SC) g[i] = g[i] * __builtin_fmaf(-t[i], t[i], 1.0f);
+      }
+      return E::pack(g);
+    }
+  }
 #pragma unroll
   for (int i = 0; i < EPV; ++i) g[i] = grad_elem<SC, SM>(p, rs, f[i], t[i], wk[i], false);
   if (yi >= 0) {
@@ -769,7 +787,7 @@ __device__ __forceinline__ void fused_row(const Params& p, int64_t row, int64_t 
             if constexpr (KEEP_E) {
               gv = grad_vec_e<SM>(p, rs, v, sc, k * BLOCK + tid, -1);
             } else {
-              gv = grad_vec<E, SC, SM>(p, rs, v, k * BLOCK + tid, -1);
+              gv = grad_vec<E, SC, SM, true>(p, rs, v, k * BLOCK + tid, -1);
             }
             // lanes past the row are outside the descriptor: the store is dropped
             __builtin_amdgcn_raw_buffer_store_b128(gv, rsrc, voff, k * BLOCK * 16, kStoreNT);
@@ -810,8 +828,11 @@ __device__ __forceinline__ int64_t uniform_i64(int64_t v) {
 // Each row's values for the epilogue are stored as the row completes; the
 // workgroup arrives once, at its end.
 constexpr int kRowsStaged = 256;
+// bf16 rows of 256 x 16 slots: three workgroups per CU (at most 168 VGPRs);
+// four (128 VGPRs) measured 2-3 % slower at 4096 x 32768 on MI355X.
 template <class E, int BLOCK, int NREG, int SC, int SM>
-__global__ __launch_bounds__(BLOCK) void rows_kernel(Params p) {
+__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(
+    1, (E::EPV == 8 && BLOCK == 256 && NREG == 16) ? 3 : 8))) void rows_kernel(Params p) {
   constexpr bool DYN = NREG >= 16;
   __shared__ RowShared<BLOCK> sh;
   __shared__ int64_t s_y[DYN ? 1 : kRowsStaged];
