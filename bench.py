@@ -252,6 +252,82 @@ def linear_bench(steps: int, warmup: int, rows: int = 4096, H: int = 4096, V: in
                      "frac": tf / 2500.0, "flops_per_step": flops}}), flush=True)
 
 
+def shard_bench(reps: int = 20, G: int = 8) -> None:
+    """One device's share of the headline batch split over G vocabulary shards
+    (1023 rows x 128256 / G columns of fp32, reduction sum): stage 1 on its
+    columns, then stage 2 with the G shards' partials (gathered beforehand,
+    as the all-gather of a multi-device run would), timed cold per call
+    pair; next to the fused kernel on the same columns. JSON line."""
+    import torch
+    import synth
+    from softmax_cross_entropy_amd import _lib
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    s = stream.cuda_stream
+    flush = Flusher(dev)
+    w = synth.WORKLOADS["ce_1023x128256_f32"]
+    inp = synth.make_inputs(w, dev)
+    rows, V = w.rows, w.V
+    Vl = V // G
+    slices = [inp.logits[:, g * Vl:(g + 1) * Vl].contiguous() for g in range(G)]
+    t = inp.target
+    parts = torch.zeros((G, rows, 32), dtype=torch.uint8, device=dev)
+    for g in range(G):
+        _lib.check(_lib.ce_shard_partials(slices[g].data_ptr(), _lib.CE_F32, rows, Vl, Vl, g * Vl,
+                                          V, t.data_ptr(), 0, -100, 0.0, 0.0,
+                                          parts[g].data_ptr(), s), "ce_shard_partials")
+    loss = torch.empty((), device=dev)
+    wsb = _lib.ce_shard_workspace_bytes(rows)
+    ws = torch.zeros((wsb,), dtype=torch.uint8, device=dev)
+    fws_b = _lib.ce_workspace_bytes(rows, Vl, _lib.CE_F32, _lib.CE_F_GRAD)
+    fws = torch.zeros((fws_b,), dtype=torch.uint8, device=dev)
+    buf = torch.empty_like(slices[0])
+
+    def sharded():
+        _lib.check(_lib.ce_shard_partials(buf.data_ptr(), _lib.CE_F32, rows, Vl, Vl, 0, V,
+                                          t.data_ptr(), 0, -100, 0.0, 0.0, parts[0].data_ptr(),
+                                          s), "ce_shard_partials")
+        _lib.check(_lib.ce_shard_finish(buf.data_ptr(), _lib.CE_F32, rows, Vl, Vl, 0, V,
+                                        t.data_ptr(), 0, -100, 0.0, 0.0, 0.0, _lib.CE_RED_SUM, 0,
+                                        parts.data_ptr(), G, loss.data_ptr(), 0, 0, 0, 0,
+                                        ws.data_ptr(), wsb, s), "ce_shard_finish")
+
+    def fused():  # the single-device kernel on the same columns (its own row of V_l classes)
+        _lib.check(_lib.ce_forward(buf.data_ptr(), _lib.CE_F32, rows, Vl, Vl, t.data_ptr(), 0,
+                                   -100, 0.0, 0.0, 0.0, _lib.CE_RED_SUM, _lib.CE_F_GRAD,
+                                   loss.data_ptr(), 0, 0, 0, 0, 0, fws.data_ptr(), fws_b, s),
+                   "ce_forward")
+
+    def stage1():
+        _lib.check(_lib.ce_shard_partials(buf.data_ptr(), _lib.CE_F32, rows, Vl, Vl, 0, V,
+                                          t.data_ptr(), 0, -100, 0.0, 0.0, parts[0].data_ptr(),
+                                          s), "ce_shard_partials")
+
+    res = {}
+    for name, fn in (("shard", sharded), ("stage1_alone", stage1), ("fused_same_columns", fused)):
+        ts = []
+        for i in range(reps + 2):
+            buf.copy_(slices[0])
+            flush(stream)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if i >= 2:
+                ts.append(e0.elapsed_time(e1) * 1e3)
+        res[name] = _stats(ts)
+    n_counted = int((t != -100).sum().item())
+    one_pass = rows * Vl * 4
+    print(json.dumps({
+        "shard": f"one of {G} vocabulary shards of the 1023 x 128256 fp32 batch (sum)",
+        "rows": rows, "V_local": Vl, "V_total": V,
+        "us": {k: {kk: round(vv, 2) for kk, vv in v.items()} for k, v in res.items()},
+        "ratio_to_fused": res["shard"]["median"] / res["fused_same_columns"]["median"],
+        "GBps_three_passes": (2 * one_pass + n_counted * Vl * 4) / (res["shard"]["median"] * 1e-6)
+                             / 1e9}), flush=True)
+
+
 def _cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -551,6 +627,9 @@ def main(argv=None) -> int:
     ap.add_argument("--sweep", action="store_true",
                     help="context sweep over V at the Liger benchmark shape, this library "
                          "against PyTorch eager F.cross_entropy (JSON line per V), then exit")
+    ap.add_argument("--shard", action="store_true",
+                    help="one of 8 vocabulary shards of the default batch: the two shard calls "
+                         "against the fused kernel on the same columns (JSON line), then exit")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the fused kernel's HBM traffic from two rocprofv3 --pmc "
                          "counter_collection.csv files of this benchmark, then exit")
@@ -572,6 +651,10 @@ def main(argv=None) -> int:
     if a.sweep:
         from softmax_cross_entropy_amd import _lib
         sweep(a.steps, a.warmup, _lib.CE_F_SHAPE_ALT if a.alt_shape else 0)
+        return 0
+
+    if a.shard:
+        shard_bench()
         return 0
 
     import torch

@@ -248,6 +248,59 @@ ce_status ce_linear_forward(const void* hidden, int64_t ld_hidden, const void* w
                             float* grad_weight, int64_t ld_grad_weight, void* workspace,
                             size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Vocabulary-parallel cross-entropy: the part one device runs when the V_total
+ * classes are split over num_shards devices, this one holding the columns
+ * [v_offset, v_offset + V) of every row. The Liger-Kernel page above, Tiling
+ * Strategy, processes a row of any length in chunks; here the chunks live on
+ * different devices (the tt-mlir PR #9324 page's commit list moves the
+ * composites towards multi-chip sharding).
+ *  1. ce_shard_partials reduces this device's columns of each row to one
+ *     32-byte partial (max, sum of exponentials, smoothing sum, largest raw
+ *     logit with its first global index, the target logit when the target is
+ *     one of these columns).
+ *  2. The caller gathers the num_shards partial arrays, in increasing
+ *     v_offset order, into partials_all (num_shards, rows) x 32 bytes (an
+ *     all-gather between devices; on one device, the arrays side by side).
+ *  3. ce_shard_finish combines each row's partials in that order (every
+ *     shard gets bitwise identical row scalars), writes the outputs of
+ *     ce_forward (each shard the same values) and overwrites this device's
+ *     columns with their gradient.
+ * Conventions of ce_forward; target and weight are global: target (rows)
+ * holds class indices in [0, V_total), weight is (V_total) or NULL (with
+ * label smoothing and weights, weight + v_offset must be 16-byte aligned
+ * for the vector path). Argmax and token accuracy are over all V_total
+ * classes, lowest global index on ties.
+ * ------------------------------------------------------------------------ */
+
+/* Workspace bytes ce_shard_finish needs (>= 256), or 0 for invalid rows. */
+size_t ce_shard_workspace_bytes(int64_t rows);
+
+/* Stage 1.
+ *  logits     [device] (rows, row_stride): this device's V columns, read only.
+ *  partials   [device] rows x 32 bytes, written.
+ * Errors: CE_E_SHAPE also when v_offset < 0 or v_offset + V > V_total. */
+ce_status ce_shard_partials(const void* logits, int dtype, int64_t rows, int64_t V,
+                            int64_t row_stride, int64_t v_offset, int64_t V_total,
+                            const int64_t* target, const float* weight, int64_t ignore_index,
+                            float label_smoothing, float softcap, void* partials, void* stream);
+
+/* Stage 3 (after the gather).
+ *  logits        [device] this device's columns, overwritten by the gradient.
+ *  partials_all  [device] (num_shards, rows) partials, shards by increasing
+ *                v_offset; this device's own are among them.
+ *  flags         CE_F_CHECK_TARGETS only.
+ *  loss, z_loss, token_accuracy, argmax, counts as for ce_forward.
+ *  workspace     >= ce_shard_workspace_bytes(rows), 256-byte aligned, zero
+ *                filled before its first use; reusable across calls. */
+ce_status ce_shard_finish(void* logits, int dtype, int64_t rows, int64_t V, int64_t row_stride,
+                          int64_t v_offset, int64_t V_total, const int64_t* target,
+                          const float* weight, int64_t ignore_index, float label_smoothing,
+                          float lse_square_scale, float softcap, int reduction, uint32_t flags,
+                          const void* partials_all, int num_shards, float* loss, float* z_loss,
+                          float* token_accuracy, int64_t* argmax, int64_t* counts,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, human-readable text of a ce_status value. */
 const char* ce_status_string(int status);
 

@@ -72,6 +72,13 @@ _SIGNATURES = {
                                          ctypes.c_float, ctypes.c_int, ctypes.c_uint32, _P,
                                          ctypes.c_int, _I64, _P, _P, _P, _P, _P, _P, _I64, _P,
                                          _I64, _P, ctypes.c_size_t, _P]),
+    "ce_shard_workspace_bytes": (ctypes.c_size_t, [_I64]),
+    "ce_shard_partials": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I64, _I64, _I64, _P, _P,
+                                         _I64, ctypes.c_float, ctypes.c_float, _P, _P]),
+    "ce_shard_finish": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I64, _I64, _I64, _P, _P,
+                                       _I64, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                       ctypes.c_int, ctypes.c_uint32, _P, ctypes.c_int, _P, _P,
+                                       _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "ce_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     # include/ce_stream.h: the measurement stream kernels
     "ce_stream_num_configs": (ctypes.c_int, []),
@@ -180,6 +187,33 @@ def ce_linear_forward(hidden: int, ld_hidden: int, weight: int, ld_weight: int, 
                                        per_row, chunk_rows, loss, z_loss, token_accuracy, argmax,
                                        counts, grad_hidden, ld_grad_hidden, grad_weight,
                                        ld_grad_weight, workspace, workspace_bytes, stream))
+
+
+def ce_shard_workspace_bytes(rows: int) -> int:
+    return int(lib().ce_shard_workspace_bytes(rows))
+
+
+def ce_shard_partials(logits: int, dtype: int, rows: int, V: int, row_stride: int, v_offset: int,
+                      V_total: int, target: int, weight: int, ignore_index: int,
+                      label_smoothing: float, softcap: float, partials: int, stream: int) -> int:
+    """Raw call; returns the ce_status (0 = CE_OK)."""
+    return int(lib().ce_shard_partials(logits, dtype, rows, V, row_stride, v_offset, V_total,
+                                       target, weight, ignore_index, label_smoothing, softcap,
+                                       partials, stream))
+
+
+def ce_shard_finish(logits: int, dtype: int, rows: int, V: int, row_stride: int, v_offset: int,
+                    V_total: int, target: int, weight: int, ignore_index: int,
+                    label_smoothing: float, lse_square_scale: float, softcap: float,
+                    reduction: int, flags: int, partials_all: int, num_shards: int, loss: int,
+                    z_loss: int, token_accuracy: int, argmax: int, counts: int, workspace: int,
+                    workspace_bytes: int, stream: int) -> int:
+    """Raw call; returns the ce_status (0 = CE_OK)."""
+    return int(lib().ce_shard_finish(logits, dtype, rows, V, row_stride, v_offset, V_total,
+                                     target, weight, ignore_index, label_smoothing,
+                                     lse_square_scale, softcap, reduction, flags, partials_all,
+                                     num_shards, loss, z_loss, token_accuracy, argmax, counts,
+                                     workspace, workspace_bytes, stream))
 
 
 CE_STREAM_READ = 0

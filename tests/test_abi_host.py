@@ -200,3 +200,27 @@ def test_python_layer_rejects_rank1_and_cpu_tensors():
     with pytest.raises((TypeError, ValueError)):
         sce.forward_raw(torch.zeros(4, 5, dtype=torch.float16).cuda() if torch.cuda.is_available()
                         else torch.zeros(4, 5, dtype=torch.float16), torch.zeros(4))
+
+
+def test_shard_argument_checks():
+    """The vocabulary-parallel entry points validate before touching memory."""
+    f = FAKE
+    assert _lib.ce_shard_partials(f, _lib.CE_F32, 4, 100, 100, 950, 1000, f, 0, -100, 0.0, 0.0, f,
+                                  0) == _lib.CE_E_SHAPE  # v_offset + V > V_total
+    assert _lib.ce_shard_partials(f, _lib.CE_F32, 4, 100, 100, -1, 1000, f, 0, -100, 0.0, 0.0, f,
+                                  0) == _lib.CE_E_SHAPE
+    assert _lib.ce_shard_partials(f, 9, 4, 100, 100, 0, 1000, f, 0, -100, 0.0, 0.0, f,
+                                  0) == _lib.CE_E_DTYPE
+    assert _lib.ce_shard_partials(0, _lib.CE_F32, 4, 100, 100, 0, 1000, f, 0, -100, 0.0, 0.0, f,
+                                  0) == _lib.CE_E_NULL
+    args = dict(logits=f, dtype=_lib.CE_F32, rows=4, V=100, row_stride=100, v_offset=0,
+                V_total=1000, target=f, weight=0, ignore_index=-100, label_smoothing=0.0,
+                lse_square_scale=0.0, softcap=0.0, reduction=_lib.CE_RED_SUM, flags=0,
+                partials_all=f, num_shards=2, loss=f, z_loss=0, token_accuracy=0, argmax=0,
+                counts=0, workspace=f, workspace_bytes=1 << 20, stream=0)
+    assert _lib.ce_shard_finish(**dict(args, num_shards=0)) == _lib.CE_E_PARAM
+    assert _lib.ce_shard_finish(**dict(args, label_smoothing=1.5)) == _lib.CE_E_PARAM
+    assert _lib.ce_shard_finish(**dict(args, workspace_bytes=8)) == _lib.CE_E_WORKSPACE
+    assert _lib.ce_shard_finish(**dict(args, workspace=f + 8)) == _lib.CE_E_WORKSPACE
+    assert _lib.ce_shard_finish(**dict(args, loss=0)) == _lib.CE_E_NULL
+    assert _lib.ce_shard_workspace_bytes(1000) >= 256 + 3 * 4000
