@@ -78,9 +78,11 @@ typedef enum {
   CE_E_WORKSPACE = -5,    /* workspace NULL, too small or not 256-B aligned    */
   CE_E_HIP = -6,          /* a HIP runtime call or kernel launch failed        */
   CE_E_TARGET_RANGE = -7, /* CE_F_CHECK_TARGETS: a target outside [0, V)      */
-  CE_E_EXCHANGE = -8      /* CE_F_CHECK_TARGETS: a row split over workgroups   */
+  CE_E_EXCHANGE = -8,     /* CE_F_CHECK_TARGETS: a row split over workgroups   */
                           /* gave up waiting for one of its parts (its values */
                           /* and the reduced outputs are NaN)                 */
+  CE_E_SCRATCH = -9       /* ce_forward_noalloc: ce_workspace_bytes(...) of   */
+                          /* the problem exceeds CE_FORWARD_NOALLOC_MAX_BYTES */
 } ce_status;
 
 typedef enum { CE_F32 = 0, CE_BF16 = 1 } ce_dtype;
@@ -151,6 +153,32 @@ ce_status ce_forward(void* logits, int dtype, int64_t rows, int64_t V, int64_t r
                      int reduction, uint32_t flags, float* loss, float* z_loss,
                      float* token_accuracy, int64_t* argmax, int64_t* counts, float* row_stats,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device scratch ce_forward_noalloc holds per device (16 MiB). */
+#define CE_FORWARD_NOALLOC_MAX_BYTES (16u << 20)
+
+/* ce_forward for callers that cannot allocate device memory (code under
+ * stream capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments, results and kernels without the workspace argument. The
+ * workspace is a static device array of CE_FORWARD_NOALLOC_MAX_BYTES that
+ * every device holds from the library's first use until the process ends;
+ * the call allocates and frees nothing.
+ *  - The first call on a device looks the array up for that device and
+ *    enqueues one kernel that zero-fills it, ahead of its own work.
+ *  - stream must belong to the current device (else CE_E_PARAM).
+ *  - CE_E_SCRATCH if ce_workspace_bytes(rows, V, dtype, flags) exceeds
+ *    CE_FORWARD_NOALLOC_MAX_BYTES (past 62598 rows at V = 131072 in fp32
+ *    or V = 262144; 119832 rows of fp32 at V = 32768); nothing is enqueued
+ *    then.
+ *  - All calls on one device share the array and each leaves it ready for
+ *    the next: calls in flight at the same time on one device (on different
+ *    streams or host threads) race and must not overlap. */
+ce_status ce_forward_noalloc(void* logits, int dtype, int64_t rows, int64_t V,
+                             int64_t row_stride, const int64_t* target, const float* weight,
+                             int64_t ignore_index, float label_smoothing,
+                             float lse_square_scale, float softcap, int reduction,
+                             uint32_t flags, float* loss, float* z_loss, float* token_accuracy,
+                             int64_t* argmax, int64_t* counts, float* row_stats, void* stream);
 
 /* Backward: grad (rows, row_stride) [device] *= grad_output in place.
  *  grad_output [device] fp32: one value, or rows values when per_row != 0

@@ -28,6 +28,10 @@ CE_E_WORKSPACE = -5
 CE_E_HIP = -6
 CE_E_TARGET_RANGE = -7
 CE_E_EXCHANGE = -8
+CE_E_SCRATCH = -9
+
+# bytes of the static scratch ce_forward_noalloc holds per device
+CE_FORWARD_NOALLOC_MAX_BYTES = 16 << 20
 
 CE_F32 = 0
 CE_BF16 = 1
@@ -61,6 +65,10 @@ _SIGNATURES = {
                                   ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_int,
                                   ctypes.c_uint32, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
                                   _P]),
+    "ce_forward_noalloc": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I64, _P, _P, _I64,
+                                          ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                          ctypes.c_int, ctypes.c_uint32, _P, _P, _P, _P, _P, _P,
+                                          _P]),
     "ce_backward": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I64, _P, ctypes.c_int, _P]),
     "ce_backward_recompute": (ctypes.c_int, [_P, ctypes.c_int, _I64, _I64, _I64, _P, _P, _I64,
                                              ctypes.c_float, ctypes.c_float, ctypes.c_float,
@@ -146,6 +154,18 @@ def ce_forward(logits: int, dtype: int, rows: int, V: int, row_stride: int, targ
                                 ignore_index, label_smoothing, lse_square_scale, softcap,
                                 reduction, flags, loss, z_loss, token_accuracy, argmax, counts,
                                 row_stats, workspace, workspace_bytes, stream))
+
+
+def ce_forward_noalloc(logits: int, dtype: int, rows: int, V: int, row_stride: int,
+                       target: int, weight: int, ignore_index: int, label_smoothing: float,
+                       lse_square_scale: float, softcap: float, reduction: int, flags: int,
+                       loss: int, z_loss: int, token_accuracy: int, argmax: int, counts: int,
+                       row_stats: int, stream: int) -> int:
+    """Raw call; returns the ce_status (0 = CE_OK)."""
+    return int(lib().ce_forward_noalloc(logits, dtype, rows, V, row_stride, target, weight,
+                                        ignore_index, label_smoothing, lse_square_scale,
+                                        softcap, reduction, flags, loss, z_loss, token_accuracy,
+                                        argmax, counts, row_stats, stream))
 
 
 def ce_backward_recompute(logits: int, dtype: int, rows: int, V: int, row_stride: int,

@@ -1,6 +1,8 @@
 // C ABI of the fused softmax cross-entropy library (declared in include/ce.h):
 // argument validation, path planning, workspace layout and the launch
 // sequence prologue -> row kernel(s) (with the last-block epilogue).
+#include <mutex>
+
 #include "ce_plan.hpp"
 
 #define CE_API extern "C" __attribute__((visibility("default")))
@@ -31,13 +33,59 @@ CE_API int ce_plan_path(const void* logits, int dtype, int64_t rows, int64_t V,
 }
 
 
-CE_API ce_status ce_forward(void* logits, int dtype, int64_t rows, int64_t V, int64_t row_stride,
-                            const int64_t* target, const float* weight, int64_t ignore_index,
-                            float label_smoothing, float lse_square_scale, float softcap,
-                            int reduction, uint32_t flags, float* loss, float* z_loss,
-                            float* token_accuracy, int64_t* argmax, int64_t* counts,
-                            float* row_stats, void* workspace, size_t workspace_bytes,
-                            void* stream) {
+// Device memory of ce_forward_noalloc: its workspace, one copy per device
+// that loads the library, held until the process ends. Host code never
+// passes the name itself to a kernel (on the host it is only a stand-in for
+// the symbol): it uses the device address hipGetSymbolAddress returns for
+// the current device, kept in g_scratch.
+static __device__ __align__(256) unsigned char scratch[CE_FORWARD_NOALLOC_MAX_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];  // device address of scratch per device; null until set up
+
+__global__ void scratch_zero_kernel(uint4* p, size_t n) {
+  for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n;
+       i += static_cast<size_t>(gridDim.x) * blockDim.x)
+    p[i] = uint4{0u, 0u, 0u, 0u};
+}
+
+// The current device's scratch address. The first call on a device looks
+// the address up and enqueues one zero fill of the whole array on `st` (a
+// kernel, ahead of that call's own kernels), which is the zero fill every
+// workspace needs before its first use.
+ce_status current_scratch(hipStream_t st, char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return CE_E_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return CE_E_HIP;
+  if (st != nullptr) {
+    int sdev = -1;
+    if (hipStreamGetDevice(st, &sdev) != hipSuccess || sdev != dev) return CE_E_PARAM;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return CE_E_HIP;
+    constexpr size_t n = CE_FORWARD_NOALLOC_MAX_BYTES / sizeof(uint4);
+    scratch_zero_kernel<<<dim3(1024), dim3(256), 0, st>>>(static_cast<uint4*>(ptr), n);
+    if (hipGetLastError() != hipSuccess) return CE_E_HIP;
+    g_scratch[dev] = ptr;
+  }
+  *out = static_cast<char*>(g_scratch[dev]);
+  return CE_OK;
+}
+
+// ce_forward's body on a given workspace; `noalloc`: the workspace is the
+// scratch array (too small a problem is CE_E_SCRATCH, not CE_E_WORKSPACE).
+ce_status forward_on(void* logits, int dtype, int64_t rows, int64_t V, int64_t row_stride,
+                     const int64_t* target, const float* weight, int64_t ignore_index,
+                     float label_smoothing, float lse_square_scale, float softcap, int reduction,
+                     uint32_t flags, float* loss, float* z_loss, float* token_accuracy,
+                     int64_t* argmax, int64_t* counts, float* row_stats, void* workspace,
+                     size_t workspace_bytes, bool noalloc, void* stream) {
   const ce_status bad = check_options(dtype, rows, V, row_stride, label_smoothing,
                                       lse_square_scale, softcap, reduction);
   if (bad != CE_OK) return bad;
@@ -48,6 +96,13 @@ CE_API ce_status ce_forward(void* logits, int dtype, int64_t rows, int64_t V, in
   make_plan(logits, dtype, rows, V, row_stride, weight, label_smoothing, flags, &pl);
   if (rows * (plan_partials(pl) > 0 ? plan_partials(pl) : 1) > kMaxInt) return CE_E_SHAPE;
   const Layout L = layout(rows, pl);
+  if (noalloc) {
+    if (L.total > CE_FORWARD_NOALLOC_MAX_BYTES) return CE_E_SCRATCH;
+    const ce_status sc = current_scratch(static_cast<hipStream_t>(stream),
+                                         reinterpret_cast<char**>(&workspace));
+    if (sc != CE_OK) return sc;
+    workspace_bytes = CE_FORWARD_NOALLOC_MAX_BYTES;
+  }
   if (workspace == nullptr || reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
     return CE_E_WORKSPACE;
   if (workspace_bytes < L.total) return CE_E_WORKSPACE;
@@ -102,6 +157,33 @@ CE_API ce_status ce_forward(void* logits, int dtype, int64_t rows, int64_t V, in
   }
   if (flags & CE_F_CHECK_TARGETS) return check_status(p.hdr, ep, st);
   return CE_OK;
+}
+
+}  // namespace
+
+CE_API ce_status ce_forward(void* logits, int dtype, int64_t rows, int64_t V, int64_t row_stride,
+                            const int64_t* target, const float* weight, int64_t ignore_index,
+                            float label_smoothing, float lse_square_scale, float softcap,
+                            int reduction, uint32_t flags, float* loss, float* z_loss,
+                            float* token_accuracy, int64_t* argmax, int64_t* counts,
+                            float* row_stats, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  return forward_on(logits, dtype, rows, V, row_stride, target, weight, ignore_index,
+                    label_smoothing, lse_square_scale, softcap, reduction, flags, loss, z_loss,
+                    token_accuracy, argmax, counts, row_stats, workspace, workspace_bytes, false,
+                    stream);
+}
+
+CE_API ce_status ce_forward_noalloc(void* logits, int dtype, int64_t rows, int64_t V,
+                                    int64_t row_stride, const int64_t* target,
+                                    const float* weight, int64_t ignore_index,
+                                    float label_smoothing, float lse_square_scale, float softcap,
+                                    int reduction, uint32_t flags, float* loss, float* z_loss,
+                                    float* token_accuracy, int64_t* argmax, int64_t* counts,
+                                    float* row_stats, void* stream) {
+  return forward_on(logits, dtype, rows, V, row_stride, target, weight, ignore_index,
+                    label_smoothing, lse_square_scale, softcap, reduction, flags, loss, z_loss,
+                    token_accuracy, argmax, counts, row_stats, nullptr, 0, true, stream);
 }
 
 CE_API ce_status ce_backward(void* grad, int dtype, int64_t rows, int64_t V, int64_t row_stride,
@@ -185,6 +267,8 @@ CE_API const char* ce_status_string(int status) {
     case CE_E_TARGET_RANGE: return "a target is outside [0, V) and not ignore_index";
     case CE_E_EXCHANGE:
       return "a row split over workgroups gave up waiting for one of its parts (NaN results)";
+    case CE_E_SCRATCH:
+      return "the problem needs more workspace than ce_forward_noalloc's static scratch holds";
     default: return "unknown status";
   }
 }

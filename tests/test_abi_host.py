@@ -59,7 +59,7 @@ def test_missing_library_fails_loudly(tmp_path):
 
 
 def test_status_strings():
-    for s in range(-8, 1):
+    for s in range(-9, 1):
         assert _lib.ce_status_string(s) and _lib.ce_status_string(s) != "unknown status"
     assert _lib.ce_status_string(42) == "unknown status"
 
@@ -224,3 +224,24 @@ def test_shard_argument_checks():
     assert _lib.ce_shard_finish(**dict(args, workspace=f + 8)) == _lib.CE_E_WORKSPACE
     assert _lib.ce_shard_finish(**dict(args, loss=0)) == _lib.CE_E_NULL
     assert _lib.ce_shard_workspace_bytes(1000) >= 256 + 3 * 4000
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch():
+    # host-side check before anything is enqueued: 62599 rows of fp32 at
+    # V = 131072 need one layout step more than the static scratch holds
+    for rows, want in ((62599, _lib.CE_E_SCRATCH), (1 << 20, _lib.CE_E_SCRATCH)):
+        assert _lib.ce_workspace_bytes(rows, 131072, _lib.CE_F32, _lib.CE_F_GRAD) > \
+            _lib.CE_FORWARD_NOALLOC_MAX_BYTES
+        st = _lib.ce_forward_noalloc(1 << 20, _lib.CE_F32, rows, 131072, 131072, 1 << 20, 0,
+                                     -100, 0.0, 0.0, 0.0, _lib.CE_RED_MEAN, _lib.CE_F_GRAD,
+                                     1 << 20, 0, 0, 0, 0, 0, 0)
+        assert st == want
+    assert _lib.ce_workspace_bytes(62598, 131072, _lib.CE_F32, _lib.CE_F_GRAD) <= \
+        _lib.CE_FORWARD_NOALLOC_MAX_BYTES
+    # argument errors come first, as for ce_forward
+    assert _lib.ce_forward_noalloc(1 << 20, 7, 4, 16, 16, 1 << 20, 0, -100, 0.0, 0.0, 0.0,
+                                   _lib.CE_RED_MEAN, 0, 1 << 20, 0, 0, 0, 0, 0, 0) == \
+        _lib.CE_E_DTYPE
+    assert _lib.ce_forward_noalloc(1 << 20, _lib.CE_F32, 4, 16, 16, 1 << 20, 0, -100, 0.0, 0.0,
+                                   0.0, _lib.CE_RED_MEAN, 0, 0, 0, 0, 0, 0, 0, 0) == \
+        _lib.CE_E_NULL
