@@ -81,12 +81,47 @@ def build(jobs: int = 0, verbose: bool = False) -> str:
     return LIB_PATH
 
 
+# Build with AddressSanitizer and UndefinedBehaviorSanitizer on the host code
+# for the host-side checks of the C ABI (argument validation, planning,
+# workspace layout): each sanitizer flag applies to the host pass only, the
+# device code is the ordinary build's. Only CPU checks load this library.
+SAN_DIR = os.path.join(BUILD, "host_san")
+SAN_LIB = os.path.join(SAN_DIR, "libce_host_san.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
+
+
+def build_host_sanitized(jobs: int = 0, verbose: bool = False) -> str:
+    """The library with its host code under ASan and UBSan; returns its path. A program that loads it must be linked with the same
+    sanitizers (it provides their runtime)."""
+    os.makedirs(SAN_DIR, exist_ok=True)
+    cc = hipcc()
+    flags = [*COMMON_FLAGS, *SAN_FLAGS]
+    objs, cmds = [], []
+    for src in SOURCES:
+        obj = os.path.join(SAN_DIR, os.path.splitext(src)[0] + ".o")
+        objs.append(obj)
+        cmds.append([cc, *flags, "-c", os.path.join(CSRC, src), "-o", obj])
+    n = jobs or min(len(cmds), os.cpu_count() or 1)
+    with cf.ThreadPoolExecutor(max_workers=n) as ex:
+        for f in [ex.submit(_run, c, verbose) for c in cmds]:
+            f.result()
+    tmp = SAN_LIB + ".tmp"
+    _run([cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, *LINK_FLAGS, "-o", tmp],
+         verbose)
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--jobs", type=int, default=0)
     ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--host-sanitized", action="store_true",
+                    help="build only the host-side ASan/UBSan library for the ABI checks")
     a = ap.parse_args(argv)
-    path = build(a.jobs, a.verbose)
+    path = build_host_sanitized(a.jobs, a.verbose) if a.host_sanitized else build(a.jobs,
+                                                                                  a.verbose)
     print(path)
     return 0
 
