@@ -239,8 +239,9 @@ ce_status ce_backward_recompute(const void* logits, int dtype, int64_t rows, int
  * ------------------------------------------------------------------------ */
 
 /* Bytes of device workspace ce_linear_forward needs (>= 256), or 0 for
- * invalid sizes. chunk_rows = 0 picks the default chunk (rows whose fp32
- * logits, bf16 gradient and its transpose take at most 6 GiB). */
+ * invalid sizes. chunk_rows = 0 picks the default chunk: at most 2048 rows,
+ * and at most 6 GiB of the chunk's fp32 logits, bf16 gradient and its
+ * transpose (2.1 GB for 2048 rows at V = 128256). */
 size_t ce_linear_workspace_bytes(int64_t rows, int64_t H, int64_t V, int64_t chunk_rows,
                                  uint32_t flags);
 
@@ -261,8 +262,9 @@ size_t ce_linear_workspace_bytes(int64_t rows, int64_t H, int64_t V, int64_t chu
  *  chunk_rows rows per chunk (> 0), or 0 for the default; the workspace
  *             must have been sized with the same value.
  *  workspace  [device] >= ce_linear_workspace_bytes(...) bytes, 256-byte
- *             aligned, zero-filled before its first use; reusable as for
- *             ce_forward.
+ *             aligned; any contents (each call clears the part it needs
+ *             with a kernel on `stream`). Two calls in flight at once must
+ *             not share a workspace.
  * Errors as ce_forward; CE_E_DTYPE if dtype is not CE_BF16; CE_E_SHAPE also
  * for H < 1 or a leading dimension below H. */
 ce_status ce_linear_forward(const void* hidden, int64_t ld_hidden, const void* weight,

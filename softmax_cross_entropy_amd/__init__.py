@@ -7,10 +7,11 @@ is missing -- there is no CPU or PyTorch fallback.
 """
 
 from .functional import (CEOutput, CrossEntropyFunction, CrossEntropyLoss, backward_,
-                         backward_recompute, cross_entropy, forward_raw)
+                         backward_recompute, cross_entropy, forward_raw, release_workspaces)
 from .linear import (LinearCrossEntropyFunction, LinearCrossEntropyLoss, linear_cross_entropy,
                      linear_forward_raw)
 
 __all__ = ["CEOutput", "CrossEntropyFunction", "CrossEntropyLoss", "backward_",
-           "backward_recompute", "cross_entropy", "forward_raw", "LinearCrossEntropyFunction",
+           "backward_recompute", "cross_entropy", "forward_raw", "release_workspaces",
+           "LinearCrossEntropyFunction",
            "LinearCrossEntropyLoss", "linear_cross_entropy", "linear_forward_raw"]

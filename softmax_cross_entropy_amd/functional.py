@@ -54,6 +54,12 @@ def _stream(dev: torch.device) -> int:
 _WORKSPACES = {}
 
 
+def release_workspaces() -> None:
+    """Drop the cached workspaces of every device and stream (the next call
+    allocates and clears a new one)."""
+    _WORKSPACES.clear()
+
+
 def _workspace(dev: torch.device, nbytes: int) -> torch.Tensor:
     """Zero-filled workspace cached per (device, stream), grown on demand.
 

@@ -4,9 +4,10 @@ ce_linear_forward (include/ce.h).
 ``linear_cross_entropy(hidden, weight, target, ...)`` is
 ``cross_entropy(hidden @ weight.T, target, ...)`` with the options of the
 Liger-Kernel page "Kernel Profile: CrossEntropy (Tier 3 - Fused/Complex)"
-(Forward Pass, Module Parameters), computed in row chunks so the full
-(rows, V) logits are never held at once (the page's Classification names the
-fused linear cross-entropy as this kernel extended with the linear layer).
+(Forward Pass, Module Parameters), computed in row chunks (at most 2048 rows
+by default), so a batch of more rows never holds its full (rows, V) logits
+at once (the page's Classification names the fused linear cross-entropy as
+this kernel extended with the linear layer).
 
 Gradients: for reduction "mean" and "sum" the forward computes
 d loss / d hidden and d loss / d weight with the loss (gradient in forward);
@@ -25,7 +26,7 @@ import torch
 
 from . import _lib
 from ._lib import CE_BF16, CE_F32, REDUCTION_CODES, check
-from .functional import CEOutput, _stream, _workspace
+from .functional import CEOutput, _stream
 
 
 def _ptr(a: Optional[torch.Tensor]) -> int:
@@ -81,7 +82,9 @@ def linear_forward_raw(hidden: torch.Tensor, weight: torch.Tensor, target: torch
     nbytes = _lib.ce_linear_workspace_bytes(rows, H, V, chunk_rows, flags)
     if nbytes == 0:
         raise ValueError(f"invalid sizes rows={rows} H={H} V={V} chunk_rows={chunk_rows}")
-    ws = _workspace(dev, nbytes)
+    # Allocated per call (returned to torch's caching allocator afterwards,
+    # not held by this module): the library clears what it needs itself.
+    ws = torch.empty((nbytes,), device=dev, dtype=torch.uint8)
     st = _lib.ce_linear_forward(
         hidden.data_ptr(), hidden.stride(0), weight.data_ptr(), weight.stride(0), CE_BF16, rows,
         H, V, t.data_ptr(), _ptr(cw), ignore_index, label_smoothing, lse_square_scale,

@@ -281,3 +281,39 @@ def test_linear_medium_default_chunk():
                              argmax=True, counts=True)
     torch.cuda.synchronize()
     _check(x, w, t, res, eps=0.1, lam=1e-4, what="medium")
+
+
+def test_linear_dirty_workspace_and_default_chunks():
+    """The workspace may hold anything: every call clears what it needs. 2100
+    rows take two default chunks (2048 + 52); calls on a workspace filled with
+    0xFF bytes, and again after a refill, give the bits of a call on a zeroed
+    one, and the oracle's values."""
+    from softmax_cross_entropy_amd import _lib
+    rows, H, V = 2100, 256, 4000
+    x, w, t = _make(rows, H, V, 321, 40)
+    _announce(name="linear-dirty-workspace", rows=rows, H=H, V=V)
+    xd, wd, td = x.to(DEV), w.to(DEV), t.to(DEV)
+    nbytes = _lib.ce_linear_workspace_bytes(rows, H, V, 0, 0)
+    s = torch.cuda.current_stream().cuda_stream
+    outs = []
+    for fill in (0x00, 0xFF, 0xFF):
+        ws = torch.full((nbytes,), fill, dtype=torch.uint8, device=DEV)
+        loss = torch.empty((), device=DEV)
+        am = torch.empty((rows,), dtype=torch.int64, device=DEV)
+        cnt = torch.empty((2,), dtype=torch.int64, device=DEV)
+        gh = torch.empty((rows, H), device=DEV)
+        gw = torch.empty((V, H), device=DEV)
+        st = _lib.ce_linear_forward(xd.data_ptr(), H, wd.data_ptr(), H, _lib.CE_BF16, rows, H, V,
+                                    td.data_ptr(), 0, -100, 0.1, 1e-4, 0.0, _lib.CE_RED_MEAN, 0,
+                                    0, 0, 0, loss.data_ptr(), 0, 0, am.data_ptr(), cnt.data_ptr(),
+                                    gh.data_ptr(), H, gw.data_ptr(), H, ws.data_ptr(), nbytes, s)
+        assert st == 0, _lib.ce_status_string(st)
+        torch.cuda.synchronize()
+        outs.append((loss, am, cnt, gh, gw))
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a,
+                               b.view(torch.int32) if b.dtype == torch.float32 else b)
+    loss, am, cnt, gh, gw = outs[0]
+    _check(x, w, t, (loss, None, None, am, cnt, gh, gw), eps=0.1, lam=1e-4,
+           what="dirty-workspace")
