@@ -30,7 +30,7 @@ struct ShardArgs {
 };
 
 constexpr int kShardBlock = 256;
-constexpr int kShardUnroll = 8;  // stage 1: vectors per thread in flight
+constexpr int kShardUnroll = 16;  // vectors per thread in flight (4096 per workgroup)
 
 // W = sum of all class weights (the prologue's, over V_total) or V_total,
 // and the mean's scales from the prologue when it ran.
@@ -188,16 +188,16 @@ __device__ __forceinline__ void fold_shards(const Params& p, const ShardArgs& sa
 }
 
 // Stage 2: one workgroup per row (one arrival per row at the epilogue's
-// counter). The row's first loads go out first (they do not depend on the
-// row scalars); wave 0 folds the row's G partials in shard order and thread 0
-// computes the row scalars and writes the row's outputs; then the workgroup
-// walks its slice in spans of kShardBlock x U vectors, the next span's loads
-// in flight while the current one's gradient is written over the logits.
+// counter). The loads of the row's first span (kShardBlock x U vectors, the
+// whole slice up to 4096 vectors) go out first, as they do not depend on the
+// row scalars; wave 0 folds the row's G partials in shard order and thread 0
+// computes the row scalars and writes the row's outputs; then each span's
+// gradient is written over the logits, the next span loaded after it.
 template <class E, int SC, int SM, bool VEC>
 __global__ __launch_bounds__(kShardBlock) void shard_finish_kernel(Params p, ShardArgs sa) {
   constexpr int EPV = E::EPV;
   constexpr int BLOCK = kShardBlock;
-  constexpr int U = 4;
+  constexpr int U = kShardUnroll;
   __shared__ RowScalars s_rs;
   __shared__ int s_last;
   const int tid = threadIdx.x;
@@ -255,11 +255,12 @@ __global__ __launch_bounds__(kShardBlock) void shard_finish_kernel(Params p, Sha
     if constexpr (VEC) {
       u4* wp = reinterpret_cast<u4*>(rp);
       for (int j0 = 0; j0 < nvec; j0 += BLOCK * U) {
-        u4 nx[U];
+        if (j0 > 0) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int j = j0 + (U + u) * BLOCK + tid;
-          nx[u] = (!skip && j < nvec) ? __builtin_nontemporal_load(vp + j) : u4{0u, 0u, 0u, 0u};
+          for (int u = 0; u < U; ++u) {
+            const int j = j0 + u * BLOCK + tid;
+            v[u] = (!skip && j < nvec) ? __builtin_nontemporal_load(vp + j) : u4{0u, 0u, 0u, 0u};
+          }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -269,8 +270,6 @@ __global__ __launch_bounds__(kShardBlock) void shard_finish_kernel(Params p, Sha
             __builtin_nontemporal_store(g, wp + j);
           }
         }
-#pragma unroll
-        for (int u = 0; u < U; ++u) v[u] = nx[u];
       }
       if (tail0 + tid < p.V) {
         const int64_t k = tail0 + tid;
