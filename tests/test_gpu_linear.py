@@ -317,3 +317,55 @@ def test_linear_dirty_workspace_and_default_chunks():
     loss, am, cnt, gh, gw = outs[0]
     _check(x, w, t, (loss, None, None, am, cnt, gh, gw), eps=0.1, lam=1e-4,
            what="dirty-workspace")
+
+
+def test_linear_bench_shape_sampled():
+    """The benchmark's batch: 4096 x 4096 hidden, V = 128256, mean, default
+    chunks, both gradients. Every row's loss term, argmax and the counts
+    against the oracle (evaluated in row blocks: oracle.linear_forward_rows),
+    d loss / d hidden on 16 sampled rows and d loss / d weight on 16 sampled
+    classes, to the tolerances of _check."""
+    from oracle import linear_forward_rows
+    rows, H, V = 4096, 4096, 128256
+    g = torch.Generator(device=DEV)
+    g.manual_seed(7)
+    x = (torch.randn(rows, H, device=DEV, generator=g) * 0.5).to(torch.bfloat16)
+    w = (torch.randn(V, H, device=DEV, generator=g) * (2.0 / H ** 0.5)).to(torch.bfloat16)
+    t = synth.make_targets(rows, V, 7, rows // 20)
+    _announce(name="linear-bench-shape", rows=rows, H=H, V=V)
+    loss, _, acc, am, cnt, gh, gw = linear_forward_raw(x, w, t.to(DEV), token_accuracy=True,
+                                                       argmax=True, counts=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    counted = t.numpy() != -100
+    sr = np.sort(np.concatenate([[0, rows - 1], rng.choice(np.nonzero(counted)[0], 13,
+                                                           replace=False),
+                                 np.nonzero(~counted)[0][:1]]))
+    sc = np.sort(np.concatenate([[0, V - 1], rng.choice(V, 14, replace=False)]))
+    am_g = am.cpu().numpy()
+    xb, wb = _bits(x), _bits(w)
+    print("  gpu done; oracle over every row in blocks", flush=True)
+    ref = linear_forward_rows(xb, wb, t.numpy(), sample_rows=sr, sample_cols=sc, at_cols=am_g)
+    # loss: the fp32 logits move by at most dz per row, the row's loss by 2 dz
+    dz = H * 2.0 ** -24 * ref.logits_abs_max
+    tol = 1e-5 * abs(ref.loss) + (2.0 * dz[counted]).sum() / ref.D + 1e-7
+    assert abs(loss.item() - ref.loss) <= tol, (loss.item(), ref.loss, tol)
+    # argmax: exact where the top two logits are farther apart than the bound
+    gap = ref.top2[:, 0] - ref.top2[:, 1]
+    exact = counted & (gap > 2.0 * dz)
+    np.testing.assert_array_equal(am_g[exact], ref.argmax[exact])
+    near = counted & ~exact
+    assert np.all(ref.at_cols[near] >= ref.top2[near, 0] - 2.0 * dz[near])
+    assert np.all(am_g[~counted] == -1)
+    c = cnt.cpu().numpy()
+    assert int(c[0]) == ref.n_valid
+    assert int(c[1]) == int(np.sum((am_g == t.numpy()) & counted))
+    assert abs(acc.item() - np.float32(c[1] / c[0])) <= 1e-7
+    got_h = gh[torch.from_numpy(sr).to(DEV)].double().cpu().numpy()
+    got_w = gw[torch.from_numpy(sc).to(DEV)].double().cpu().numpy()
+    tol_h = (2.0 ** -8 + V * 2.0 ** -24) * ref.mag_hidden + 1e-7
+    tol_w = (2.0 ** -8 + rows * 2.0 ** -24) * ref.mag_weight + 1e-7
+    eh = np.abs(got_h - ref.grad_hidden) - tol_h
+    ew = np.abs(got_w - ref.grad_weight) - tol_w
+    assert np.all(eh <= 0), ("grad_hidden", float(eh.max()))
+    assert np.all(ew <= 0), ("grad_weight", float(ew.max()))

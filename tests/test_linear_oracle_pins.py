@@ -134,3 +134,38 @@ def test_tolerance_helpers_golden():
     gh, gw = grad_magnitudes(h, w, G)
     np.testing.assert_array_equal(gh, np.array(c["grad_hidden_mag"]))
     np.testing.assert_array_equal(gw, np.array(c["grad_weight_mag"]))
+
+
+@pytest.mark.parametrize("reduction", ["mean", "sum", "none"])
+def test_row_chunked_form_equals_whole_batch(reduction):
+    """linear_forward_rows (row blocks, global gradient scales, weight
+    gradient summed block by block) gives linear_forward's values."""
+    from oracle import grad_magnitudes, linear_forward_rows
+    rng = np.random.default_rng(11)
+    rows, H, V = 13, 6, 9
+    x = rng.standard_normal((rows, H))
+    w = rng.standard_normal((V, H))
+    t = rng.integers(0, V, rows)
+    t[[2, 7]] = -100
+    cw = rng.uniform(0.5, 2.0, V)
+    opts = dict(class_weight=cw, label_smoothing=0.1, lse_square_scale=0.01, softcap=4.0,
+                reduction=reduction)
+    full = linear_forward(x, w, t, **opts)
+    sr = np.array([0, 2, 5, 12])
+    sc = np.array([1, 8, 3])
+    at = rng.integers(0, V, rows)
+    part = linear_forward_rows(x, w, t, sample_rows=sr, sample_cols=sc, at_cols=at, row_chunk=4,
+                               **opts)
+    np.testing.assert_allclose(part.loss, full.ce.loss, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(part.z_loss, full.ce.z_loss, rtol=1e-13, atol=1e-15)
+    np.testing.assert_array_equal(part.argmax, full.ce.argmax)
+    assert part.n_correct == full.ce.n_correct and part.n_valid == full.ce.n_valid
+    np.testing.assert_allclose(part.grad_hidden, full.grad_hidden[sr], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(part.grad_weight, full.grad_weight[sc], rtol=1e-12, atol=1e-15)
+    srt = np.sort(full.logits, axis=1)
+    np.testing.assert_allclose(part.top2, srt[:, ::-1][:, :2], rtol=1e-14)
+    np.testing.assert_allclose(part.at_cols, full.logits[np.arange(rows), at], rtol=1e-14)
+    np.testing.assert_allclose(part.logits_abs_max, full.logits_abs.max(axis=1), rtol=1e-14)
+    mh, mw = grad_magnitudes(x, w, full.ce.grad)
+    np.testing.assert_allclose(part.mag_hidden, mh[sr], rtol=1e-12)
+    np.testing.assert_allclose(part.mag_weight, mw[sc], rtol=1e-12)
