@@ -252,6 +252,67 @@ def linear_bench(steps: int, warmup: int, rows: int = 4096, H: int = 4096, V: in
                      "frac": tf / 2500.0, "flops_per_step": flops}}), flush=True)
 
 
+def linear_forward_bench(steps: int, warmup: int, rows: int = 4096, H: int = 4096,
+                         V: int = 128256) -> None:
+    """The linear layer fused with the cross-entropy without gradients (an
+    evaluation step: loss, z-loss, token accuracy, argmax) at the language-model
+    head shape: the matrix-core kernel that keeps the logits on chip
+    (CE_F_LINEAR_ON_CHIP), the library GEMM path with fp32 logits (the
+    default), and PyTorch eager
+    (bf16 matmul, fp32 cross-entropy) under no_grad. Matrix-core roofline:
+    2 rows V H flops per step against the bf16 dense peak."""
+    import torch
+    import torch.nn.functional as F
+    import synth
+    from softmax_cross_entropy_amd import _lib, linear_forward_raw
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    x = (torch.randn(rows, H, device=dev, generator=g) * 0.5).to(torch.bfloat16)
+    w = (torch.randn(V, H, device=dev, generator=g) * (2.0 / H ** 0.5)).to(torch.bfloat16)
+    t = synth.make_targets(rows, V, 7, rows // 20).to(dev)
+    kw = dict(reduction="mean", grad=False, token_accuracy=True, argmax=True)
+
+    def matrix_core():
+        linear_forward_raw(x, w, t, flags=_lib.CE_F_LINEAR_ON_CHIP, **kw)
+
+    def library():
+        linear_forward_raw(x, w, t, **kw)
+
+    def eager():
+        with torch.no_grad():
+            lg = (x @ w.t()).float()
+            F.cross_entropy(lg, t, ignore_index=-100)
+            lg.argmax(dim=1)
+
+    res = {}
+    for name, fn in (("matrix_core_kernel", matrix_core), ("library_gemm", library),
+                     ("torch_eager", eager)):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / steps
+    flops = 2.0 * rows * V * H
+    tf = flops / (res["matrix_core_kernel"] * 1e-3) / 1e12
+    print(json.dumps({
+        "linear_forward": "linear layer fused with the cross-entropy, no gradients (loss, "
+                          "token accuracy, argmax), mean, bf16 inputs",
+        "config": {"rows": rows, "H": H, "V": V},
+        "ms_per_step": res,
+        "speedup_vs_library_gemm": res["library_gemm"] / res["matrix_core_kernel"],
+        "speedup_vs_torch_eager": res["torch_eager"] / res["matrix_core_kernel"],
+        "roofline": {"bound": "mfma", "achieved": tf, "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": tf / 2500.0, "flops_per_step": flops}}), flush=True)
+
+
 def shard_bench(reps: int = 20, G: int = 8) -> None:
     """One device's share of the headline batch split over G vocabulary shards
     (1023 rows x 128256 / G columns of fp32, reduction sum): stage 1 on its
@@ -624,6 +685,9 @@ def main(argv=None) -> int:
     ap.add_argument("--linear", action="store_true",
                     help="the linear layer fused with the cross-entropy at 4096 x 4096 hidden, "
                          "V = 128256 (JSON line with its matrix-core roofline), then exit")
+    ap.add_argument("--forward-only", action="store_true",
+                    help="--linear: the forward without gradients (matrix-core kernel against "
+                         "the library GEMM path and PyTorch eager)")
     ap.add_argument("--chunk-rows", type=int, default=0,
                     help="--linear: rows per chunk (0: the library's default)")
     ap.add_argument("--sweep", action="store_true",
@@ -647,7 +711,10 @@ def main(argv=None) -> int:
         return 2
 
     if a.linear:
-        linear_bench(a.steps, a.warmup, chunk_rows=a.chunk_rows)
+        if a.forward_only:
+            linear_forward_bench(a.steps, a.warmup)
+        else:
+            linear_bench(a.steps, a.warmup, chunk_rows=a.chunk_rows)
         return 0
 
     if a.sweep:

@@ -103,9 +103,13 @@ enum {
                                 /* 256/512-thread ones; 16 K to 32 K: a pair   */
                                 /* of 1024-thread workgroups per row vs four   */
                                 /* 512-thread ones)                            */
-  CE_F_EXCHANGE_ONE_POLL = 1u << 9 /* test hook: a row split over workgroups  */
+  CE_F_EXCHANGE_ONE_POLL = 1u << 9, /* test hook: a row split over workgroups */
                                 /* polls its parts' partials once before it    */
                                 /* gives up (forces the failure path below)    */
+  CE_F_LINEAR_ON_CHIP = 1u << 10 /* ce_linear_forward without gradients: the */
+                                /* hand-written matrix-core kernel that keeps  */
+                                /* the logits on chip (no logits workspace)    */
+                                /* instead of the library GEMM and fp32 logits */
 };
 
 /* Kernel paths (ce_plan_path). */

@@ -48,6 +48,7 @@ CE_F_FORCE_SPLITV = 1 << 6
 CE_F_FORCE_SCALAR = 1 << 7
 CE_F_SHAPE_ALT = 1 << 8
 CE_F_EXCHANGE_ONE_POLL = 1 << 9
+CE_F_LINEAR_ON_CHIP = 1 << 10
 
 CE_PATH_FUSED = 1
 CE_PATH_SPLITV = 2

@@ -6,6 +6,10 @@
 
 #include "ce_device.hpp"
 
+namespace cedev {
+struct ShardArgs;
+}
+
 namespace cehost {
 
 // Fused row shapes: BLOCK threads, each holding NREG vectors in VGPRs,
@@ -66,5 +70,9 @@ hipError_t launch_backward_f32(void* grad, int64_t rows, int64_t V, int64_t stri
                                const float* go, int per_row, bool vec, hipStream_t st);
 hipError_t launch_backward_bf16(void* grad, int64_t rows, int64_t V, int64_t stride,
                                 const float* go, int per_row, bool vec, hipStream_t st);
+// The vocabulary-shard finish (ce_shard.hip): fold each row's partials in
+// shard order, write the outputs, and with p.grad the slice's gradient.
+hipError_t launch_shard_finish(int dtype, const cedev::Params& p, const cedev::ShardArgs& sa,
+                               bool vec, hipStream_t st);
 
 }  // namespace cehost

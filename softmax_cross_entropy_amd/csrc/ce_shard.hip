@@ -83,6 +83,13 @@ bool shard_vec(const void* logits, int dtype, int64_t row_stride, const float* w
 
 }  // namespace
 
+namespace cehost {
+hipError_t launch_shard_finish(int dtype, const cedev::Params& p, const cedev::ShardArgs& sa,
+                               bool vec, hipStream_t st) {
+  return dispatch<Finish>(dtype, p, sa, vec, st);
+}
+}  // namespace cehost
+
 CE_API size_t ce_shard_workspace_bytes(int64_t rows) {
   if (rows < 0 || rows > kMaxInt) return 0;
   return kAlign + 3 * align_up(static_cast<size_t>(rows) * 4);

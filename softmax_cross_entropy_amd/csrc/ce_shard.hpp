@@ -155,34 +155,54 @@ __global__ __launch_bounds__(kShardBlock) void shard_partial_kernel(Params p, Sh
   }
 }
 
-// Wave 0: the row's G partials folded in shard order (lanes read up to 64
-// of them at once, lane 0 folds them from the lanes); lane 0 returns
-// (m, s, sz, largest raw logit, its index, target logit).
+// Wave 0: the row's G partials folded in a fixed tree: lane l folds the
+// partials l K .. l K + K - 1 (K = ceil(G / 64)) in shard order, then the
+// lanes combine in a butterfly, each pair taking the lower lane's value
+// first, so every lane ends with the same bits and every device that folds
+// the same partials gets them too. Returns (m, s, sz, largest raw logit, its
+// index, target logit).
 __device__ __forceinline__ void fold_shards(const Params& p, const ShardArgs& sa, int64_t row,
                                             float& m, float& s, float& sz, float& bv, int& bi,
                                             float& xy) {
   const int lane = threadIdx.x & 63;
-  for (int g0 = 0; g0 < sa.G; g0 += 64) {
-    Partial q = {kLowest, 0.0f, 0.0f, -__builtin_inff(), kNoIndex, 0.0f, 0, 0};
-    if (g0 + lane < sa.G) q = sa.parts[static_cast<int64_t>(g0 + lane) * p.rows + row];
-    const int n = min(64, sa.G - g0);
-    for (int i = 0; i < n; ++i) {
-      const float qm = __shfl(q.m, i, 64), qs = __shfl(q.s, i, 64);
-      const float qz = __shfl(q.sz, i, 64), qb = __shfl(q.bv, i, 64);
-      const int qi = __shfl(q.bi, i, 64), qh = __shfl(q.has_y, i, 64);
-      const float qy = __shfl(q.xy, i, 64);
-      if (g0 + i == 0) {
-        m = qm;
-        s = qs;
-        sz = qz;
-        bv = qb;
-        bi = qi;
-      } else {
-        ms_combine(m, s, qm, qs);
-        sz += qz;
-        arg_combine(bv, bi, qb, qi);  // shards in column order: ties keep the earlier
+  const int K = (sa.G + 63) / 64;
+  m = kLowest;
+  s = 0.0f;
+  sz = 0.0f;
+  bv = -__builtin_inff();
+  bi = kNoIndex;
+  xy = 0.0f;
+  int hy = 0;
+  for (int k = 0; k < K; ++k) {
+    const int gi = lane * K + k;
+    if (gi < sa.G) {
+      const Partial q = sa.parts[static_cast<int64_t>(gi) * p.rows + row];
+      ms_combine(m, s, q.m, q.s);
+      sz += q.sz;
+      arg_combine(bv, bi, q.bv, q.bi);  // equal values: the lower index
+      if (q.has_y) {
+        xy = q.xy;
+        hy = 1;
       }
-      if (qh) xy = qy;
+    }
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float m2 = __shfl_xor(m, off, 64), s2 = __shfl_xor(s, off, 64);
+    const float z2 = __shfl_xor(sz, off, 64), b2 = __shfl_xor(bv, off, 64);
+    const int i2 = __shfl_xor(bi, off, 64), h2 = __shfl_xor(hy, off, 64);
+    const float y2 = __shfl_xor(xy, off, 64);
+    const bool low = (lane & off) == 0;
+    float ma = low ? m : m2, sa_ = low ? s : s2;
+    const float mb = low ? m2 : m, sb = low ? s2 : s;
+    ms_combine(ma, sa_, mb, sb);
+    m = ma;
+    s = sa_;
+    sz = low ? sz + z2 : z2 + sz;
+    arg_combine(bv, bi, b2, i2);  // symmetric: the same result in both lanes
+    if (h2) {
+      xy = y2;
+      hy = 1;
     }
   }
 }

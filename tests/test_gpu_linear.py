@@ -369,3 +369,35 @@ def test_linear_bench_shape_sampled():
     ew = np.abs(got_w - ref.grad_weight) - tol_w
     assert np.all(eh <= 0), ("grad_hidden", float(eh.max()))
     assert np.all(ew <= 0), ("grad_weight", float(ew.max()))
+
+
+# The forward without gradients on the matrix-core kernel (CE_F_LINEAR_ON_CHIP:
+# partials of 256-class blocks, logits kept on chip) and on the default
+# library GEMM path with fp32 logits. Shapes: ragged classes (V not a
+# multiple of 256), rows not a multiple of 128, H not a multiple of 64, and
+# one row block spanning several XCD patches.
+FWD_SHAPES = [(37, 64, 3001), (300, 96, 4096), (130, 136, 8000), (33, 32, 40003),
+              (1030, 128, 2304)]
+
+
+@pytest.mark.parametrize("opt", list(OPTS))
+@pytest.mark.parametrize("reduction", ["mean", "sum", "none"])
+@pytest.mark.parametrize("shape", FWD_SHAPES)
+def test_linear_forward_only_matrix_core(opt, reduction, shape):
+    from softmax_cross_entropy_amd._lib import CE_F_LINEAR_ON_CHIP
+    rows, H, V = shape
+    o = OPTS[opt]
+    x, w, t = _make(rows, H, V, 900 + rows + V, max(1, rows // 12))
+    cw = (0.5 + 1.5 * torch.rand(V, generator=torch.Generator().manual_seed(V))
+          if o.get("cw") else None)
+    _announce(name="linear-forward-only", rows=rows, H=H, V=V, opt=opt, reduction=reduction)
+    kw = dict(class_weight=None if cw is None else cw.to(DEV), label_smoothing=o.get("eps", 0.0),
+              lse_square_scale=o.get("lam", 0.0), softcap=o.get("softcap"), reduction=reduction,
+              grad=False, z_loss=True, token_accuracy=True, argmax=True, counts=True)
+    res = linear_forward_raw(x.to(DEV), w.to(DEV), t.to(DEV), flags=CE_F_LINEAR_ON_CHIP, **kw)
+    lib = linear_forward_raw(x.to(DEV), w.to(DEV), t.to(DEV), **kw)
+    torch.cuda.synchronize()
+    _check(x, w, t, res, cw=cw, eps=o.get("eps", 0.0), lam=o.get("lam", 0.0),
+           softcap=o.get("softcap"), reduction=reduction, what=f"forward-only/{opt}")
+    _check(x, w, t, lib, cw=cw, eps=o.get("eps", 0.0), lam=o.get("lam", 0.0),
+           softcap=o.get("softcap"), reduction=reduction, what=f"forward-only-library/{opt}")
