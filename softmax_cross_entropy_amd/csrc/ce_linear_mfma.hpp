@@ -10,14 +10,16 @@
 // Fused/Complex)", Classification, names the fused linear cross-entropy as
 // the kernel this one extends with a linear layer.
 //
-// Tiles (one workgroup): 256 classes x 128 rows, the reduction dimension H
-// in slices of 32 (H a multiple of 32). The products are computed transposed, classes on the
-// matrix instruction's M side (operand A = weight rows) and batch rows on
-// its N side (operand B = hidden rows): both operands are then read
-// H-contiguous, and each lane's accumulators hold 16 classes of one row,
-// so the per-row reductions of the epilogue run mostly inside a lane.
-// Four waves: two halves of the classes x two halves of the rows, each wave
-// 128 classes x 64 rows = 4 x 2 tiles of 32 x 32.
+// Tiles (one workgroup): 256 classes x 256 rows, the reduction dimension H
+// in slices of 32 (H a multiple of 32), four slices in flight. The products
+// are computed transposed, classes on the matrix instruction's M side
+// (operand A = weight rows) and batch rows on its N side (operand B = hidden
+// rows): both operands are then read H-contiguous, and each lane's
+// accumulators hold 16 classes of one row, so the per-row reductions of the
+// epilogue run mostly inside a lane. Eight waves: kLinWC groups of the
+// classes x kLinWR groups of the rows, each wave 256 / kLinWC classes x
+// 32 kLinNJ rows in tiles of 32 x 32 (two waves per SIMD, one workgroup
+// per CU).
 #pragma once
 
 #include "ce_shard.hpp"
@@ -25,16 +27,20 @@
 namespace cedev {
 
 constexpr int kLinTileV = 256;    // classes per workgroup
+constexpr int kLinWC = 2;         // waves along the classes (each 256 / kLinWC classes)
+constexpr int kLinWR = 4;         // waves along the rows
 constexpr int kLinNJ = 2;         // 32-row tiles per wave
-constexpr int kLinTileR = 64 * kLinNJ;  // batch rows per workgroup (two row halves)
+constexpr int kLinNI = kLinTileV / kLinWC / 32;  // 32-class tiles per wave
+constexpr int kLinTileR = 32 * kLinNJ * kLinWR;  // batch rows per workgroup
 constexpr int kLinTileK = 32;     // H per stage (32: 64-byte rows of bf16, 64: 128-byte rows)
-constexpr int kLinStages = 3;     // LDS stages in flight
+constexpr int kLinStages = 4;     // LDS stages in flight
 constexpr int kLinWavesPerEU = 2;
-constexpr int kLinThreads = 256;
+constexpr int kLinWaves = kLinWC * kLinWR;
+constexpr int kLinThreads = 64 * kLinWaves;
 constexpr int kLinRowBytes = kLinTileK * 2;
 constexpr int kLinChunks = kLinTileK / 8;   // 16-byte chunks per LDS row
-constexpr int kLinLoadsA = kLinTileV * kLinRowBytes / 1024 / 4;  // 1 KiB loads per wave per stage
-constexpr int kLinLoadsB = kLinTileR * kLinRowBytes / 1024 / 4;
+constexpr int kLinLoadsA = kLinTileV * kLinRowBytes / 1024 / kLinWaves;  // 1 KiB loads per wave
+constexpr int kLinLoadsB = kLinTileR * kLinRowBytes / 1024 / kLinWaves;  // per stage
 // Position of chunk c of row R in LDS: c ^ lin_swz(R). Rows 16 / chunks
 // apart share banks; the permutation spreads the rows of each such period.
 __device__ __forceinline__ int lin_swz(int r) { return (r / (16 / kLinChunks)) % kLinChunks; }
@@ -60,7 +66,8 @@ struct LinArgs {
 // turn, so the workgroups running together on one XCD (and sharing its L2)
 // are those with the same blockIdx.x mod 8: each XCD takes its own range of
 // class blocks and walks it in patches of 4 class blocks x 8 row blocks, 32
-// workgroups that read 4 weight tiles and 8 hidden tiles between them.
+// workgroups (one per CU of the XCD) that read 4 weight tiles and 8 hidden
+// tiles between them.
 __device__ __forceinline__ bool lin_work(const LinArgs& g, int& cb, int& rb) {
   const int xcd = blockIdx.x & 7;
   const int q = blockIdx.x >> 3;
@@ -83,7 +90,7 @@ __global__ __launch_bounds__(kLinThreads) __attribute__((amdgpu_waves_per_eu(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wc = wave & 1, wr = wave >> 1;  // class half, row half
+  const int wc = wave % kLinWC, wr = wave / kLinWC;  // class group, row group
   const int64_t c0 = static_cast<int64_t>(cb) * kLinTileV;
   const int64_t r0 = static_cast<int64_t>(rb) * kLinTileR;
 
@@ -96,10 +103,15 @@ __global__ __launch_bounds__(kLinThreads) __attribute__((amdgpu_waves_per_eu(
   // 4), so the fragment reads below (16 lanes, 16 consecutive rows, one chunk
   // each) hit 16 distinct groups of 4 banks. Rows past V or past the batch
   // are read from the last valid row (their results are never used).
-  // The stages, and after the products the epilogue's areas: 4 waves x 32
-  // rows x 132 floats, then the records of one class half (2 x 32 NJ rows).
+  // The stages, and after the products the epilogue's areas: per wave 32
+  // rows x (CW + 4) floats, then the records of the class groups above the
+  // first (kLinWC - 1) x 2 x 32 NJ rows.
+  constexpr int NI = kLinNI;
+  constexpr int CW = 32 * NI;  // classes per wave
+  constexpr int kEP = CW + 4;
   constexpr int kStageBytes = NST * (kLinTileV + kLinTileR) * kLinRowBytes;
-  constexpr int kEpilogueBytes = 4 * 32 * 132 * 4 + 2 * 32 * NJ * 32;
+  constexpr int kEpilogueBytes =
+      kLinWaves * 32 * kEP * 4 + (kLinWC - 1) * kLinWR * 32 * NJ * static_cast<int>(sizeof(Partial));
   __shared__ __attribute__((aligned(1024)))
   uint8_t smem[kStageBytes > kEpilogueBytes ? kStageBytes : kEpilogueBytes];
   constexpr int SA = kLinTileV * kLinRowBytes, SB = kLinTileR * kLinRowBytes;
@@ -135,9 +147,9 @@ __global__ __launch_bounds__(kLinThreads) __attribute__((amdgpu_waves_per_eu(
                                        &sB[buf][(wave * kLinLoadsB + q) * 1024], 16, 0, 0);
   };
 
-  f32x16 acc[4][NJ];
+  f32x16 acc[NI][NJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
     for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
 
@@ -149,7 +161,7 @@ __global__ __launch_bounds__(kLinThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
   for (int st = 0; st < NS; ++st)
     fo[st] = (lane & 31) * kLinRowBytes + ((2 * st + (lane >> 5)) ^ sw) * 16;
-  const int fa = wc * 128 * kLinRowBytes, fb = wr * (32 * NJ) * kLinRowBytes;
+  const int fa = wc * CW * kLinRowBytes, fb = wr * (32 * NJ) * kLinRowBytes;
   constexpr int TS = 32 * kLinRowBytes;  // bytes of a 32-row tile
   const int nk = g.H / kLinTileK;
   // stages 0 .. NST - 2 in flight before the loop
@@ -161,16 +173,16 @@ __global__ __launch_bounds__(kLinThreads) __attribute__((amdgpu_waves_per_eu(
   // Fragments of the 16-wide steps of a stage: those of step 0 are read
   // before the stage's products start (right after the barrier), those of
   // each later step while the products of the step before run.
-  bf16x8 fa_[2][4], fb_[2][NJ];
-  auto read_frags = [&](int buf, int off, bf16x8 (&a)[4], bf16x8 (&b)[NJ]) {
+  bf16x8 fa_[2][NI], fb_[2][NJ];
+  auto read_frags = [&](int buf, int off, bf16x8 (&a)[NI], bf16x8 (&b)[NJ]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const bf16x8*>(&sA[buf][fa + i * TS + off]);
+    for (int i = 0; i < NI; ++i) a[i] = *reinterpret_cast<const bf16x8*>(&sA[buf][fa + i * TS + off]);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) b[j] = *reinterpret_cast<const bf16x8*>(&sB[buf][fb + j * TS + off]);
   };
-  auto products = [&](const bf16x8 (&a)[4], const bf16x8 (&b)[NJ]) {
+  auto products = [&](const bf16x8 (&a)[NI], const bf16x8 (&b)[NJ]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
@@ -184,11 +196,12 @@ __global__ __launch_bounds__(kLinThreads) __attribute__((amdgpu_waves_per_eu(
       products(fa_[st & 1], fb_[st & 1]);
       // interleave: one product, one fragment read of the next step
 #pragma unroll
-      for (int u = 0; u < 4 + NJ; ++u) {
+      for (int u = 0; u < NI + NJ; ++u) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4 * NJ - (4 + NJ), 0);
+      if constexpr (NI * NJ > NI + NJ)
+        __builtin_amdgcn_sched_group_barrier(0x008, NI * NJ - (NI + NJ), 0);
     }
     // Stage ks + NST - 1 goes out after this stage's last fragment reads (in
     // program order, so the reads need not wait for it), into the buffer
@@ -217,23 +230,24 @@ __global__ __launch_bounds__(kLinThreads) __attribute__((amdgpu_waves_per_eu(
     if (ks + 1 < nk) read_frags((ks + 1) % NST, fo[0], fa_[0], fb_[0]);
   }
 
-  // ---- epilogue: per row, the partial over this wave's 128 classes ----
+  // ---- epilogue: per row, the partial over this wave's CW classes ----
   // Accumulator r of tile (i, j) in lane l holds row 32 j + l % 32 of the
   // wave's rows and class 32 i + 8 (r / 4) + 4 (l / 32) + r % 4 of its
-  // classes. One 32-row tile at a time, the wave writes its 128 x 32 logits
-  // to its own LDS area (row-major, rows of 132 floats so that the 16-byte
-  // reads of 16 rows hit distinct banks); then lane l takes row l % 32 and
-  // classes 64 (l / 32) .. + 63, and lanes l and l ^ 32 combine.
-  constexpr int kEP = 132;
+  // classes. One 32-row tile at a time, the wave writes its CW x 32 logits
+  // to its own LDS area (row-major, rows of CW + 4 floats so that the
+  // 16-byte reads of 16 rows hit distinct banks); then lane l takes row
+  // l % 32 and classes CW / 2 (l / 32) .. + CW / 2 - 1, and lanes l and
+  // l ^ 32 combine.
   float* ep = reinterpret_cast<float*>(smem) + wave * 32 * kEP;
   const int er = lane & 31, eh = lane >> 5;
-  const int64_t cbase = c0 + wc * 128 + eh * 64;  // the lane's first class
-  const int nv = static_cast<int>(p.V - cbase < 64 ? (p.V - cbase > 0 ? p.V - cbase : 0) : 64);
+  const int64_t cbase = c0 + wc * CW + eh * (CW / 2);  // the lane's first class
+  const int nv = static_cast<int>(p.V - cbase < CW / 2 ? (p.V - cbase > 0 ? p.V - cbase : 0)
+                                                       : CW / 2);
   Partial rec[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         *reinterpret_cast<f4*>(&ep[er * kEP + i * 32 + 8 * q + 4 * eh]) =
@@ -243,7 +257,7 @@ __global__ __launch_bounds__(kLinThreads) __attribute__((amdgpu_waves_per_eu(
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const int64_t row = r0 + wr * (32 * NJ) + j * 32 + er;
     const int64_t y = row < p.rows ? p.target[row] : p.ignore_index;
-    const float* xr = &ep[er * kEP + eh * 64];
+    const float* xr = &ep[er * kEP + eh * (CW / 2)];
     float bv = -__builtin_inff(), zmax = kLowest;
     int bi = kNoIndex;
     for (int e = 0; e < nv; ++e) {
@@ -260,7 +274,7 @@ __global__ __launch_bounds__(kLinThreads) __attribute__((amdgpu_waves_per_eu(
     const bool here = y >= cbase && y < cbase + nv;
     float xy = here ? xr[y - cbase] : 0.0f;
     int has_y = here ? 1 : 0;
-    // the other 64 classes of the row, in lane l ^ 32
+    // the other classes of the wave for this row, in lane l ^ 32
     float m2 = __shfl_xor(zmax, 32, 64), s2 = __shfl_xor(s, 32, 64);
     float sz2 = __shfl_xor(sz, 32, 64), bv2 = __shfl_xor(bv, 32, 64);
     int bi2 = __shfl_xor(bi, 32, 64);
@@ -279,29 +293,32 @@ __global__ __launch_bounds__(kLinThreads) __attribute__((amdgpu_waves_per_eu(
     __builtin_amdgcn_wave_barrier();  // the area is written again by the next tile
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
-  // The two waves of a row half: the upper class half hands its records to
-  // the lower one through LDS (reused from the slices), which folds them in
-  // class order and stores the block's partial.
+  // The class groups of a row half: the groups above the first hand their
+  // records to the first through LDS, which folds them in class order and
+  // stores the block's partial.
   __syncthreads();
-  Partial* sx = reinterpret_cast<Partial*>(smem + 4 * 32 * kEP * 4);  // past the 4 waves' areas
-  if (wc == 1 && lane < 32) {
+  Partial* sx = reinterpret_cast<Partial*>(smem + kLinWaves * 32 * kEP * 4);
+  constexpr int RH = 32 * NJ;  // rows per row group
+  if (wc > 0 && lane < 32) {
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) sx[wr * (32 * NJ) + j * 32 + lane] = rec[j];
+    for (int j = 0; j < NJ; ++j) sx[((wc - 1) * kLinWR + wr) * RH + j * 32 + lane] = rec[j];
   }
   __syncthreads();
   if (wc == 0 && lane < 32) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      const int64_t row = r0 + wr * (32 * NJ) + j * 32 + lane;
+      const int64_t row = r0 + wr * RH + j * 32 + lane;
       if (row < p.rows) {
         Partial q = rec[j];
-        const Partial u = sx[wr * (32 * NJ) + j * 32 + lane];
-        ms_combine(q.m, q.s, u.m, u.s);
-        q.sz += u.sz;
-        arg_combine(q.bv, q.bi, u.bv, u.bi);
-        if (u.has_y) {
-          q.xy = u.xy;
-          q.has_y = 1;
+        for (int c = 1; c < kLinWC; ++c) {
+          const Partial u = sx[((c - 1) * kLinWR + wr) * RH + j * 32 + lane];
+          ms_combine(q.m, q.s, u.m, u.s);
+          q.sz += u.sz;
+          arg_combine(q.bv, q.bi, u.bv, u.bi);
+          if (u.has_y) {
+            q.xy = u.xy;
+            q.has_y = 1;
+          }
         }
         g.parts[static_cast<int64_t>(cb) * p.rows + row] = q;
       }
