@@ -417,38 +417,57 @@ __device__ __forceinline__ bool epilogue_publish(const Params& p, int64_t row, b
   return arrive(p, total_blocks);
 }
 
-// Whole block, in the block that arrived last only.
-template <int BLOCK>
+// Whole block, in the block that arrived last only. UNROLL: rows per thread
+// in flight (the VGPRs this takes are the kernel's peak in the lighter
+// kernels, so it is 8 unless a kernel has registers to spare).
+template <int BLOCK, int UNROLL = 8>
 __device__ __forceinline__ void epilogue_reduce(const Params& p) {
   __shared__ double s_red[2][BLOCK / 64];
   __shared__ int64_t s_cnt[2][BLOCK / 64];
   const int tid = threadIdx.x;
+  // Every load here is device-coherent and takes a full memory latency at
+  // the end of a launch, when the last gradient stores are draining: thread
+  // 0 issues its two header words together with its first rows, and each
+  // thread has UNROLL rows in flight at once, with indexes clamped into the
+  // arrays so no load sits behind a per-lane branch. The sums still run in
+  // row order and skip the rows past the end, so the result does not depend
+  // on UNROLL.
+  uint32_t xe = 0u;
+  double D_hdr = 0.0;
+  if (tid == 0) {
+    if (p.xstamp != 0u)
+      xe = __hip_atomic_load(&p.hdr->xerr_epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (p.has_hdr || p.self_scales)
+      D_hdr = __hip_atomic_load(&p.hdr->D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   double ce = 0.0, zl = 0.0;
   int64_t ok = 0, cnt = 0;
-  // kEpiUnroll rows per thread in flight (the loads are device-coherent, so
-  // each has the full memory latency); the sums still run in row order.
-  constexpr int kEpiUnroll = 8;
-  for (int64_t r0 = tid; r0 < p.rows; r0 += static_cast<int64_t>(BLOCK) * kEpiUnroll) {
+  constexpr int kEpiUnroll = UNROLL;
+  constexpr int64_t kRound = static_cast<int64_t>(BLOCK) * kEpiUnroll;
+  for (int64_t rb = 0; rb < p.rows; rb += kRound) {
+    // a uniform base per round and one 32-bit index per row, shared by the
+    // three arrays (a scalar base plus a vector offset per load)
+    const int nr = static_cast<int>(p.rows - rb < kRound ? p.rows - rb : kRound);
+    const float* bce = p.row_ce + rb;
+    const float* bz = p.row_z + rb;
+    const int32_t* bok = p.row_ok + rb;
     float vce[kEpiUnroll], vz[kEpiUnroll];
     int32_t vf[kEpiUnroll];
 #pragma unroll
     for (int u = 0; u < kEpiUnroll; ++u) {
-      const int64_t r = r0 + static_cast<int64_t>(u) * BLOCK;
-      const bool in = r < p.rows;
-      vce[u] = in ? __hip_atomic_load(p.row_ce + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                  : 0.0f;
-      vz[u] = in ? __hip_atomic_load(p.row_z + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                 : 0.0f;
-      vf[u] = in ? __hip_atomic_load(p.row_ok + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+      const int i = tid + u * BLOCK;
+      const uint32_t ic = static_cast<uint32_t>(i < nr ? i : nr - 1);
+      vce[u] = __hip_atomic_load(bce + ic, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      vz[u] = __hip_atomic_load(bz + ic, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      vf[u] = __hip_atomic_load(bok + ic, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 #pragma unroll
     for (int u = 0; u < kEpiUnroll; ++u) {
-      if (r0 + static_cast<int64_t>(u) * BLOCK < p.rows) {
-        ce += static_cast<double>(vce[u]);
-        zl += static_cast<double>(vz[u]);
-        ok += vf[u] & 1;
-        cnt += (vf[u] >> 1) & 1;
-      }
+      const bool in = tid + u * BLOCK < nr;
+      ce = in ? ce + static_cast<double>(vce[u]) : ce;
+      zl = in ? zl + static_cast<double>(vz[u]) : zl;
+      ok += in ? (vf[u] & 1) : 0;
+      cnt += in ? ((vf[u] >> 1) & 1) : 0;
     }
   }
 #pragma unroll
@@ -477,13 +496,10 @@ __device__ __forceinline__ void epilogue_reduce(const Params& p) {
     }
     // A split row whose exchange gave up in this call poisons the reduced
     // outputs (its own values are NaN already when its part 0 gave up).
-    const bool xfail = p.xstamp != 0u && __hip_atomic_load(&p.hdr->xerr_epoch, __ATOMIC_RELAXED,
-                                                           __HIP_MEMORY_SCOPE_AGENT) == p.xstamp;
+    const bool xfail = p.xstamp != 0u && xe == p.xstamp;
     if (xfail) tce = tz = __builtin_nan("");
     const double n = static_cast<double>(ncount);
-    const double D = (p.has_hdr || p.self_scales)
-                         ? __hip_atomic_load(&p.hdr->D, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                         : n;
+    const double D = (p.has_hdr || p.self_scales) ? D_hdr : n;
     if (p.reduction == 1) {
       if (p.loss) p.loss[0] = static_cast<float>(tce / D + tz / n);
       if (p.z_loss) p.z_loss[0] = static_cast<float>(tz / n);
@@ -503,12 +519,12 @@ __device__ __forceinline__ void epilogue_reduce(const Params& p) {
 
 // The last block's work: the reduction, or with no_reduce only the reset of
 // the arrival counter (the per-row values stay for a later reduction).
-template <int BLOCK>
+template <int BLOCK, int UNROLL = 8>
 __device__ __forceinline__ void epilogue_finish(const Params& p) {
   if (p.no_reduce) {
     if (threadIdx.x == 0) p.hdr->done = 0u;
   } else {
-    epilogue_reduce<BLOCK>(p);
+    epilogue_reduce<BLOCK, UNROLL>(p);
   }
 }
 

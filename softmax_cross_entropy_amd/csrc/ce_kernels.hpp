@@ -868,7 +868,9 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(
   if (p.epilogue) {
     if (threadIdx.x == 0) s_last = arrive(p, static_cast<uint32_t>(G));
     __syncthreads();
-    if (s_last) epilogue_finish<BLOCK>(p);
+    // 16 rows per thread in flight where the row loop's registers leave room
+    // (4096 rows on 256 threads in one round of loads)
+    if (s_last) epilogue_finish<BLOCK, DYN ? 16 : 8>(p);
   }
 }
 
