@@ -387,6 +387,9 @@ SHAPE_CASES = [
     (torch.float32, 65001, 300, dict(weight=True, eps=0.05)),         # 512 x 16 pair / 512 x 32
     (torch.float32, 129001, 300, dict(lam=1e-4)),                     # quarters / 1024 x 16 pair
     (torch.bfloat16, 16001, 2600, dict(softcap=20.0)),                # 256 x 8
+    # 256 x 16 with rows claimed: the last block reduces 16 rows per thread per
+    # round, so 4500 rows take a full round of 4096 and a ragged one
+    (torch.bfloat16, 32001, 4500, dict(eps=0.05, lam=1e-4)),          # 256 x 16 / 1024 x 4
     (torch.bfloat16, 65001, 600, dict()),                             # 512 x 8 pair / 512 x 16
     (torch.bfloat16, 131001, 300, dict(weight=True, eps=0.1, softcap=30.0, lam=1e-4)),
     # the largest shapes with every per-element option (fewer rows: oracle time)
