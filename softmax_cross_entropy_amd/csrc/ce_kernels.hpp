@@ -272,10 +272,12 @@ __shared__ double s_self_scales[3];
 // fixed order in every workgroup, so all get the same bits) and keeps the
 // mean scales in LDS; workgroup 0 also stores D, n and the scales in the
 // header for the epilogue (device-scope stores, complete before its arrival).
-template <int BLOCK>
+// UNROLL targets per thread are in flight at once: 16 where the kernel has
+// registers to spare (the order of the sums does not depend on it).
+template <int BLOCK, int UNROLL = 8>
 __device__ __forceinline__ void compute_self_scales(const Params& p) {
   constexpr int NW = BLOCK / 64;
-  constexpr int kU = 8;
+  constexpr int kU = UNROLL;
   __shared__ double s_D[NW];
   __shared__ int64_t s_n[NW];
   const int tid = threadIdx.x;
@@ -283,10 +285,26 @@ __device__ __forceinline__ void compute_self_scales(const Params& p) {
   int64_t n = 0;
   for (int64_t r0 = tid; r0 < p.rows; r0 += static_cast<int64_t>(BLOCK) * kU) {
     int64_t yv[kU];
+    if constexpr (UNROLL > 8) {
+      // one round of loads for 16 rows per thread (4096 rows on 256 threads
+      // at once), indexes clamped instead of branched on; rows past the end
+      // count as ignored
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int64_t r = r0 + static_cast<int64_t>(u) * BLOCK;
-      yv[u] = r < p.rows ? p.target[r] : p.ignore_index;
+      for (int u = 0; u < kU; ++u) {
+        const int64_t r = r0 + static_cast<int64_t>(u) * BLOCK;
+        yv[u] = p.target[r < p.rows - 1 ? r : p.rows - 1];
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int64_t r = r0 + static_cast<int64_t>(u) * BLOCK;
+        yv[u] = r < p.rows ? yv[u] : p.ignore_index;
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int64_t r = r0 + static_cast<int64_t>(u) * BLOCK;
+        yv[u] = r < p.rows ? p.target[r] : p.ignore_index;
+      }
     }
     float wv[kU];
 #pragma unroll
@@ -512,7 +530,7 @@ struct RowClaim {
 
 template <class E, int BLOCK, int NREG, int SC, int SM, bool DYN>
 __device__ __forceinline__ void fused_row(const Params& p, int64_t row, int64_t y,
-                                          RowShared<BLOCK>& sh) {
+                                          RowShared<BLOCK>& sh, uint32_t* arrival = nullptr) {
   constexpr int EPV = E::EPV;
   constexpr int NS = NREG;
   constexpr int NW = BLOCK / 64;
@@ -768,6 +786,20 @@ __device__ __forceinline__ void fused_row(const Params& p, int64_t row, int64_t 
   if (tid == 0 && p.epilogue) {
     const RowScalars& rs = sh.rs;
     publish_row(p, row, rs.ce, rs.zl, rs.ok, 1);
+    if constexpr (DYN) {
+      // The workgroup's last row: it arrives once this row's values are
+      // stored, and the arrival's round trip overlaps the gradient stores
+      // below (the result is read after them). The address carries an
+      // opaque per-lane zero, so the atomic stays a one-lane one whose
+      // result is not waited for here.
+      if (sh.next_row >= p.rows) {
+        __builtin_amdgcn_s_waitcnt(0);
+        int zero = 0;
+        asm volatile("" : "+v"(zero));
+        *arrival = __hip_atomic_fetch_add(&p.hdr->done + zero, 1u, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
   }
 
   // ---- pass 2: gradient from on-chip data, written over the logits ----
@@ -840,12 +872,15 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(
   const int64_t G = gridDim.x;
   // self_scales: every workgroup counts n and D once, before its rows (kept
   // out of the row loop, whose registers it would otherwise crowd)
-  if (p.self_scales) compute_self_scales<BLOCK>(p);
+  if (p.self_scales) compute_self_scales<BLOCK, DYN ? 16 : 8>(p);
+  // thread 0: the arrival count returned when the workgroup arrived with its
+  // last row (claimed rows), else ~0
+  uint32_t arrival = ~0u;
   if constexpr (DYN) {
     int64_t row = blockIdx.x;
     int64_t y = p.target[row];
     while (true) {
-      fused_row<E, BLOCK, NREG, SC, SM, true>(p, row, y, sh);
+      fused_row<E, BLOCK, NREG, SC, SM, true>(p, row, y, sh, &arrival);
       row = uniform_i64(sh.next_row);
       y = uniform_i64(sh.next_y);
       if (row >= p.rows) break;
@@ -866,7 +901,9 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(
     }
   }
   if (p.epilogue) {
-    if (threadIdx.x == 0) s_last = arrive(p, static_cast<uint32_t>(G));
+    if (threadIdx.x == 0)
+      s_last = arrival != ~0u ? arrival == static_cast<uint32_t>(G) - 1u
+                              : arrive(p, static_cast<uint32_t>(G));
     __syncthreads();
     // 16 rows per thread in flight where the row loop's registers leave room
     // (4096 rows on 256 threads in one round of loads)
