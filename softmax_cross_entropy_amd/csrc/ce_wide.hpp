@@ -219,7 +219,8 @@ template <class E, int BLOCK, int NREG, int PARTS, int SC, int SM, int GB = 0>
 __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
                                           WideShared<BLOCK>& sh, int64_t& next_t,
                                           int64_t& next_y, const float* gscale = nullptr,
-                                          int gscale_per_row = 0) {
+                                          int gscale_per_row = 0,
+                                          uint32_t* arrival = nullptr) {
   constexpr int NW = BLOCK / 64;
   constexpr int EPV = E::EPV;
   constexpr int GS = (EPV == 4) ? 4 : 2;  // slots per pass-1 group
@@ -659,6 +660,23 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
     // before the next part's loads could go out.
     next_t = uniform_i64(sh.next_t);
     next_y = uniform_i64(sh.next_y);
+    // fp32: the workgroup's last part arrives at the epilogue's counter now
+    // (this part's row values, if any, are stored), and the arrival's round
+    // trip overlaps the gradient stores below (the result is read after
+    // them). The address carries an opaque per-lane zero, so the atomic
+    // stays a one-lane one whose result is not waited for here. (The check
+    // in every part measured slower on the bf16 kernels, whose workgroups
+    // run many more parts at the benchmarked sizes.)
+    if constexpr (E::EPV == 4) {
+      if (arrival != nullptr && p.epilogue && tid == 0 &&
+          next_t >= (PARTS > 1 ? p.rows : p.rows * PARTS)) {
+        __builtin_amdgcn_s_waitcnt(0);
+        int zero = 0;
+        asm volatile("" : "+v"(zero));
+        *arrival = __hip_atomic_fetch_add(&p.hdr->done + zero, 1u, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
 
     // ---- pass 2: the gradient from on-chip data, written over the logits ----
     // (part 0 of a row whose exchange gave up, argmax -1, writes NaN over the
@@ -749,6 +767,9 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
   // (kept out of the part loop, whose registers it would otherwise crowd)
   if (p.self_scales) compute_self_scales<BLOCK>(p);
   if (threadIdx.x == 0) sh.limit = p.spin_limit > 0 ? p.spin_limit : kGroupSpinLimit;
+  // thread 0: the arrival count returned when the workgroup arrived with its
+  // last part, else ~0
+  uint32_t arrival = ~0u;
   if constexpr (PARTS > 1) {
     // group j = workgroups G j ... G j + G - 1 starts with row j (the grid
     // holds at most one group per row)
@@ -757,7 +778,8 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
     int64_t y = p.target[row];
     while (row < p.rows) {
       int64_t nr, ny;
-      wide_part<E, BLOCK, NREG, PARTS, SC, SM>(p, PARTS * row + h, y, sh, nr, ny);
+      wide_part<E, BLOCK, NREG, PARTS, SC, SM>(p, PARTS * row + h, y, sh, nr, ny, nullptr, 0,
+                                               &arrival);
       row = nr;
       y = ny;
     }
@@ -767,13 +789,14 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
     int64_t y = p.target[t];
     while (t < parts) {
       int64_t nt, ny;
-      wide_part<E, BLOCK, NREG, PARTS, SC, SM>(p, t, y, sh, nt, ny);
+      wide_part<E, BLOCK, NREG, PARTS, SC, SM>(p, t, y, sh, nt, ny, nullptr, 0, &arrival);
       t = nt;
       y = ny;
     }
   }
   if (p.epilogue) {
-    if (threadIdx.x == 0) s_last = arrive(p, gridDim.x);
+    if (threadIdx.x == 0)
+      s_last = arrival != ~0u ? arrival == gridDim.x - 1u : arrive(p, gridDim.x);
     __syncthreads();
     if (s_last) epilogue_finish<BLOCK>(p);
   }
