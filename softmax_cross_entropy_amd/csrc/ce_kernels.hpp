@@ -39,6 +39,7 @@ constexpr int kStoreNT = 2;  // non-temporal store (streaming gradient)
 constexpr int kLoadNT = 2;   // non-temporal load (each logit is read once)
 // s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt left at their maxima
 constexpr int kWaitVmcnt0 = 0x0F70;
+constexpr int kWaitVmcnt8 = 0x0F78;  // vmcnt(8), the other counters not waited on
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int nvec) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),

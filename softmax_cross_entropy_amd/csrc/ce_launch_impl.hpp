@@ -82,18 +82,41 @@ hipError_t launch_fused(int shape, const Params& p, hipStream_t st) {
 // at most one workgroup per part; rows split over G parts take a multiple
 // of G workgroups (fixed groups G j ... G j + G - 1), at least one group,
 // balanced over rows like the row kernel.
-template <class E, int BLOCK, int NREG, int PARTS, int SC, int SM>
-hipError_t launch_wide_t(const Params& p, hipStream_t st) {
+template <class E, int BLOCK, int NREG, int PARTS, int SC, int SM, int PF>
+hipError_t launch_wide_inst(const Params& p, hipStream_t st) {
   static int cache[64] = {};
   int r = 0;
   const hipError_t e =
-      resident_blocks(cedev::wide_kernel<E, BLOCK, NREG, PARTS, SC, SM>, BLOCK, cache, &r);
+      resident_blocks(cedev::wide_kernel<E, BLOCK, NREG, PARTS, SC, SM, PF>, BLOCK, cache, &r);
   if (e != hipSuccess) return e;
   const int64_t groups = balanced_grid(p.rows, r / PARTS);
   const int64_t grid = (groups > 0 ? groups : 1) * PARTS;
-  cedev::wide_kernel<E, BLOCK, NREG, PARTS, SC, SM>
+  cedev::wide_kernel<E, BLOCK, NREG, PARTS, SC, SM, PF>
       <<<dim3(static_cast<unsigned>(grid)), BLOCK, 0, st>>>(p);
   return hipGetLastError();
+}
+
+// Quarter rows: with at most kPrefetchRowsPerGroup rows per group of four
+// resident workgroups, the instance that loads kPrefetchSlots slots of each
+// workgroup's next part into LDS during its exchange (measured on MI355X at
+// 128256 fp32 columns: 4 % faster up to 32 rows per group, slower from 48,
+// where the prefetch's code costs more in the steady state than it saves at
+// the start and end of the launch).
+constexpr int kPrefetchSlots = 4;
+constexpr int64_t kPrefetchRowsPerGroup = 32;
+
+template <class E, int BLOCK, int NREG, int PARTS, int SC, int SM>
+hipError_t launch_wide_t(const Params& p, hipStream_t st) {
+  if constexpr (PARTS == 4 && BLOCK == 512 && NREG > 8) {
+    static int cache[64] = {};
+    int r = 0;
+    const hipError_t e = resident_blocks(
+        cedev::wide_kernel<E, BLOCK, NREG, PARTS, SC, SM, kPrefetchSlots>, BLOCK, cache, &r);
+    if (e != hipSuccess) return e;
+    if (p.rows <= kPrefetchRowsPerGroup * (r / PARTS))
+      return launch_wide_inst<E, BLOCK, NREG, PARTS, SC, SM, kPrefetchSlots>(p, st);
+  }
+  return launch_wide_inst<E, BLOCK, NREG, PARTS, SC, SM, 0>(p, st);
 }
 
 template <class E, int BLOCK, int NREG, int PARTS>

@@ -8,6 +8,7 @@ configuration, automatic path) compare every row's gradient except at
 16384 x 262144, where a seeded sample of rows is compared.
 """
 
+import dataclasses
 import math
 
 import numpy as np
@@ -652,7 +653,7 @@ def _sample_rows(rows, k, seed, extra=()):
 
 
 def _full_workload(name, grad_sample=None):
-    w = synth.WORKLOADS[name]
+    w = synth.WORKLOADS[name] if isinstance(name, str) else name
     for red in w.reductions:
         _announce(name=w.name, rows=w.rows, V=w.V, dtype=w.dtype, reduction=red)
         inp = synth.make_inputs(w, DEV)
@@ -707,3 +708,15 @@ def test_full_c4_bf16_all_options():
 
 def test_full_c5_bf16_huge():
     _full_workload("ce_16384x262144_bf16", grad_sample=512)
+
+
+def test_quarter_rows_many_rows_per_group_f32():
+    """fp32 rows of 16400 vectors (quarter rows) in a batch of 4200: more than
+    32 rows per group of four resident workgroups, so the launch takes the
+    kernel instance without the LDS prefetch of the next part (the headline's
+    1023 rows take the one with it); every row's scalars and argmax, and a
+    sample of gradients, against the oracle."""
+    base = synth.WORKLOADS["ce_1023x128256_f32"]
+    w = dataclasses.replace(base, name="ce_4200x65600_f32", rows=4200, V=65600,
+                            reductions=("mean",))
+    _full_workload(w, grad_sample=256)
