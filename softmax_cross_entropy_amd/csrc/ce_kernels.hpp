@@ -531,8 +531,13 @@ struct RowClaim {
 
 template <class E, int BLOCK, int NREG, int SC, int SM, bool DYN>
 __device__ __forceinline__ void fused_row(const Params& p, int64_t row, int64_t y,
-                                          RowShared<BLOCK>& sh, uint32_t* arrival = nullptr) {
+                                          RowShared<BLOCK>& sh, uint32_t* arrival = nullptr,
+                                          int64_t* pf_row = nullptr) {
   constexpr int EPV = E::EPV;
+  // Claimed rows: PF slots of the next row are loaded into LDS while this
+  // row's gradient is computed and stored (see before pass 2).
+  constexpr int PF = DYN ? 4 : 0;
+  __shared__ u4 s_pfr[PF > 0 ? PF * BLOCK : 1];
   constexpr int NS = NREG;
   constexpr int NW = BLOCK / 64;
   constexpr bool KEEP_E = (EPV == 4) && !SC;
@@ -592,9 +597,28 @@ __device__ __forceinline__ void fused_row(const Params& p, int64_t row, int64_t 
   const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(rp, nv);
   const int voff = tid * 16;
   u4 r[NREG];
+  bool from_lds = false;
+  if constexpr (PF > 0) from_lds = pf_row != nullptr && *pf_row == row;
+  if (from_lds) {
+    // The row's first PF slots are in LDS, each thread's own vectors (loaded
+    // by its own lane). The row before stored at least 9 slots after issuing
+    // them, so at most 8 operations of this wave in flight means they have
+    // landed (without gradient stores: none in flight).
+    if (p.grad) {
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt8);
+    } else {
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int k = 0; k < NREG; ++k)
-    r[k] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, k * BLOCK * 16, kLoadNT);
+    for (int k = 0; k < NREG; ++k)
+      r[k] = k < PF ? s_pfr[k * BLOCK + tid]
+                    : __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, k * BLOCK * 16, kLoadNT);
+  } else {
+#pragma unroll
+    for (int k = 0; k < NREG; ++k)
+      r[k] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, k * BLOCK * 16, kLoadNT);
+  }
   // ---- pass 1 ----
   // Thread state: (tm, ts) = max of z and sum of exp(z - tm), tsz = smoothing
   // sum, tb = raw maximum and tg = first group holding it (NG: the tail).
@@ -803,6 +827,28 @@ __device__ __forceinline__ void fused_row(const Params& p, int64_t row, int64_t 
     }
   }
 
+  // The next row is claimed and its target known: the first PF slots of it
+  // go to LDS now (buffer loads that write LDS directly, so no registers),
+  // and HBM keeps reading while this row's gradient is computed and stored.
+  // Counted rows only (an ignored row is never read), of more than 8 slots
+  // (the wait above counts on at least 9 gradient stores after these loads).
+  if constexpr (PF > 0) {
+    if (pf_row != nullptr) {
+      *pf_row = -1;
+      const int64_t nrow = sh.next_row;
+      const int64_t nyv = sh.next_y;
+      if (nrow < p.rows && nyv != p.ignore_index && nyv >= 0 && nyv < p.V && nv > 8 * BLOCK) {
+        const __amdgpu_buffer_rsrc_t rn = make_rsrc(row_ptr(p, nrow, E::BYTES), nv);
+#pragma unroll
+        for (int k = 0; k < PF; ++k)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rn, (__attribute__((address_space(3))) void*)(&s_pfr[k * BLOCK + wave * 64]), 16,
+              voff, k * BLOCK * 16, 0, 0);
+        *pf_row = nrow;
+      }
+    }
+  }
+
   // ---- pass 2: gradient from on-chip data, written over the logits ----
   if (p.grad) {
     const RowScalars rs = sh.rs;
@@ -877,11 +923,12 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(
   // thread 0: the arrival count returned when the workgroup arrived with its
   // last row (claimed rows), else ~0
   uint32_t arrival = ~0u;
+  int64_t pf_row = -1;  // the row whose first slots the LDS prefetch holds, or -1
   if constexpr (DYN) {
     int64_t row = blockIdx.x;
     int64_t y = p.target[row];
     while (true) {
-      fused_row<E, BLOCK, NREG, SC, SM, true>(p, row, y, sh, &arrival);
+      fused_row<E, BLOCK, NREG, SC, SM, true>(p, row, y, sh, &arrival, &pf_row);
       row = uniform_i64(sh.next_row);
       y = uniform_i64(sh.next_y);
       if (row >= p.rows) break;
