@@ -96,18 +96,22 @@ hipError_t launch_wide_inst(const Params& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Quarter rows: with at most kPrefetchRowsPerGroup rows per group of four
-// resident workgroups, the instance that loads kPrefetchSlots slots of each
-// workgroup's next part into LDS during its exchange (measured on MI355X at
-// 128256 fp32 columns: 4 % faster up to 32 rows per group, slower from 48,
-// where the prefetch's code costs more in the steady state than it saves at
-// the start and end of the launch).
+// Split rows on 512-thread workgroups of 16 slots: with at most
+// kPrefetchRowsPerGroup rows per group of resident workgroups, the instance
+// that loads kPrefetchSlots slots of each workgroup's next part into LDS
+// during its exchange and gradient pass. Measured on MI355X: quarter rows
+// 4 % faster up to 32 rows per group at 128256 fp32 columns and slower from
+// 48 (the prefetch's code then costs more in the steady state than it saves
+// at the ends of the launch); row pairs 2-7 % faster up to 16-48 rows per
+// group and 1.6 % slower at 64 (16384 x 65536 fp32), and 4 % slower with a
+// softcap and smoothing together (4096 x 131072 bf16 with every option,
+// where the vector ALU is the bound), so those pairs keep the plain kernel.
 constexpr int kPrefetchSlots = 4;
 constexpr int64_t kPrefetchRowsPerGroup = 32;
 
 template <class E, int BLOCK, int NREG, int PARTS, int SC, int SM>
 hipError_t launch_wide_t(const Params& p, hipStream_t st) {
-  if constexpr (PARTS == 4 && BLOCK == 512 && NREG > 8) {
+  if constexpr ((PARTS == 4 || (PARTS == 2 && !(SC && SM))) && BLOCK == 512 && NREG > 8) {
     static int cache[64] = {};
     int r = 0;
     const hipError_t e = resident_blocks(
