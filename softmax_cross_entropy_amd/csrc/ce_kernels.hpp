@@ -534,9 +534,12 @@ __device__ __forceinline__ void fused_row(const Params& p, int64_t row, int64_t 
                                           RowShared<BLOCK>& sh, uint32_t* arrival = nullptr,
                                           int64_t* pf_row = nullptr) {
   constexpr int EPV = E::EPV;
-  // Claimed rows: PF slots of the next row are loaded into LDS while this
-  // row's gradient is computed and stored (see before pass 2).
-  constexpr int PF = DYN ? 4 : 0;
+  // Claimed fp32 rows: PF slots of the next row are loaded into LDS while
+  // this row's gradient is computed and stored (see before pass 2). (bf16
+  // rows measured faster with it only when every launch starts from caches
+  // flushed of the previous launch's writes, and slower back to back, so
+  // they keep loading every slot from HBM.)
+  constexpr int PF = (DYN && EPV == 4) ? 4 : 0;
   __shared__ u4 s_pfr[PF > 0 ? PF * BLOCK : 1];
   constexpr int NS = NREG;
   constexpr int NW = BLOCK / 64;

@@ -82,45 +82,18 @@ hipError_t launch_fused(int shape, const Params& p, hipStream_t st) {
 // at most one workgroup per part; rows split over G parts take a multiple
 // of G workgroups (fixed groups G j ... G j + G - 1), at least one group,
 // balanced over rows like the row kernel.
-template <class E, int BLOCK, int NREG, int PARTS, int SC, int SM, int PF>
-hipError_t launch_wide_inst(const Params& p, hipStream_t st) {
+template <class E, int BLOCK, int NREG, int PARTS, int SC, int SM>
+hipError_t launch_wide_t(const Params& p, hipStream_t st) {
   static int cache[64] = {};
   int r = 0;
   const hipError_t e =
-      resident_blocks(cedev::wide_kernel<E, BLOCK, NREG, PARTS, SC, SM, PF>, BLOCK, cache, &r);
+      resident_blocks(cedev::wide_kernel<E, BLOCK, NREG, PARTS, SC, SM>, BLOCK, cache, &r);
   if (e != hipSuccess) return e;
   const int64_t groups = balanced_grid(p.rows, r / PARTS);
   const int64_t grid = (groups > 0 ? groups : 1) * PARTS;
-  cedev::wide_kernel<E, BLOCK, NREG, PARTS, SC, SM, PF>
+  cedev::wide_kernel<E, BLOCK, NREG, PARTS, SC, SM>
       <<<dim3(static_cast<unsigned>(grid)), BLOCK, 0, st>>>(p);
   return hipGetLastError();
-}
-
-// Split rows on 512-thread workgroups of 16 slots: with at most
-// kPrefetchRowsPerGroup rows per group of resident workgroups, the instance
-// that loads kPrefetchSlots slots of each workgroup's next part into LDS
-// during its exchange and gradient pass. Measured on MI355X: quarter rows
-// 4 % faster up to 32 rows per group at 128256 fp32 columns and slower from
-// 48 (the prefetch's code then costs more in the steady state than it saves
-// at the ends of the launch); row pairs 2-7 % faster up to 16-48 rows per
-// group and 1.6 % slower at 64 (16384 x 65536 fp32), and 4 % slower with a
-// softcap and smoothing together (4096 x 131072 bf16 with every option,
-// where the vector ALU is the bound), so those pairs keep the plain kernel.
-constexpr int kPrefetchSlots = 4;
-constexpr int64_t kPrefetchRowsPerGroup = 32;
-
-template <class E, int BLOCK, int NREG, int PARTS, int SC, int SM>
-hipError_t launch_wide_t(const Params& p, hipStream_t st) {
-  if constexpr ((PARTS == 4 || (PARTS == 2 && !(SC && SM))) && BLOCK == 512 && NREG > 8) {
-    static int cache[64] = {};
-    int r = 0;
-    const hipError_t e = resident_blocks(
-        cedev::wide_kernel<E, BLOCK, NREG, PARTS, SC, SM, kPrefetchSlots>, BLOCK, cache, &r);
-    if (e != hipSuccess) return e;
-    if (p.rows <= kPrefetchRowsPerGroup * (r / PARTS))
-      return launch_wide_inst<E, BLOCK, NREG, PARTS, SC, SM, kPrefetchSlots>(p, st);
-  }
-  return launch_wide_inst<E, BLOCK, NREG, PARTS, SC, SM, 0>(p, st);
 }
 
 template <class E, int BLOCK, int NREG, int PARTS>

@@ -215,21 +215,17 @@ __device__ __forceinline__ void next_words(const Params& p, uint32_t c, int64_t 
 // 2 e), not as fp32 over the logits. A part writes only after every
 // part of its row has published its partial, i.e. after every logit of the
 // row has been consumed, so the compacted writes never meet a pending read.
-template <class E, int BLOCK, int NREG, int PARTS, int SC, int SM, int GB = 0, int PF = 0>
+template <class E, int BLOCK, int NREG, int PARTS, int SC, int SM, int GB = 0>
 __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
                                           WideShared<BLOCK>& sh, int64_t& next_t,
                                           int64_t& next_y, const float* gscale = nullptr,
                                           int gscale_per_row = 0,
-                                          uint32_t* arrival = nullptr, int64_t* pf_row = nullptr) {
+                                          uint32_t* arrival = nullptr) {
   constexpr int NW = BLOCK / 64;
   constexpr int EPV = E::EPV;
   constexpr int GS = (EPV == 4) ? 4 : 2;  // slots per pass-1 group
   constexpr int NG = NREG / GS;
   constexpr bool KEEP_E = (EPV == 4) && !SC;
-  static_assert(PF == 0 || (PARTS > 1 && PF < NREG), "prefetch: split rows only");
-  // PF slots of the group's next row are loaded into LDS during this part's
-  // exchange and gradient (see below)
-  __shared__ u4 s_pf[PF > 0 ? PF * BLOCK : 1];
   Acc* s_acc = sh.acc;
   int* s_cand = sh.cand;
 
@@ -335,28 +331,9 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
     const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(hp, nv);
     const int voff = tid * 16;
     u4 r[NREG];
-    bool from_lds = false;
-    if constexpr (PF > 0) from_lds = *pf_row == row;
-    if (from_lds) {
-      // This part's first PF slots are in LDS, each thread's own vectors
-      // (loaded by its own lane). The part before stored at least 9 slots
-      // after issuing them, so at most 8 operations of this wave still in
-      // flight means they have landed (without gradient stores: all of them).
-      if (p.grad) {
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt8);
-      } else {
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int k = 0; k < NREG; ++k)
-        r[k] = k < PF ? s_pf[k * BLOCK + tid]
-                      : __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, k * BLOCK * 16, kLoadNT);
-    } else {
-#pragma unroll
-      for (int k = 0; k < NREG; ++k)
-        r[k] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, k * BLOCK * 16, kLoadNT);
-    }
+    for (int k = 0; k < NREG; ++k)
+      r[k] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, k * BLOCK * 16, kLoadNT);
     int64_t ny = 0;  // target of the group's next row (part 0, thread 0)
     if constexpr (PARTS > 1) {
       if (tid == 0 && h == 0) ny = group_target<PARTS>(p, claim);
@@ -683,28 +660,6 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
     // before the next part's loads could go out.
     next_t = uniform_i64(sh.next_t);
     next_y = uniform_i64(sh.next_y);
-    if constexpr (PF > 0) {
-      // The group's next row is known: the first PF slots of this
-      // workgroup's part of it go to LDS now (buffer loads that write LDS
-      // directly, so no registers), while this part's gradient is computed
-      // and stored; HBM keeps streaming through the exchanges. Counted rows
-      // only (an ignored row is never read), not after a failed exchange, and
-      // only for parts of more than 8 slots (the wait above counts on at
-      // least 9 gradient stores after these loads).
-      *pf_row = -1;
-      const bool counted_next =
-          next_t < p.rows && next_y != p.ignore_index && next_y >= 0 && next_y < p.V;
-      if (counted_next && sh.rs.arg >= 0 && nv > 8 * BLOCK) {
-        char* np = row_ptr(p, next_t, E::BYTES) + static_cast<int64_t>(v0) * 16;
-        const __amdgpu_buffer_rsrc_t rn = make_rsrc(np, nv);
-#pragma unroll
-        for (int k = 0; k < PF; ++k)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              rn, (__attribute__((address_space(3))) void*)(&s_pf[k * BLOCK + wave * 64]), 16,
-              voff, k * BLOCK * 16, 0, 0);
-        *pf_row = next_t;
-      }
-    }
     // fp32: the workgroup's last part arrives at the epilogue's counter now
     // (this part's row values, if any, are stored), and the arrival's round
     // trip overlaps the gradient stores below (the result is read after
@@ -802,7 +757,7 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
 // stores are (they drain while the next part arrives).
 // Four waves per SIMD: one 1024-thread workgroup or two 512-thread ones per
 // CU, so at most 128 VGPRs.
-template <class E, int BLOCK, int NREG, int PARTS, int SC, int SM, int PF = 0>
+template <class E, int BLOCK, int NREG, int PARTS, int SC, int SM>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void wide_kernel(
     Params p) {
   static_assert(PARTS == 1 || PARTS == 2 || PARTS == 4, "whole, half or quarter rows");
@@ -815,7 +770,6 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
   // thread 0: the arrival count returned when the workgroup arrived with its
   // last part, else ~0
   uint32_t arrival = ~0u;
-  int64_t pf_row = -1;  // the row whose part the LDS prefetch holds, or -1
   if constexpr (PARTS > 1) {
     // group j = workgroups G j ... G j + G - 1 starts with row j (the grid
     // holds at most one group per row)
@@ -824,8 +778,8 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
     int64_t y = p.target[row];
     while (row < p.rows) {
       int64_t nr, ny;
-      wide_part<E, BLOCK, NREG, PARTS, SC, SM, 0, PF>(p, PARTS * row + h, y, sh, nr, ny, nullptr,
-                                                      0, &arrival, &pf_row);
+      wide_part<E, BLOCK, NREG, PARTS, SC, SM>(p, PARTS * row + h, y, sh, nr, ny, nullptr, 0,
+                                               &arrival);
       row = nr;
       y = ny;
     }

@@ -711,11 +711,10 @@ def test_full_c5_bf16_huge():
 
 
 def test_quarter_rows_many_rows_per_group_f32():
-    """fp32 rows of 16400 vectors (quarter rows) in a batch of 4200: more than
-    32 rows per group of four resident workgroups, so the launch takes the
-    kernel instance without the LDS prefetch of the next part (the headline's
-    1023 rows take the one with it); every row's scalars and argmax, and a
-    sample of gradients, against the oracle."""
+    """fp32 rows of 16400 vectors (quarter rows) in a batch of 4200, about 33
+    rows per group of four resident workgroups (the headline batch has 8):
+    every row's scalars and argmax, and a sample of gradients, against the
+    oracle."""
     base = synth.WORKLOADS["ce_1023x128256_f32"]
     w = dataclasses.replace(base, name="ce_4200x65600_f32", rows=4200, V=65600,
                             reductions=("mean",))
