@@ -330,6 +330,33 @@ def test_backward_recompute(opt, dtype, reduction, go, fwd_path, layout):
     assert_grad_close(g, ref.grad * scale, ref.mag * np.abs(scale), zero_rows=ref.not_counted)
 
 
+@pytest.mark.parametrize("reduction", ["mean", "sum"])
+def test_nograd_forward_claimed_rows_f32(reduction):
+    """The forward without the gradient on fp32 rows of 12000 classes (the
+    claimed-row kernel, 256 x 16 slots, more rows than workgroups, so rows
+    follow one another on a workgroup): every scalar output against the
+    oracle, and the logits untouched."""
+    rows, V = 1600, 12000
+    x = synth.make_logits(rows, V, torch.float32, 2.5, 41)
+    t = synth.make_targets(rows, V, 41, rows // 10)
+    _announce(name="nograd-claimed-f32", rows=rows, V=V, reduction=reduction)
+    xd = x.to(DEV)
+    x_before = xd.clone()
+    loss, z, acc, arg, counts = forward_raw(xd, t.to(DEV), None, -100, 0.1, 1e-3, None, reduction,
+                                            grad=False, z_loss=True, token_accuracy=True,
+                                            argmax=True, counts=True)
+    torch.cuda.synchronize()
+    assert torch.equal(xd, x_before)
+    ref = OracleRef(host_logits(x), t.numpy(), label_smoothing=0.1, lse_square_scale=1e-3,
+                    reduction=reduction)
+    assert_loss_close(loss.cpu().numpy(), ref.loss, "loss")
+    assert_loss_close(z.cpu().numpy(), ref.z_loss, "z_loss")
+    np.testing.assert_array_equal(arg.cpu().numpy(), ref.argmax)
+    c = counts.cpu().numpy()
+    assert int(c[0]) == ref.summ.n and int(c[1]) == ref.n_correct
+    assert_acc_exact(acc.item(), ref.n_correct, ref.summ.n)
+
+
 def test_keep_logits_autograd_matches_inplace():
     import softmax_cross_entropy_amd as sce
     rows, V = 300, 8200
