@@ -68,13 +68,37 @@ __device__ __forceinline__ float zval(const Params& p, float x) {
   }
 }
 
-// Weights of the EPV classes of vector jg (weighted smoothing only).
+// Weights of the EPV classes of vector jg (weighted smoothing only), for
+// paths whose lanes stop at the row's last vector.
 template <class E>
 __device__ __forceinline__ void load_w(const float* w, int64_t jg, float (&wk)[E::EPV]) {
   const f4* wv = reinterpret_cast<const f4*>(w + jg * E::EPV);
 #pragma unroll
   for (int q = 0; q < E::EPV / 4; ++q) {
     const f4 t = wv[q];
+    wk[4 * q + 0] = t[0];
+    wk[4 * q + 1] = t[1];
+    wk[4 * q + 2] = t[2];
+    wk[4 * q + 3] = t[3];
+  }
+}
+
+// A vector's weights in the fused row kernels, whose lanes past the row (or
+// part) run the slot's code with their stores dropped: read through a
+// descriptor over the V weights (rs), at the lane's byte offset voff plus
+// the slot's uniform offset soff, so those lanes get 0 instead of reading
+// past the array, and no per-vector address arithmetic is needed.
+struct WSlot {
+  __amdgpu_buffer_rsrc_t rs;
+  int voff;
+  int soff;
+};
+template <class E>
+__device__ __forceinline__ void load_w(const float*, const WSlot& ws, float (&wk)[E::EPV]) {
+#pragma unroll
+  for (int q = 0; q < E::EPV / 4; ++q) {
+    const f4 t = __builtin_bit_cast(
+        f4, __builtin_amdgcn_raw_buffer_load_b128(ws.rs, ws.voff + 16 * q, ws.soff, 0));
     wk[4 * q + 0] = t[0];
     wk[4 * q + 1] = t[1];
     wk[4 * q + 2] = t[2];
@@ -183,9 +207,10 @@ __device__ __forceinline__ float grad_one(const Params& p, const RowScalars& rs,
 
 // FOLD (bf16 results without smoothing, where it is taken): A p_k as one
 // exponential when A > 0.
-template <class E, int SC, int SM, bool FOLD = false>
+// jg: the vector's index into the weights, or its WSlot.
+template <class E, int SC, int SM, bool FOLD = false, class J = int64_t>
 __device__ __forceinline__ u4 grad_vec(const Params& p, const RowScalars& rs, const u4 v,
-                                       int64_t jg, int yi) {
+                                       const J& jg, int yi) {
   constexpr int EPV = E::EPV;
   float f[EPV], wk[EPV];
   E::unpack(v, f);
@@ -408,9 +433,9 @@ __device__ __forceinline__ float vec_max(const float (&f)[EPV]) {
 // Gradient of one fp32 vector from its stored exponentials e = 2^((x - m_g) log2 e):
 // p_k = e sc / A with sc = A 2^((m_g - m) log2 e - log2 s), so
 // g = e sc - B w_k - C [k = y].
-template <int SM>
+template <int SM, class J = int64_t>
 __device__ __forceinline__ u4 grad_vec_e(const Params& p, const RowScalars& rs, const u4 v,
-                                         float sc, int64_t jg, int yi) {
+                                         float sc, const J& jg, int yi) {
   float e[4], g[4];
   F32::unpack(v, e);
   if constexpr (SM) {
@@ -620,6 +645,8 @@ __device__ __forceinline__ void fused_row(const Params& p, int64_t row, int64_t 
   if (tid < tail) xt = E::ld(rp, tail0 + tid);
   const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(rp, nv);
   const int voff = tid * 16;
+  // the class weights of the thread's vectors (weighted smoothing)
+  const WSlot wsl = {make_rsrc_bytes(p.weight, static_cast<int>(p.V) * 4), tid * (EPV * 4), 0};
   u4 r[NREG];
   bool from_lds = false;
   if constexpr (PF > 0) from_lds = pf_row != nullptr && *pf_row == row;
@@ -703,7 +730,7 @@ __device__ __forceinline__ void fused_row(const Params& p, int64_t row, int64_t 
           if constexpr (SM) {
             if (p.weight) {
               float wk[EPV];
-              load_w<E>(p.weight, k * BLOCK + tid, wk);
+              load_w<E>(p.weight, WSlot{wsl.rs, wsl.voff, k * BLOCK * EPV * 4}, wk);
 #pragma unroll
               for (int i = 0; i < EPV; ++i) zs = __builtin_fmaf(wk[i], z[i], zs);
             } else {
@@ -888,9 +915,10 @@ __device__ __forceinline__ void fused_row(const Params& p, int64_t row, int64_t 
             const u4 v = slot(r, k);
             u4 gv;
             if constexpr (KEEP_E) {
-              gv = grad_vec_e<SM>(p, rs, v, sc, k * BLOCK + tid, -1);
+              gv = grad_vec_e<SM>(p, rs, v, sc, WSlot{wsl.rs, wsl.voff, k * BLOCK * 16}, -1);
             } else {
-              gv = grad_vec<E, SC, SM, true>(p, rs, v, k * BLOCK + tid, -1);
+              gv = grad_vec<E, SC, SM, true>(p, rs, v,
+                                             WSlot{wsl.rs, wsl.voff, k * BLOCK * EPV * 4}, -1);
             }
             // lanes past the row are outside the descriptor: the store is dropped
             __builtin_amdgcn_raw_buffer_store_b128(gv, rsrc, voff, k * BLOCK * 16, kStoreNT);

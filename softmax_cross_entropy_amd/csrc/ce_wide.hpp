@@ -330,6 +330,9 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
     }
     const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(hp, nv);
     const int voff = tid * 16;
+    // the class weights of the thread's vectors (weighted smoothing)
+    const WSlot wsl = {make_rsrc_bytes(p.weight, static_cast<int>(p.V) * 4),
+                       (v0 + tid) * (EPV * 4), 0};
     u4 r[NREG];
 #pragma unroll
     for (int k = 0; k < NREG; ++k)
@@ -399,7 +402,7 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
             if constexpr (SM) {
               if (p.weight) {
                 float wk[EPV];
-                load_w<E>(p.weight, v0 + k * BLOCK + tid, wk);
+                load_w<E>(p.weight, WSlot{wsl.rs, wsl.voff, k * BLOCK * EPV * 4}, wk);
 #pragma unroll
                 for (int i = 0; i < EPV; ++i) zs = __builtin_fmaf(wk[i], z[i], zs);
               } else {
@@ -704,9 +707,10 @@ __device__ __forceinline__ void wide_part(const Params& p, int64_t t, int64_t y,
             if (k * BLOCK < nv) {
               u4 gv;
               if constexpr (KEEP_E) {
-                gv = grad_vec_e<SM>(p, rs, r[k], sc, v0 + k * BLOCK + tid, -1);
+                gv = grad_vec_e<SM>(p, rs, r[k], sc, WSlot{wsl.rs, wsl.voff, k * BLOCK * 16}, -1);
               } else {
-                gv = grad_vec<E, SC, SM>(p, rs, r[k], v0 + k * BLOCK + tid, -1);
+                gv = grad_vec<E, SC, SM>(p, rs, r[k], WSlot{wsl.rs, wsl.voff, k * BLOCK * EPV * 4},
+                                         -1);
               }
               // lanes past the part are outside the descriptor: the store is dropped
               if constexpr (GB) {
