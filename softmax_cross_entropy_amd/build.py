@@ -27,7 +27,7 @@ ARCH = "gfx950"
 
 SOURCES = ["ce_api.hip", "ce_linear.hip", "ce_inst_f32.hip", "ce_inst_bf16.hip",
            "ce_inst_f32_wide.hip", "ce_inst_bf16_wide.hip", "ce_inst_f32_gbf16.hip",
-           "ce_stream.hip", "ce_shard.hip"]
+           "ce_inst_nograd.hip", "ce_stream.hip", "ce_shard.hip"]
 # rocBLAS runs the products of the linear layer fused with the cross-entropy.
 LINK_FLAGS = ["-lrocblas", "-Wl,-rpath,/opt/rocm/lib"]
 

@@ -60,6 +60,10 @@ hipError_t launch_wide_bf16(const Shape& s, const cedev::Params& p, hipStream_t 
 bool gbf16_shape(int shape);
 hipError_t launch_wide_gbf16(int shape, const cedev::Params& p, const float* gscale,
                              int per_row, hipStream_t st);
+// nograd_rows_kernel (ce_nograd.hpp): rows of the default split-row shapes
+// when no gradient is asked for, each streamed through one workgroup.
+hipError_t launch_nograd_f32(const cedev::Params& p, hipStream_t st);
+hipError_t launch_nograd_bf16(const cedev::Params& p, hipStream_t st);
 hipError_t launch_forward_f32(const Plan& plan, const cedev::Params& p, hipStream_t st);
 hipError_t launch_forward_bf16(const Plan& plan, const cedev::Params& p, hipStream_t st);
 hipError_t launch_recompute_f32(const cedev::Params& p, void* grad, int64_t grad_stride,

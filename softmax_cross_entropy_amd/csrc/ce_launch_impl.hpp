@@ -68,10 +68,18 @@ hipError_t launch_fused(int shape, const Params& p, hipStream_t st) {
     case 3: return launch_rows<E, SC, SM, 512, 16>(p, st);
     case 4: return launch_rows<E, SC, SM, 512, 32>(p, st);
     case kPair512Shape:
-    case kPair1024Shape:
-    case kWide4Shape:
     case kPair8Shape:
     case kQuadShape:
+      // Without the gradient nothing is written back, so these rows stream
+      // through one workgroup each instead of being split over a group (the
+      // alternative layouts keep the split-row kernels).
+      if (!p.grad) {
+        if constexpr (E::EPV == 4) return launch_nograd_f32(p, st);
+        return launch_nograd_bf16(p, st);
+      }
+      [[fallthrough]];
+    case kPair1024Shape:
+    case kWide4Shape:
       if constexpr (E::EPV == 4) return launch_wide_f32(kShapes[shape], p, st);
       return launch_wide_bf16(kShapes[shape], p, st);
     default: return hipErrorInvalidValue;

@@ -130,6 +130,7 @@ def backward_recompute(x2: torch.Tensor, t: torch.Tensor, weight: Optional[torch
     dev = x2.device
     dt = dtype_code(x2.dtype)
     rows, V = x2.shape
+    _check_grad_output(grad_output, rows, reduction == "none")
     if grad is None:
         grad = torch.empty((rows, V), device=dev, dtype=x2.dtype)
     t = t.to(device=dev, dtype=torch.int64).contiguous()
@@ -146,10 +147,20 @@ def backward_recompute(x2: torch.Tensor, t: torch.Tensor, weight: Optional[torch
     return grad
 
 
+def _check_grad_output(grad_output: torch.Tensor, rows: int, per_row: bool) -> None:
+    """The kernels read one grad_output value, or one per row: any other
+    length is an error here, not a read past the tensor."""
+    want = rows if per_row else 1
+    if grad_output.numel() != want:
+        raise ValueError(f"grad_output must hold {want} value(s) "
+                         f"({'one per row' if per_row else 'a scalar'}), got {grad_output.numel()}")
+
+
 def backward_(grad2: torch.Tensor, grad_output: torch.Tensor, per_row: bool) -> torch.Tensor:
     """In place: grad2 (rows, V) *= grad_output (scalar, or per row)."""
-    go = grad_output.to(device=grad2.device, dtype=torch.float32).contiguous().reshape(-1)
     rows, V = grad2.shape
+    _check_grad_output(grad_output, rows, per_row)
+    go = grad_output.to(device=grad2.device, dtype=torch.float32).contiguous().reshape(-1)
     status = _lib.ce_backward(grad2.data_ptr(), dtype_code(grad2.dtype), rows, V,
                               grad2.stride(0) if rows > 0 else V, go.data_ptr(),
                               1 if per_row else 0, _stream(grad2.device))

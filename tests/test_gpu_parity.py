@@ -357,6 +357,95 @@ def test_nograd_forward_claimed_rows_f32(reduction):
     assert_acc_exact(acc.item(), ref.n_correct, ref.summ.n)
 
 
+# ---------------------------------------------------------------------------
+# The forward without the gradient on the split-row sizes: in the default
+# layout each row streams through one workgroup (no exchange); the
+# alternative layout keeps the split-row kernels. Every scalar output against
+# the oracle, the logits untouched, and the kept per-row (m, log2 s) checked
+# by recomputing the gradient from them.
+# ---------------------------------------------------------------------------
+
+NOGRAD_CASES = [
+    # (dtype, V, rows, options); at least 256 rows (fewer take split-V)
+    (torch.float32, 20001, 300, dict(weight=True, eps=0.1, softcap=15.0, lam=1e-3)),  # pair 512x8
+    (torch.bfloat16, 40003, 300, dict()),                                             # pair 512x8
+    (torch.float32, 50001, 300, dict(eps=0.05)),                                      # pair 512x16
+    (torch.bfloat16, 131001, 280, dict(weight=True, eps=0.1, softcap=30.0, lam=1e-4)),
+    (torch.float32, 128256, 300, dict(specials=True)),                                # quarters
+    (torch.bfloat16, 262001, 260, dict(lam=1e-4, softcap=20.0, specials=True)),       # quarters
+    (torch.float32, 128256, 300, dict(sigma=0.3, tie=1.5)),       # ties in the first and last chunk
+]
+
+
+@pytest.mark.parametrize("case", range(len(NOGRAD_CASES)))
+@pytest.mark.parametrize("reduction", ["mean", "none"])
+@pytest.mark.parametrize("layout", ["fused", "fused_alt"])
+def test_nograd_streamed_rows(case, reduction, layout):
+    dtype, V, rows, o = NOGRAD_CASES[case]
+    seed = 900 + case
+    x = synth.make_logits(rows, V, dtype, o.get("sigma", 2.5), seed)
+    t = synth.make_targets(rows, V, seed, rows // 10)
+    if o.get("tie"):
+        for r in range(rows):
+            x[r, V - 5] = o["tie"]
+            if r % 2 == 0:
+                x[r, 7 + r] = o["tie"]
+        t[1::4] = V - 3
+    if o.get("specials"):
+        g = torch.Generator().manual_seed(seed)
+        cols = lambda k: torch.randperm(V, generator=g)[:k].tolist()  # noqa: E731
+        for r in range(0, rows, 7):
+            kind = (r // 7) % 5
+            if kind == 0:
+                x[r, cols(1)[0]] = float("nan")
+            elif kind == 1:  # a large logit before two NaNs
+                c = sorted(cols(3))
+                x[r, c[0]] = 50.0
+                x[r, c[1]] = float("nan")
+                x[r, c[2]] = float("nan")
+            elif kind == 2:
+                x[r, cols(1)[0]] = float("inf")
+            elif kind == 3:
+                x[r, V - 1] = float("nan")  # in the row tail
+            else:
+                x[r, cols(1)[0]] = float("-inf")
+    wt = None
+    if o.get("weight"):
+        wt = 0.5 + 1.5 * torch.rand(V, generator=torch.Generator().manual_seed(seed))
+    eps, lam, cap = o.get("eps", 0.0), o.get("lam", 0.0), o.get("softcap")
+    stride = (V + 7) // 8 * 8
+    xd = _padded(x, stride)
+    x_before = xd.clone()
+    td = t.to(DEV)
+    wd = None if wt is None else wt.to(DEV)
+    flags = PATH_FLAGS[layout]
+    _announce(name=f"nograd-stream-{case}", rows=rows, V=V, dtype=dtype, reduction=reduction,
+              layout=layout, plan=_plan(xd, wd, eps, flags))
+    stats = torch.empty((rows, 2), device=DEV, dtype=torch.float32)
+    loss, z, acc, arg, counts = forward_raw(xd, td, wd, -100, eps, lam, cap, reduction,
+                                            grad=False, z_loss=True, token_accuracy=True,
+                                            argmax=True, counts=True, row_stats=stats,
+                                            flags=flags)
+    torch.cuda.synchronize()
+    bits = torch.int16 if dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(xd.view(bits), x_before.view(bits))  # only read
+    ref = OracleRef(host_logits(x), t.numpy(), weight=None if wt is None else wt.numpy(),
+                    label_smoothing=eps, lse_square_scale=lam, softcap=cap, reduction=reduction)
+    assert_loss_close(loss.cpu().numpy(), ref.loss, "loss")
+    assert_loss_close(z.cpu().numpy(), ref.z_loss, "z_loss")
+    np.testing.assert_array_equal(arg.cpu().numpy(), ref.argmax)
+    c = counts.cpu().numpy()
+    assert int(c[0]) == ref.summ.n and int(c[1]) == ref.n_correct
+    if reduction == "none":
+        np.testing.assert_array_equal(acc.cpu().numpy(), ref.acc.astype(np.float32))
+    else:
+        assert_acc_exact(acc.item(), ref.n_correct, ref.summ.n)
+    go = torch.ones(rows) if reduction == "none" else torch.tensor(1.0)
+    g = backward_recompute(xd, td, wd, -100, eps, lam, cap, reduction, stats, go.to(DEV))
+    torch.cuda.synchronize()
+    assert_grad_close(g, ref.grad, ref.mag, zero_rows=ref.not_counted)
+
+
 def test_keep_logits_autograd_matches_inplace():
     import softmax_cross_entropy_amd as sce
     rows, V = 300, 8200
