@@ -1459,6 +1459,27 @@ __global__ __launch_bounds__(kBwdBlock) void recompute_kernel(Params p, void* gr
   const char* xp = row_ptr(p, row, E::BYTES);
   char* gp = static_cast<char*>(grad) + row * grad_stride * E::BYTES;
   const float scale = per_row ? go[row] : go[0];
+  // The block's logit loads go out first (they do not depend on the row
+  // scalars), so their latency overlaps thread 0's read of the row's
+  // statistics and the barrier.
+  const int nvec = static_cast<int>(p.V / EPV);
+  const u4* xv = reinterpret_cast<const u4*>(xp);
+  const int j0 = b * kBwdBlock * U;
+  const int64_t tail0 = static_cast<int64_t>(nvec) * EPV;
+  // The owner of the target's vector reads the target logit before any
+  // store (grad may be the logits).
+  const int jy = static_cast<int>(y / EPV);
+  const bool owns_y = VEC && !skip && y < tail0 && jy >= j0 && jy < j0 + kBwdBlock * U &&
+                      (jy - j0) % kBwdBlock == tid;
+  const float xy = owns_y ? E::ld(xp, y) : 0.0f;
+  u4 v[U];
+  if constexpr (VEC) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + u * kBwdBlock + tid;
+      v[u] = (!skip && j < nvec) ? __builtin_nontemporal_load(xv + j) : u4{0u, 0u, 0u, 0u};
+    }
+  }
   if (!skip && tid == 0) {
     double W, alpha, beta;
     load_scales(p, W, alpha, beta);
@@ -1470,23 +1491,7 @@ __global__ __launch_bounds__(kBwdBlock) void recompute_kernel(Params p, void* gr
   __syncthreads();
   const RowScalars rs = s_rs;
   if constexpr (VEC) {
-    const int nvec = static_cast<int>(p.V / EPV);
-    const u4* xv = reinterpret_cast<const u4*>(xp);
     u4* gv = reinterpret_cast<u4*>(gp);
-    const int j0 = b * kBwdBlock * U;
-    const int64_t tail0 = static_cast<int64_t>(nvec) * EPV;
-    // The owner of the target's vector reads the target logit before any
-    // store (grad may be the logits).
-    const int jy = static_cast<int>(y / EPV);
-    const bool owns_y = !skip && y < tail0 && jy >= j0 && jy < j0 + kBwdBlock * U &&
-                        (jy - j0) % kBwdBlock == tid;
-    const float xy = owns_y ? E::ld(xp, y) : 0.0f;
-    u4 v[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = j0 + u * kBwdBlock + tid;
-      v[u] = (!skip && j < nvec) ? __builtin_nontemporal_load(xv + j) : u4{0u, 0u, 0u, 0u};
-    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = j0 + u * kBwdBlock + tid;

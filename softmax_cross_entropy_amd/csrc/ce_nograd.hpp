@@ -22,10 +22,10 @@ namespace cedev {
 // maximum, one (max, sum) combine per group. Each thread keeps the first
 // group holding its raw maximum; the threads holding the row maximum read
 // that group back (one to two vectors) to find its first position, and the
-// block takes the lowest index. The row scalars and outputs are those of
-// fused_row, so the results equal the fused forward's bit for bit where the
-// sums are formed in the same order (they are not: the chunked slots fold
-// in another order, within the sums' rounding).
+// block takes the lowest index. The row scalars and outputs come from the
+// helpers fused_row uses; the per-thread sums take the slots in chunk order,
+// so the losses agree with the fused forward's within the sums' rounding,
+// and the argmax and counts exactly.
 // ---------------------------------------------------------------------------
 template <class E, int BLOCK, int NREG, int SC, int SM>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void nograd_rows_kernel(
