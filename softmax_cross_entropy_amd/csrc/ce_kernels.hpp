@@ -700,6 +700,9 @@ __device__ __forceinline__ void fused_row(const Params& p, int64_t row, int64_t 
       tg = take ? g : tg;
       tb = take ? gx : tb;
       const float zg = zval<SC>(p, __builtin_fmaxf(gx, kLowest));
+      // softcap rows: the exponent t (c log2 e) - zg log2 e as one fma
+      const float zgl = zg * kLog2e;
+      const float cl = p.softcap * kLog2e;
       float gsum = 0.0f;
 #pragma unroll
       for (int q = 0; q < GS; ++q) {
@@ -709,19 +712,18 @@ __device__ __forceinline__ void fused_row(const Params& p, int64_t row, int64_t 
           E::unpack(slot(r, k), f);
           float z[EPV];
           if constexpr (SC) {
-            float u[EPV], t[EPV];
+            float u[EPV];
 #pragma unroll
             for (int i = 0; i < EPV; ++i) u[i] = f[i] * p.inv_softcap;
-            tanh_vec<EPV>(u, t);
-#pragma unroll
-            for (int i = 0; i < EPV; ++i) z[i] = p.softcap * t[i];
+            tanh_vec<EPV>(u, z);  // t = tanh(x / c); z = c t is folded below
           } else {
 #pragma unroll
             for (int i = 0; i < EPV; ++i) z[i] = f[i];
           }
           float e[EPV];
 #pragma unroll
-          for (int i = 0; i < EPV; ++i) e[i] = ex2((z[i] - zg) * kLog2e);
+          for (int i = 0; i < EPV; ++i)
+            e[i] = ex2(SC ? __builtin_fmaf(z[i], cl, -zgl) : (z[i] - zg) * kLog2e);
           if constexpr (KEEP_E) slot(r, k) = F32::pack(e);
           float es = e[0];
 #pragma unroll
@@ -738,6 +740,7 @@ __device__ __forceinline__ void fused_row(const Params& p, int64_t row, int64_t 
               for (int i = 0; i < EPV; ++i) zs += z[i];
             }
           }
+          if constexpr (SC && SM) zs *= p.softcap;  // sum of w t, times c
           if ((k + 1) * BLOCK > nv) {  // lanes past the row add nothing
             asm volatile("");
             const bool ok = k * BLOCK + tid < nv;

@@ -101,6 +101,9 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
           tg = take ? c * NG + g : tg;
           tb = take ? gx : tb;
           const float zg = zval<SC>(p, __builtin_fmaxf(gx, kLowest));
+          // softcap rows: the exponent t (c log2 e) - zg log2 e as one fma
+          const float zgl = zg * kLog2e;
+          const float cl = p.softcap * kLog2e;
           float gsum = 0.0f;
 #pragma unroll
           for (int q = 0; q < GS; ++q) {
@@ -110,19 +113,18 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
               E::unpack(r[g * GS + q], f);
               float z[EPV];
               if constexpr (SC) {
-                float u[EPV], t[EPV];
+                float u[EPV];
 #pragma unroll
                 for (int i = 0; i < EPV; ++i) u[i] = f[i] * p.inv_softcap;
-                tanh_vec<EPV>(u, t);
-#pragma unroll
-                for (int i = 0; i < EPV; ++i) z[i] = p.softcap * t[i];
+                tanh_vec<EPV>(u, z);  // t = tanh(x / c); z = c t is folded below
               } else {
 #pragma unroll
                 for (int i = 0; i < EPV; ++i) z[i] = f[i];
               }
               float es = 0.0f;
 #pragma unroll
-              for (int i = 0; i < EPV; ++i) es += ex2((z[i] - zg) * kLog2e);
+              for (int i = 0; i < EPV; ++i)
+                es += ex2(SC ? __builtin_fmaf(z[i], cl, -zgl) : (z[i] - zg) * kLog2e);
               float zs = 0.0f;
               if constexpr (SM) {
                 if (p.weight) {
@@ -135,6 +137,7 @@ __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(4))) void
                   for (int i = 0; i < EPV; ++i) zs += z[i];
                 }
               }
+              if constexpr (SC && SM) zs *= p.softcap;  // sum of w t, times c
               if ((k + 1) * BLOCK > nv) {  // lanes past the row add nothing
                 const bool ok = k * BLOCK + tid < nv;
                 es = ok ? es : 0.0f;
