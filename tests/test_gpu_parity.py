@@ -409,6 +409,7 @@ def test_nograd_streamed_rows(case, reduction, layout):
                 x[r, V - 1] = float("nan")  # in the row tail
             else:
                 x[r, cols(1)[0]] = float("-inf")
+    t[5] = V + 3  # out of range: NaN loss, not counted, zero recomputed gradient
     wt = None
     if o.get("weight"):
         wt = 0.5 + 1.5 * torch.rand(V, generator=torch.Generator().manual_seed(seed))
@@ -768,10 +769,12 @@ def _sample_rows(rows, k, seed, extra=()):
     return np.array(sorted(s))
 
 
-def _full_workload(name, grad_sample=None):
+def _full_workload(name, grad_sample=None, grad=True):
+    """grad=False: the forward without the gradient (it also saves the per-row
+    statistics), and the gradient recomputed from those is what is compared."""
     w = synth.WORKLOADS[name] if isinstance(name, str) else name
     for red in w.reductions:
-        _announce(name=w.name, rows=w.rows, V=w.V, dtype=w.dtype, reduction=red)
+        _announce(name=w.name, rows=w.rows, V=w.V, dtype=w.dtype, reduction=red, grad=grad)
         inp = synth.make_inputs(w, DEV)
         x = inp.logits
         xh = host_logits(x)  # every row, before the forward overwrites them
@@ -779,10 +782,17 @@ def _full_workload(name, grad_sample=None):
         wh = None if inp.weight is None else inp.weight.cpu().numpy()
         opts = dict(weight=wh, label_smoothing=w.label_smoothing,
                     lse_square_scale=w.lse_square_scale, softcap=w.softcap or None)
+        stats = None if grad else torch.empty((w.rows, 2), device=DEV, dtype=torch.float32)
         loss, z, acc, arg, counts = forward_raw(
             x, inp.target, inp.weight, -100, w.label_smoothing, w.lse_square_scale,
-            w.softcap or None, red, grad=True, z_loss=True, token_accuracy=True, argmax=True,
-            counts=True)
+            w.softcap or None, red, grad=grad, z_loss=True, token_accuracy=True, argmax=True,
+            counts=True, row_stats=stats)
+        gsrc = x
+        if not grad:
+            go = (torch.ones(w.rows, device=DEV) if red == "none"
+                  else torch.tensor(1.0, device=DEV))
+            gsrc = backward_recompute(x, inp.target, inp.weight, -100, w.label_smoothing,
+                                      w.lse_square_scale, w.softcap or None, red, stats, go)
         torch.cuda.synchronize()
         print(f"  gpu done; oracle over {w.rows} rows", flush=True)
         o, summ = oracle_rows(xh, t_host, reduction=red, **opts)
@@ -805,9 +815,9 @@ def _full_workload(name, grad_sample=None):
         for a in range(0, sel.size, 512):
             rr = sel[a:a + 512]
             og, _ = oracle_rows(xh, t_host, reduction=red, want_grad=True, rows=rr, **opts)
-            assert_grad_close(x[torch.from_numpy(rr).to(DEV)], og["grad"], og["mag"],
+            assert_grad_close(gsrc[torch.from_numpy(rr).to(DEV)], og["grad"], og["mag"],
                               zero_rows=~summ.counted[rr], what=f"{w.name} grad rows {rr[0]}..")
-        del inp, x, xh
+        del inp, x, xh, gsrc
 
 
 def test_full_c2_bf16_accuracy_argmax():
@@ -824,6 +834,17 @@ def test_full_c4_bf16_all_options():
 
 def test_full_c5_bf16_huge():
     _full_workload("ce_16384x262144_bf16", grad_sample=512)
+
+
+def test_full_c3_nograd_streamed():
+    """The headline batch without the gradient (each row streamed through one
+    workgroup): every scalar and argmax, and every row's gradient recomputed
+    from the saved row statistics."""
+    _full_workload("ce_1023x128256_f32", grad=False)
+
+
+def test_full_c4_nograd_streamed():
+    _full_workload("ce_4096x131072_bf16_opts", grad=False, grad_sample=512)
 
 
 def test_quarter_rows_many_rows_per_group_f32():
