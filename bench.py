@@ -713,8 +713,8 @@ def main(argv=None) -> int:
         return 0
 
     if a.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported: this build runs "
-              "on one GPU only (the path shards by rows, with no communication between GPUs "
+        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported: the library runs "
+              "on one GPU (the path would shard by rows, with no communication between GPUs "
               "on the hot path).", file=sys.stderr)
         return 2
 
